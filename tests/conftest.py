@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long CPU test (oracle at large sizes)")
+
+
+@pytest.fixture(scope="session")
+def orc64():
+    import oracle
+    return oracle.Oracle("f64")
+
+
+@pytest.fixture(scope="session")
+def orc32():
+    import oracle
+    return oracle.Oracle("f32")

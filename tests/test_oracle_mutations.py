@@ -1,0 +1,126 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one slip in a private copy of the oracle's C source (a
+dropped term, a wrong sign, a wrong index, a transposed operand, a wrong
+constant), builds it with gcc into a temporary library, points the oracle
+binding at it and runs the pin tests.  At least one pin must fail for every
+mutant.  Everything here runs on the CPU; the GPU library is not involved.
+"""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = open(oracle.SRC).read()
+
+MUTANTS = [
+    ("weights mirrored", "w[o] = bspline2(f - (real)o);", "w[o] = bspline2(f + (real)o - 2);"),
+    ("base without half shift", "return (int64_t)floor(xn - (real)0.5);", "return (int64_t)floor(xn);"),
+    ("spline inner piece", "return (real)0.75 - d * d;", "return (real)0.75 - d;"),
+    ("no SVD sign fix on V", "if (dot3(v3x, v[2]) < 0)", "if (0)"),
+    ("rotation transposed", "mat_mul_bt(U, V, R);", "mat_mul_bt(V, U, R);"),
+    ("stress F^T F order", "mat_mul_bt(D, F, tau);", "for (int r_ = 0; r_ < 3; ++r_) for (int c_ = 0; c_ < 3; ++c_) "
+     "{ real s_ = 0; for (int k_ = 0; k_ < 3; ++k_) s_ += F[k_ * 3 + r_] * D[k_ * 3 + c_]; tau[r_ * 3 + c_] = s_; }"),
+    ("stress drops lambda term", "tau[a * 4] += lam * (J - 1) * J;", "tau[a * 4] += 0;"),
+    ("stress lambda term without J", "tau[a * 4] += lam * (J - 1) * J;", "tau[a * 4] += lam * (J - 1);"),
+    ("lame swapped", "*mu = E / (2 * (1 + nu));", "*mu = E * nu / ((1 + nu) * (1 - 2 * nu)) + 0 * E / (2 * (1 + nu));"),
+    ("fluid stress sign", "return K * J * (J - 1);", "return K * J * (1 - J);"),
+    ("D^-1 = 2/dx^2 in P2G", "const real inv_dx2x4 = 4 * (real)P->n * (real)P->n; /* D^{-1}",
+     "const real inv_dx2x4 = 2 * (real)P->n * (real)P->n; /* D^{-1}"),
+    ("stress term sign in P2G", "A[i] = mass * C[9 * p + i] - dt * vol", "A[i] = mass * C[9 * p + i] + dt * vol"),
+    ("mass without density", "mass = (real)P->rho * (real)P->p_vol;", "mass = (real)P->p_vol;"),
+    ("A transposed in P2G", "real ad = A[a * 3] * d[0] + A[a * 3 + 1] * d[1] + A[a * 3 + 2] * d[2];",
+     "real ad = A[a] * d[0] + A[3 + a] * d[1] + A[6 + a] * d[2];"),
+    ("P2G offset sign", "real d[3] = {(real)i * dx - x[3 * p], (real)j * dx - x[3 * p + 1], (real)k * dx - x[3 * p + 2]};\n"
+     "          int64_t id = node_index(n, i, j, k);\n          gm[id]",
+     "real d[3] = {x[3 * p] - (real)i * dx, x[3 * p + 1] - (real)j * dx, x[3 * p + 2] - (real)k * dx};\n"
+     "          int64_t id = node_index(n, i, j, k);\n          gm[id]"),
+    ("P2G axis swap in index", "int64_t id = node_index(n, i, j, k);\n          gm[id]", "int64_t id = node_index(n, j, i, k);\n          gm[id]"),
+    ("grid update without gravity", "va = gp[3 * id + a] / gm[id] + dt * (real)P->gravity[a];", "va = gp[3 * id + a] / gm[id];"),
+    ("wall one layer too thick", "int in_wall = i < wall ||", "int in_wall = i <= wall ||"),
+    ("wall only on low side", "|| i >= n - wall || j >= n - wall || k >= n - wall;", ";"),
+    ("G2P C without D^-1", "for (int i = 0; i < 9; ++i) Cn[i] = inv_dx2x4 * B[i];", "for (int i = 0; i < 9; ++i) Cn[i] = B[i];"),
+    ("G2P C transposed", "for (int c = 0; c < 3; ++c) B[a * 3 + c] += wt * vi[a] * d[c];",
+     "for (int c = 0; c < 3; ++c) B[c * 3 + a] += wt * vi[a] * d[c];"),
+    ("G2P F update right-multiplied", "mat_mul(G, F + 9 * p, F + 9 * p);", "mat_mul(F + 9 * p, G, F + 9 * p);"),
+    ("G2P fluid J additive", "J[p] = J[p] * mat_det(G);", "J[p] = J[p] + mat_det(G) - 1 + dt * 0;"),
+    ("G2P advects with pre-gravity velocity", "real xa = x[3 * p + a] + dt * vn[a];",
+     "real xa = x[3 * p + a] + dt * (vn[a] - dt * (real)P->gravity[a]);"),
+    ("G2P velocity of neighbour axis", "vn[a] += wt * vi[a];", "vn[a] += wt * vi[(a + 1) % 3];"),
+]
+
+
+def _all_pins():
+    rng = np.random.default_rng(0)
+    out = [
+        lambda o: [pins.test_weights_moments(o, f) for f in [0.5, 0.77, 1.0, 1.31, 1.49]],
+        pins.test_weights_support_and_base,
+        pins.test_weights_are_c1_continuous,
+        lambda o: [pins.test_svd_against_numpy(o, s) for s in range(6)],
+        lambda o: [pins.test_rotation_is_polar_factor(o, s) for s in range(4)],
+        pins.test_lame_closed_forms,
+        pins.test_stress_closed_forms,
+        lambda o: [pins.test_stress_is_energy_derivative(o, s) for s in range(3)],
+        pins.test_fluid_stress,
+        pins.test_p2g_single_particle_table,
+        lambda o: pins.test_p2g_mass_momentum_angular_momentum(),
+        lambda o: pins.test_affine_reproduction_translation_and_rotation(),
+        lambda o: pins.test_free_fall(),
+        lambda o: pins.test_step_momentum_conservation(),
+        lambda o: pins.test_walls_zero_velocity(),
+        lambda o: pins.test_stress_force_is_energy_gradient(),
+        lambda o: pins.test_fluid_J_matches_det_F(),
+    ]
+    del rng
+    return out
+
+
+def _build(src_text, out):
+    with tempfile.NamedTemporaryFile("w", suffix=".c", delete=False) as f:
+        f.write(src_text)
+        cpath = f.name
+    try:
+        subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                        "-DORC_REAL=double", cpath, "-o", out, "-lm"], check=True,
+                       capture_output=True)
+    finally:
+        os.unlink(cpath)
+
+
+def _failing_pins(libpath):
+    saved_path, saved_lib = oracle.LIBS["f64"], oracle._loaded.pop("f64", None)
+    oracle.LIBS["f64"] = libpath
+    failed = []
+    try:
+        o = oracle.Oracle("f64")
+        with np.errstate(all="ignore"):
+            for k, pin in enumerate(_all_pins()):
+                try:
+                    pin(o)
+                except (AssertionError, RuntimeError, np.linalg.LinAlgError, FloatingPointError):
+                    failed.append(k)
+    finally:
+        oracle.LIBS["f64"] = saved_path
+        oracle._loaded.pop("f64", None)
+        if saved_lib is not None:
+            oracle._loaded["f64"] = saved_lib
+    return failed
+
+
+def test_unmutated_source_passes_all_pins(tmp_path):
+    lib = str(tmp_path / "orig.so")
+    _build(SRC, lib)
+    assert _failing_pins(lib) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    assert SRC.count(old) == 1, f"mutation anchor for '{name}' not found exactly once"
+    lib = str(tmp_path / "mut.so")
+    _build(SRC.replace(old, new), lib)
+    assert _failing_pins(lib), f"no pin catches mutant '{name}'"
