@@ -1,0 +1,172 @@
+#!/usr/bin/env python3
+"""Throughput of one explicit MLS-MPM step on one MI355X.
+
+A "step" is one pass of the whole hot path (bucket sort by block, P2G with
+fused stress, grid update, G2P) over the resident particle set, replayed as a
+HIP graph through the C ABI.  The default workload is the 12M-particle
+heterogeneous slab on a 256^3 grid.
+
+Printed JSON line (rank 0, N=1):
+  value          particle-steps/s over K timed steps (inputs resident in HBM)
+  roofline       dominant kernel: algorithmic bytes per launch / its average
+                 launch time (HIP events around each kernel on the stream it
+                 runs on, measured in eager profiled steps), vs 8 TB/s
+  cpu_baseline   the serial fp64 oracle timed on this host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "particle-steps/sec at 12M particles (256^3 grid) + achieved HBM GB/s"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bool) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel (what the method must
+    move through that kernel; see the byte model in the design notes).
+    fp32 everywhere; F is 9 floats (elastic) or 1 (fluid J)."""
+    f = 36 if material == 0 else 4
+    e = 4 if has_E else 0
+    return {
+        # bin counts read twice, cursors written, counts zeroed
+        "k_scan_tiles": 4 * nbins,
+        "k_scan_bins": 12 * nbins,
+        "k_scatter": 8 * N,
+        # reads perm, x, v, C, F(, E); writes F(, E); accumulator write per active node
+        "k_p2g": N * (4 + 12 + 12 + 36 + f + e + f + e) + 16 * active_nodes,
+        # reads (m, p) and writes v per active node
+        "k_grid_update": 28 * active_nodes,
+        # reads perm, x, id; writes x, v, C, id, key; reads grid v once per active node
+        "k_g2p": N * (4 + 12 + 4 + 12 + 12 + 36 + 4 + 4) + 12 * active_nodes,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="slab_12m")
+    ap.add_argument("--profile-steps", type=int, default=10)
+    ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import material_point_physics_amd as mpm
+    from material_point_physics_amd import scenes
+
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    sc = scenes.SCENES[args.workload]()
+    log(f"scene {sc.name}: N={sc.N} n={sc.n} generated in {time.time() - t0:.1f}s")
+    sim = mpm.Simulation(sc)
+    stream = sim.stream
+    log("created; warmup")
+    sim.step(args.warmup)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K graph-replayed steps, synchronised on both sides
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    sim.step(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_start
+    dev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * t_wall / args.steps
+    value = sc.N * args.steps / t_wall
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {dev_ms / args.steps:.4f} ms/step device")
+
+    # ---- per-kernel launch times (HIP events around each kernel, same stream)
+    kms = mpm.mpm_step_profiled(sim.handle, args.profile_steps, stream)
+    kavg = {k: v / args.profile_steps for k, v in kms.items()}
+    m, _ = sim.read_grid()
+    mass = m.cpu().numpy()
+    active_nodes = int((mass > 0).sum())
+    n = sc.n
+    nb = (n + 7) // 8
+    pad = np.zeros((nb * 8,) * 3, bool)
+    pad[:n, :n, :n] = mass > 0
+    active_blocks = int(pad.reshape(nb, 8, nb, 8, nb, 8).any(axis=(1, 3, 5)).sum())
+    status = sim.status()
+    sim.close()
+    # Calibration for the HBM-byte counters: one plain device copy of known
+    # size (read 256 MiB, write 256 MiB), outside the timed region.
+    cal_src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+    kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None)
+    kernels = {k: {"avg_ms": round(kavg[k], 5), "alg_bytes": kb[k],
+                   "GBps": round(kb[k] / (kavg[k] * 1e-3) / 1e9, 1)} for k in kavg}
+    dom = max(kavg, key=kavg.get)
+    achieved = kb[dom] / (kavg[dom] * 1e-3) / 1e9
+    step_bytes = sum(kb.values())
+    log(f"kernels: {kernels}")
+    log(f"active nodes {active_nodes}, active blocks {active_blocks}, status {status[:4]}")
+
+    # ---- CPU baseline: the serial oracle on a bounded sample of the workload
+    cpu = None
+    if args.cpu_steps > 0:
+        import oracle
+        log(f"oracle: {args.cpu_steps} step(s) of the full workload on one core")
+        orc = oracle.OracleSim(sc, "f64")
+        t1 = time.perf_counter()
+        orc.step(args.cpu_steps)
+        t_cpu = time.perf_counter() - t1
+        cpu = {"value": round(sc.N * args.cpu_steps / t_cpu, 1), "unit": "particle-steps/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{args.cpu_steps} full step(s) of {sc.name} ({sc.N} particles, {n}^3 grid), "
+                         f"serial fp64 oracle, {t_cpu:.1f} s"}
+        log(f"oracle: {t_cpu:.1f} s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "particle-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{sc.name}: {sc.description}", "particles": sc.N, "grid": f"{n}^3",
+                   "dt": sc.dt, "material": "fixed-corotated" if sc.material == 0 else "J-fluid"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "step_hbm": {"alg_bytes_per_step": step_bytes,
+                     "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * mpm.h -- C ABI of the MI355X MLS-MPM library (libmpm.so).
+ *
+ * One explicit MLS-MPM time step of the material point method: particles
+ * are sorted by grid block, scattered to a background grid (P2G), the grid
+ * momentum is updated (gravity, sticky walls), and the grid velocities are
+ * gathered back to the particles (G2P) with the APIC affine matrix, the
+ * deformation-gradient update and the fixed-corotated stress.  These are the
+ * phases named in "Principles towards Real-Time Simulation of Material Point
+ * Method on Modern GPUs" (rebuild-mapping and particle sorting, then P2G,
+ * grid update and G2P, in its discussion of essential and non-essential
+ * phases).
+ *
+ * The interface follows that page's single-GPU principles: all device memory
+ * is handed over once at creation and never reallocated (its memory
+ * reallocation principle); stepping is asynchronous, with no host-device
+ * synchronisation inside a step (its CPU-GPU synchronisation principle); and
+ * a whole step is replayed as one captured HIP graph (its principle of few
+ * kernel launches per step).
+ *
+ * Conventions for every call:
+ *   - Pointers documented as "device" must point to memory of the current
+ *     HIP device.  "host" pointers are read only during the call.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the legacy
+ *     default stream.  Every device-side effect is enqueued on it and is
+ *     complete once the caller synchronises that stream.
+ *   - Return value: MPM_OK (0) or a negative MPM_ERR_* code.  Argument errors
+ *     are detected on the host before anything is enqueued and leave the
+ *     simulation untouched.  No C++ exception crosses this interface.
+ *   - A handle is not thread-safe; distinct handles are independent.
+ *
+ * Domain and grid: the domain is [0,1]^3, with grid_n nodes per axis at
+ * x_i = i*dx, dx = 1/grid_n.  Dense grid outputs use linear index
+ * i + n*(j + n*k) for node (i,j,k), i along x.  Particle positions are kept
+ * in [2dx, (n-2)dx] per component so that every 3x3x3 stencil lies inside
+ * the grid.
+ */
+#ifndef MPM_H
+#define MPM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---- */
+#define MPM_OK 0
+#define MPM_ERR_INVALID_ARG (-1) /* a NULL, negative or out-of-range argument */
+#define MPM_ERR_WORKSPACE (-2)   /* workspace missing, too small or misaligned */
+#define MPM_ERR_HIP (-3)         /* a HIP runtime call failed */
+#define MPM_ERR_STATE (-4)       /* the handle is not usable (e.g. graph missing) */
+
+/* ---- materials ---- */
+#define MPM_FIXED_COROTATED 0 /* elastic solid, state F (3x3) */
+#define MPM_J_FLUID 1         /* weakly compressible fluid, state J (scalar) */
+
+/* ---- status word bits (see mpm_status) ---- */
+#define MPM_STATUS_NONFINITE 0x1u  /* a NaN or Inf appeared in particle velocity, C or position */
+#define MPM_STATUS_CLAMPED 0x2u    /* a position component was clamped into [2dx,(n-2)dx] */
+#define MPM_STATUS_INVERTED 0x4u   /* det F <= 0 (or J <= 0) met in the stress evaluation */
+#define MPM_STATUS_BAD_INPUT 0x8u  /* non-finite or out-of-domain input at creation (it was clamped) */
+#define MPM_STATUS_NO_CONVERGE 0x10u /* the polar iteration hit its iteration cap */
+#define MPM_STATUS_WORDS 8         /* [0] flags, [1] clamp count, [2] inverted count,
+                                      [3] non-finite count, [4..7] reserved (0) */
+
+typedef struct mpm_sim mpm_sim;
+
+/* Scalar parameters of a simulation.
+ *   struct_size : sizeof(mpm_params), for forward compatibility.
+ *   grid_n      : nodes per axis, 8 <= grid_n <= 1024.
+ *   dt          : time step (> 0).
+ *   gravity     : acceleration added to every grid velocity, per axis.
+ *   wall_nodes  : sticky-wall thickness: all velocity components are zeroed
+ *                 on nodes with any index < wall_nodes or >= grid_n - wall_nodes
+ *                 (0 <= wall_nodes <= grid_n/2).
+ *   material    : MPM_FIXED_COROTATED or MPM_J_FLUID.
+ *   E           : Young's modulus (bulk modulus K for MPM_J_FLUID), >= 0;
+ *                 used when no per-particle modulus is given.
+ *   nu          : Poisson ratio, 0 <= nu < 0.5 (ignored for MPM_J_FLUID).
+ *   rho, p_vol  : density and initial particle volume (> 0); particle mass
+ *                 is rho * p_vol. */
+typedef struct {
+  uint32_t struct_size;
+  int32_t grid_n;
+  float dt;
+  float gravity[3];
+  int32_t wall_nodes;
+  int32_t material;
+  float E;
+  float nu;
+  float rho;
+  float p_vol;
+} mpm_params;
+
+/* Bytes of device workspace a simulation of n_particles needs (0 when the
+ * parameters are invalid).  Pure host computation. */
+size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles);
+
+/* Create a simulation and upload its initial state (the particle set of the
+ * page's problem statement: material points carried across a background
+ * grid by explicit steps).
+ *   params      : host, read during the call.
+ *   n_particles : 0 <= n < 2^31.
+ *   x0          : device, (N,3) float32 row-major positions (required if N > 0).
+ *   v0          : device, (N,3) velocities, or NULL for zero.
+ *   C0          : device, (N,3,3) row-major APIC affine matrices, or NULL for zero.
+ *   F0          : device, (N,3,3) deformation gradients for MPM_FIXED_COROTATED
+ *                 or (N) volume ratios J for MPM_J_FLUID; NULL for I (or 1).
+ *   E_p         : device, (N) per-particle Young's modulus, or NULL for params->E.
+ *   workspace   : device, at least mpm_workspace_bytes(params, N) bytes,
+ *                 256-byte aligned, owned by the caller, and must outlive the
+ *                 handle.  The library never allocates device memory.
+ *   stream      : initialisation kernels are enqueued on it; the inputs may
+ *                 be released once it has completed.
+ *   out         : host, receives the handle.
+ * Inputs with a non-finite or out-of-domain position are clamped into the
+ * domain and raise MPM_STATUS_BAD_INPUT; this is reported through
+ * mpm_status, without a host synchronisation. */
+int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, const float *v0,
+               const float *C0, const float *F0, const float *E_p, void *workspace,
+               size_t workspace_bytes, void *stream, mpm_sim **out);
+
+/* Advance n_steps >= 0 explicit steps, enqueued asynchronously on `stream`
+ * (one graph launch per step: key/bucket sort, P2G, grid update, G2P).  No
+ * host synchronisation, no allocation. */
+int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream);
+
+/* Copy the particle state after the last step, in creation order, into
+ * caller-owned device arrays: x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)
+ * for the elastic material or (N) for the fluid.  Any output may be NULL.
+ * Asynchronous on `stream`. */
+int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J, void *stream);
+
+/* Copy the grid state of the last step into caller-owned dense device arrays:
+ * mass (n^3) and momentum (n^3 x 3) = m_i * v_i after gravity and walls.
+ * Nodes the last step did not touch are 0.  Either output may be NULL.
+ * Before any step both are all zero.  Asynchronous on `stream`. */
+int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream);
+
+/* Copy the MPM_STATUS_WORDS uint32 status words (flags, counters since
+ * creation) into a caller-owned device array.  Asynchronous on `stream`. */
+int mpm_status(mpm_sim *sim, uint32_t *status_device, void *stream);
+
+/* Steps taken since creation (host-side counter, no synchronisation). */
+int64_t mpm_steps_taken(const mpm_sim *sim);
+
+/* Number of kernels a step launches, and the name of kernel k. */
+int32_t mpm_num_kernels(void);
+const char *mpm_kernel_name(int32_t k);
+
+/* Measurement helper: run n_steps steps eagerly (the same kernels and launch
+ * shapes as the graph), bracketing every kernel with HIP events on `stream`,
+ * then synchronise `stream` and add each kernel's elapsed milliseconds into
+ * kernel_ms[k] (host, mpm_num_kernels() entries, caller-initialised). */
+int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms);
+
+/* Release the handle and its graphs (not the caller's workspace).  Waits for
+ * the handle's pending work on its private stream.  NULL is ignored. */
+void mpm_destroy(mpm_sim *sim);
+
+/* Static description of a return code. */
+const char *mpm_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPM_H */

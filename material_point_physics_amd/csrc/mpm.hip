@@ -1,0 +1,1226 @@
+// mpm.hip -- MI355X (gfx950) implementation of one explicit MLS-MPM step
+// behind the C ABI declared in include/mpm.h.
+//
+// Method: "Principles towards Real-Time Simulation of Material Point Method on
+// Modern GPUs" (below [RT-MPM]) splits a step into particle sorting, P2G,
+// grid update and G2P; the equations are the textbook MLS-MPM with quadratic
+// B-splines, APIC transfer and the fixed-corotated model (Hu et al. 2018;
+// Jiang et al. 2015; Stomakhin et al. 2012).
+//
+// Step = 6 kernels, captured once into a HIP graph per buffer parity:
+//   k_scan_*      two-phase exclusive scan of per-bin counts -> bin starts,
+//                 chunk list (<= KMAX particles of one bin per chunk)
+//   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), wave-
+//                 aggregated atomic cursors -> perm[slot] = source index
+//   k_p2g         one wavefront per chunk: in-LDS counting sort by cell (second
+//                 radix digit, 64 cells = 64 lanes), deferred F update, polar
+//                 decomposition, Kirchhoff stress, APIC momentum, conflict-free
+//                 accumulation into a private 6^3-node LDS window, one native
+//                 global atomic flush per window node
+//   k_grid_update active node-blocks only: v = p/m + dt g, sticky walls,
+//                 clears the P2G accumulator
+//   k_g2p         gather, APIC C, advection + clamp, writes the state in
+//                 sorted order, computes the next step's block keys/counts
+//
+// Deferred deformation gradient: [RT-MPM] (kernel-merging discussion) notes
+// that the F update at the end of G2P can be postponed to the start of P2G
+// to avoid writing F twice, and merges SVD and stress into P2G.  Here G2P
+// produces C; the next P2G forms F = (I + dt C) F_prev, evaluates the stress
+// and stores F.  mpm_read_particles applies the same pending update, so the
+// state read back is F at the end of the step.
+//
+// Memory: every buffer is carved from the caller's workspace at creation;
+// nothing is allocated afterwards ([RT-MPM], memory-reallocation principle).
+// No kernel in a step reads a value back to the host ([RT-MPM], CPU-GPU
+// synchronisation principle): launch shapes are fixed at creation, and the
+// variable-length work lists (chunks, active blocks) are consumed by
+// persistent workgroups that read their lengths on the device.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/mpm.h"
+
+namespace {
+
+constexpr int WG = 256;          // threads per workgroup (4 wave64)
+constexpr int NB = 8;            // node-block edge of the grid layout (512 nodes per block)
+constexpr int CB = 4;            // bin edge in cells: particles are bucketed by 4^3-cell bins
+constexpr int CB3 = CB * CB * CB;  // 64 cells per bin = one wavefront
+constexpr int PW = CB + 2;       // P2G window edge: base nodes of a bin + stencil reach
+constexpr int PW3 = PW * PW * PW;  // 216 window nodes
+constexpr int KMAX = 256;        // particles per P2G chunk (4 rounds of one wavefront)
+constexpr int NQ = 8;            // P2G work queues, one per XCD
+constexpr int NUM_KERNELS = 6;
+
+enum Ctr : int {
+  CTR_NCHUNKS = 0,
+  CTR_NACTIVE = 1,
+  CTR_PENDING = 2,
+  CTR_QHEAD = 8,   // NQ queue heads
+  CTR_WORDS = 16,
+};
+
+struct PBuf {
+  float *x;      // [3][Np]
+  float *v;      // [3][Np]
+  float *C;      // [9][Np], row-major components
+  float *F;      // [9][Np] (elastic) or [1][Np] (fluid J), one step behind: see header note
+  float *E;      // [Np] per-particle Young's modulus, or nullptr
+  uint32_t *id;  // [Np] creation index
+};
+
+struct SimDev {
+  int32_t N, Np;
+  int32_t n, nb, nblk;         // grid nodes per axis, node-blocks per axis, node-blocks
+  int32_t nbin, nbins;         // bins per axis, bins
+  int32_t wall, material, has_E;
+  float dx, fn, dt;
+  float g[3];
+  float mass, vol, E;
+  float mu_per_E, lam_per_E;  // Lame parameters per unit Young's modulus
+  float stress_k;             // dt * V0 * 4 / dx^2
+  float c_scale;              // 4 / dx (G2P: C = 4/dx^2 * sum w v (x_i - x_p), offsets in cells)
+  float lo, hi;               // position clamp
+  uint32_t max_chunks;
+  PBuf buf[2];
+  uint32_t *perm, *key;
+  uint32_t *bin_count, *bin_cursor;
+  uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
+  int32_t ntiles;
+  uint4 *chunks;
+  uint32_t *active_flag, *active_list;
+  float4 *gridA;  // P2G accumulator per node: (m, p_x, p_y, p_z)
+  float4 *gridV;  // updated grid per node: (v_x, v_y, v_z, m)
+  uint32_t *ctr;
+  uint32_t *status;
+};
+
+// ------------------------------------------------------------ device utils
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Node-blocked grid index: blocks of 8^3 nodes, x fastest inside and across blocks.
+__device__ __forceinline__ uint32_t node_index(const SimDev &s, int gx, int gy, int gz) {
+  const uint32_t blk = ((uint32_t)(gz >> 3) * s.nb + (uint32_t)(gy >> 3)) * s.nb + (uint32_t)(gx >> 3);
+  return (blk << 9) | ((uint32_t)(gz & 7) << 6) | ((uint32_t)(gy & 7) << 3) | (uint32_t)(gx & 7);
+}
+
+// Base node floor(x/dx - 1/2) of a position already inside the clamp box.
+__device__ __forceinline__ int base_node(float xn) { return (int)floorf(xn - 0.5f); }
+
+// Bin of a base node: 4^3-cell bins, x fastest.
+__device__ __forceinline__ uint32_t bin_key(const SimDev &s, int bx, int by, int bz) {
+  return ((uint32_t)(bz >> 2) * s.nbin + (uint32_t)(by >> 2)) * s.nbin + (uint32_t)(bx >> 2);
+}
+
+// Quadratic B-spline weights of nodes base+0,1,2 at fractional offset f in [0.5,1.5).
+__device__ __forceinline__ void bspline_weights(float f, float w[3]) {
+  const float a = 1.5f - f, b = f - 1.0f, c = f - 0.5f;
+  w[0] = 0.5f * a * a;
+  w[1] = 0.75f - b * b;
+  w[2] = 0.5f * c * c;
+}
+
+// Wave-aggregated atomic add of 1 per valid lane into counters[key]: one
+// atomic per distinct key in the wavefront.  Returns each lane's slot
+// (old value + rank among the lanes with the same key).
+__device__ __forceinline__ uint32_t wave_aggregated_increment(uint32_t *counters, uint32_t key, bool valid) {
+  const int lane = lane_id();
+  uint64_t todo = __ballot(valid);
+  uint32_t slot = 0;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const uint32_t lkey = __shfl(key, leader);
+    const uint64_t peers = __ballot(valid && key == lkey) & todo;
+    uint32_t old = 0;
+    if (lane == leader) old = atomicAdd(counters + lkey, (uint32_t)__popcll(peers));
+    old = __shfl(old, leader);
+    if ((peers >> lane) & 1ull) slot = old + (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
+    todo &= ~peers;
+  }
+  return slot;
+}
+
+__device__ __forceinline__ void flag_status(const SimDev &s, uint32_t bit, int counter_word) {
+  atomicOr(&s.status[0], bit);
+  if (counter_word > 0) atomicAdd(&s.status[counter_word], 1u);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+// contiguous range of logical blocks so that neighbouring particles (and the
+// grid nodes they share) stay in one XCD's L2.  grid must be a multiple of 8.
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t bid, uint32_t grid) {
+  return (bid & 7u) * (grid >> 3) + (bid >> 3);
+}
+
+// ------------------------------------------------------- 3x3 linear algebra
+
+__device__ __forceinline__ float det3(const float A[9]) {
+  return A[0] * (A[4] * A[8] - A[5] * A[7]) - A[1] * (A[3] * A[8] - A[5] * A[6]) +
+         A[2] * (A[3] * A[7] - A[4] * A[6]);
+}
+
+// Eigenvector of the smallest eigenvalue of a symmetric 3x3 matrix by cyclic
+// Jacobi rotations (Rutishauser's formulation of the symmetric Jacobi method,
+// as in Golub & Van Loan, "Matrix Computations"): accurate to about eps/gap
+// even when two eigenvalues nearly coincide.  Only used for reflected F.
+__device__ void smallest_eigvec_sym3(const float Hin[9], float v[3]) {
+  float a[3][3], W[3][3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      a[r][c] = Hin[r * 3 + c];
+      W[r][c] = (r == c) ? 1.f : 0.f;
+    }
+  for (int sweep = 0; sweep < 10; ++sweep) {
+    const float off = a[0][1] * a[0][1] + a[0][2] * a[0][2] + a[1][2] * a[1][2];
+    const float dia = a[0][0] * a[0][0] + a[1][1] * a[1][1] + a[2][2] * a[2][2];
+    if (off <= 1e-14f * dia) break;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int p = k == 2 ? 1 : 0, q = k == 0 ? 1 : 2;
+      const float apq = a[p][q];
+      if (apq == 0.f) continue;
+      const float theta = (a[q][q] - a[p][p]) / (2.f * apq);
+      const float t = copysignf(1.f, theta) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+      const float c = rsqrtf(t * t + 1.f), sn = t * c;
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {  // columns p, q
+        const float xp = a[r][p], xq = a[r][q];
+        a[r][p] = c * xp - sn * xq;
+        a[r][q] = sn * xp + c * xq;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {  // rows p, q
+        const float xp = a[p][r], xq = a[q][r];
+        a[p][r] = c * xp - sn * xq;
+        a[q][r] = sn * xp + c * xq;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const float xp = W[r][p], xq = W[r][q];
+        W[r][p] = c * xp - sn * xq;
+        W[r][q] = sn * xp + c * xq;
+      }
+    }
+  }
+  int m = 0;
+  if (a[1][1] < a[m][m]) m = 1;
+  if (a[2][2] < a[m][m]) m = 2;
+  v[0] = W[0][m];
+  v[1] = W[1][m];
+  v[2] = W[2][m];
+}
+
+// Rotation R in SO(3) closest to F (the fixed-corotated model's rotation).
+// Higham's scaled Newton iteration for the polar decomposition (Higham 1986,
+// "Computing the polar decomposition -- with applications"):
+//   X <- (zeta X + X^{-T} / zeta) / 2,  zeta = |det X|^{-1/3},
+// which converges quadratically to the orthogonal polar factor Q.  When
+// det F < 0, Q is a reflection; the SO(3) rotation with the sign on the
+// smallest singular value is Q (I - 2 v v^T), v the right singular vector of
+// the smallest singular value (smallest eigenvector of H = Q^T F).
+// Returns status bits (inverted / no convergence).
+__device__ uint32_t rotation_of(const float F[9], float R[9]) {
+  float X[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) X[k] = F[k];
+  uint32_t st = 0;
+  float detF = det3(F);
+  if (!(fabsf(detF) > 1e-20f) || !isfinite(detF)) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) R[k] = (k % 4 == 0) ? 1.f : 0.f;
+    return MPM_STATUS_INVERTED;
+  }
+  bool done = false;
+  for (int it = 0; it < 24 && !done; ++it) {
+    const float c00 = X[4] * X[8] - X[5] * X[7], c01 = X[5] * X[6] - X[3] * X[8], c02 = X[3] * X[7] - X[4] * X[6];
+    const float c10 = X[2] * X[7] - X[1] * X[8], c11 = X[0] * X[8] - X[2] * X[6], c12 = X[1] * X[6] - X[0] * X[7];
+    const float c20 = X[1] * X[5] - X[2] * X[4], c21 = X[2] * X[3] - X[0] * X[5], c22 = X[0] * X[4] - X[1] * X[3];
+    const float det = X[0] * c00 + X[1] * c01 + X[2] * c02;
+    const float ad = fabsf(det);
+    const float zeta = exp2f(-0.333333333f * log2f(ad));
+    const float a = 0.5f * zeta, b = 0.5f / (zeta * det);
+    const float Y[9] = {a * X[0] + b * c00, a * X[1] + b * c01, a * X[2] + b * c02,
+                        a * X[3] + b * c10, a * X[4] + b * c11, a * X[5] + b * c12,
+                        a * X[6] + b * c20, a * X[7] + b * c21, a * X[8] + b * c22};
+    float diff = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const float d = Y[k] - X[k];
+      diff += d * d;
+      X[k] = Y[k];
+    }
+    done = diff < 1e-11f;
+  }
+  if (!done) st |= MPM_STATUS_NO_CONVERGE;
+  if (detF < 0.f) {
+    st |= MPM_STATUS_INVERTED;
+    float H[9];  // Q^T F
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) H[r * 3 + c] = X[0 * 3 + r] * F[0 * 3 + c] + X[1 * 3 + r] * F[1 * 3 + c] + X[2 * 3 + r] * F[2 * 3 + c];
+    float Hs[9];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) Hs[r * 3 + c] = 0.5f * (H[r * 3 + c] + H[c * 3 + r]);
+    float v[3];
+    smallest_eigvec_sym3(Hs, v);
+    const float qv[3] = {X[0] * v[0] + X[1] * v[1] + X[2] * v[2], X[3] * v[0] + X[4] * v[1] + X[5] * v[2],
+                         X[6] * v[0] + X[7] * v[1] + X[8] * v[2]};
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) X[r * 3 + c] -= 2.0f * qv[r] * v[c];
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) R[k] = X[k];
+  return st;
+}
+
+// --------------------------------------------------------------- kernels
+
+// Creation: AoS inputs -> SoA buffer 0 (creation order), ids, first keys.
+__global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__ x0, const float *__restrict__ v0,
+                                             const float *__restrict__ C0, const float *__restrict__ F0,
+                                             const float *__restrict__ E_p) {
+  const uint32_t i = blockIdx.x * WG + threadIdx.x;
+  const bool valid = i < (uint32_t)s.N;
+  const PBuf b = s.buf[0];
+  const int Np = s.Np;
+  uint32_t key = 0;
+  if (valid) {
+    bool bad = false;
+    int base[3];
+    for (int a = 0; a < 3; ++a) {
+      float xa = x0[3 * (size_t)i + a];
+      if (!(xa >= s.lo && xa <= s.hi)) bad = true;  // also catches NaN
+      xa = fminf(fmaxf(xa, s.lo), s.hi);
+      b.x[a * Np + i] = xa;
+      b.v[a * Np + i] = v0 ? v0[3 * (size_t)i + a] : 0.f;
+      base[a] = base_node(xa * s.fn);
+    }
+    if (bad) flag_status(s, MPM_STATUS_BAD_INPUT, 0);
+    for (int k = 0; k < 9; ++k) b.C[k * Np + i] = C0 ? C0[9 * (size_t)i + k] : 0.f;
+    if (s.material == MPM_J_FLUID) {
+      b.F[i] = F0 ? F0[i] : 1.f;
+    } else {
+      for (int k = 0; k < 9; ++k) b.F[k * Np + i] = F0 ? F0[9 * (size_t)i + k] : ((k % 4 == 0) ? 1.f : 0.f);
+    }
+    if (s.has_E) b.E[i] = E_p[i];
+    b.id[i] = i;
+    key = bin_key(s, base[0], base[1], base[2]);
+    s.key[i] = key;
+  }
+  wave_aggregated_increment(s.bin_count, key, valid);
+}
+
+// Zero a uint32 range (fill kernel; graphs avoid memset nodes).
+__global__ __launch_bounds__(WG) void k_zero_u32(uint32_t *p, size_t n) {
+  for (size_t k = (size_t)blockIdx.x * WG + threadIdx.x; k < n; k += (size_t)gridDim.x * WG) p[k] = 0u;
+}
+
+__global__ __launch_bounds__(WG) void k_zero_f32(float *p, size_t n) {
+  for (size_t k = (size_t)blockIdx.x * WG + threadIdx.x; k < n; k += (size_t)gridDim.x * WG) p[k] = 0.f;
+}
+
+// Block-wide inclusive scan of one value per thread (NT threads); returns the
+// inclusive prefix and writes the workgroup total to *total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t *wsum, uint32_t *total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  uint32_t inc = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(inc, d);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t x = wsum[w];
+    if (w < wave) before += x;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc;
+}
+
+constexpr int SCAN_PER = 8;                  // bins per thread
+constexpr int SCAN_TILE = WG * SCAN_PER;     // bins per scan tile
+
+// Scan, phase 1: per-tile totals of particle counts and chunk counts.
+__global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
+  __shared__ uint32_t wsum[WG / 64];
+  const uint32_t nbins = (uint32_t)s.nbins;
+  const uint32_t b0 = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_PER;
+  uint32_t c = 0, ch = 0;
+#pragma unroll
+  for (int k = 0; k < SCAN_PER; ++k) {
+    const uint32_t cnt = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
+    c += cnt;
+    ch += (cnt + KMAX - 1) / KMAX;
+  }
+  uint32_t tc, tch;
+  block_scan_incl<WG>(c, wsum, &tc);
+  block_scan_incl<WG>(ch, wsum, &tch);
+  if (threadIdx.x == 0) {
+    s.tile_sum[2 * blockIdx.x] = tc;
+    s.tile_sum[2 * blockIdx.x + 1] = tch;
+  }
+}
+
+// Scan, phase 2: each tile adds the totals of the tiles before it, scans its
+// bins and writes the bin cursors for k_scatter, the chunk list for k_p2g, and
+// zeroes the counts for k_g2p; the last tile publishes the chunk total.
+__global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
+  __shared__ uint32_t wsum[WG / 64];
+  const uint32_t nbins = (uint32_t)s.nbins;
+  const uint32_t t = blockIdx.x;
+  uint32_t pc = 0, pch = 0;
+  for (uint32_t k = threadIdx.x; k < t; k += WG) {
+    pc += s.tile_sum[2 * k];
+    pch += s.tile_sum[2 * k + 1];
+  }
+  uint32_t tile_base_c, tile_base_ch;
+  block_scan_incl<WG>(pc, wsum, &tile_base_c);
+  block_scan_incl<WG>(pch, wsum, &tile_base_ch);
+  const uint32_t b0 = t * SCAN_TILE + threadIdx.x * SCAN_PER;
+  uint32_t c[SCAN_PER], ch[SCAN_PER], csum = 0, chsum = 0;
+#pragma unroll
+  for (int k = 0; k < SCAN_PER; ++k) {
+    c[k] = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
+    ch[k] = (c[k] + KMAX - 1) / KMAX;
+    csum += c[k];
+    chsum += ch[k];
+  }
+  uint32_t tc, tch;
+  const uint32_t ic = block_scan_incl<WG>(csum, wsum, &tc);
+  const uint32_t ich = block_scan_incl<WG>(chsum, wsum, &tch);
+  uint32_t run = tile_base_c + ic - csum, chrun = tile_base_ch + ich - chsum;
+#pragma unroll
+  for (int k = 0; k < SCAN_PER; ++k) {
+    const uint32_t b = b0 + k;
+    if (b < nbins) {
+      s.bin_cursor[b] = run;
+      for (uint32_t j = 0; j < ch[k]; ++j) {
+        const uint32_t off = j * KMAX;
+        s.chunks[chrun + j] = make_uint4(run + off, min((uint32_t)KMAX, c[k] - off), b, 0u);
+      }
+      s.bin_count[b] = 0u;
+    }
+    run += c[k];
+    chrun += ch[k];
+  }
+  if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS] = tile_base_ch + tch;
+  if (t == 0) {
+    if (threadIdx.x == 0) s.ctr[CTR_NACTIVE] = 0u;
+    if (threadIdx.x < NQ) s.ctr[CTR_QHEAD + threadIdx.x] = 0u;
+  }
+}
+
+// Bucket scatter: particle i of the current order goes to the next free slot
+// of its block.  One atomic per distinct block per wavefront.
+__global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
+  const uint32_t i = blockIdx.x * WG + threadIdx.x;
+  const bool valid = i < (uint32_t)s.N;
+  const uint32_t key = valid ? s.key[i] : 0u;
+  const uint32_t slot = wave_aggregated_increment(s.bin_cursor, key, valid);
+  if (valid && slot < (uint32_t)s.N) s.perm[slot] = i;
+}
+
+// P2G.  Persistent single-wavefront workgroups take chunks (<= KMAX particles
+// of one 4^3-cell bin) from their XCD's queue.
+//
+// Accumulation without atomics: on gfx950, LDS float atomics serialise per
+// lane, so the window is private to the wavefront and updated with plain
+// read-modify-writes.  The chunk's particles are ordered by (rank within
+// their cell, cell): lanes that share a rank have distinct cells, so for a
+// fixed stencil offset their target nodes are distinct, and one masked
+// ds_read/ds_write pair per offset adds all of them.  A round of 64 lanes
+// that spans several ranks runs one pass per rank.  The LDS executes a
+// wavefront's accesses in issue order; compiler fences keep that order.
+template <int MAT, bool HAS_E>
+__global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
+  __shared__ float4 win[PW3];
+  __shared__ uint32_t hist[CB3];
+  __shared__ uint32_t rstart[KMAX + 1];
+  __shared__ uint64_t rmask[KMAX];
+  __shared__ uint32_t order[KMAX];
+
+  const PBuf in = s.buf[src], out = s.buf[src ^ 1];
+  const int lane = threadIdx.x;
+  const int Np = s.Np;
+  const uint32_t q = blockIdx.x & (NQ - 1);
+  const uint32_t nch = s.ctr[CTR_NCHUNKS];
+  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  const bool pending = s.ctr[CTR_PENDING] != 0u;
+  const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
+
+  for (;;) {
+    uint32_t c = 0;
+    if (lane == 0) c = qbeg + atomicAdd(&s.ctr[CTR_QHEAD + q], 1u);
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c >= qend) break;
+    const uint4 ch = s.chunks[c];
+    const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
+    const int bxb = (int)(bin % (uint32_t)s.nbin), byb = (int)((bin / (uint32_t)s.nbin) % (uint32_t)s.nbin),
+              bzb = (int)(bin / ((uint32_t)s.nbin * (uint32_t)s.nbin));
+    const int ox0 = bxb * CB, oy0 = byb * CB, oz0 = bzb * CB;  // first base node of the bin = window origin
+
+    for (int k = lane; k < PW3; k += 64) win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    hist[lane] = 0u;
+    __syncthreads();
+
+    // Pass A: cell of each particle and its rank within the cell.  Lanes with
+    // the same cell are matched bit by bit with ballots; the lowest lane of
+    // each group updates the cell's running count (leaders have distinct
+    // cells, so no atomics are needed).
+    uint32_t packed[KMAX / 64];
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      const uint32_t qi = (uint32_t)(64 * j + lane);
+      const bool v = qi < count;
+      uint32_t cell = 0u;
+      if (v) {
+        const uint32_t i = min(s.perm[start + qi], (uint32_t)s.N - 1u);
+        const int cx = min(max(base_node(in.x[i] * fn) - ox0, 0), CB - 1);
+        const int cy = min(max(base_node(in.x[Np + i] * fn) - oy0, 0), CB - 1);
+        const int cz = min(max(base_node(in.x[2 * Np + i] * fn) - oz0, 0), CB - 1);
+        cell = (uint32_t)((cz * CB + cy) * CB + cx);
+      }
+      uint64_t peers = __ballot(v);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const uint64_t bk = __ballot((cell >> k) & 1u);
+        peers &= ((cell >> k) & 1u) ? bk : ~bk;
+      }
+      const uint32_t before = hist[cell];
+      const uint32_t rank = before + (uint32_t)__popcll(peers & below);
+      if (v && (peers & below) == 0ull) hist[cell] = before + (uint32_t)__popcll(peers);
+      __asm__ __volatile__("" ::: "memory");
+      packed[j] = cell | (rank << 8);
+    }
+    __syncthreads();
+    // Rank tables: rmask[r] = cells holding more than r particles (lane = cell),
+    // rstart[r] = position of the first particle of rank r.
+    {
+      const uint32_t cnt = hist[lane];
+      uint32_t mx = cnt;
+      for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
+      uint32_t run = 0;
+      for (uint32_t r = 0; r < mx; ++r) {
+        const uint64_t m = __ballot(cnt > r);
+        if (lane == 0) {
+          rstart[r] = run;
+          rmask[r] = m;
+        }
+        run += (uint32_t)__popcll(m);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      const uint32_t qi = (uint32_t)(64 * j + lane);
+      if (qi < count) {
+        const uint32_t cell = packed[j] & 0xFFu, rank = packed[j] >> 8;
+        const uint32_t pos = rstart[rank] + (uint32_t)__popcll(rmask[rank] & ((1ull << cell) - 1ull));
+        order[min(pos, (uint32_t)KMAX - 1u)] = qi | (rank << 16);
+      }
+    }
+    __syncthreads();
+
+    // Pass B: rounds of 64 particles in (rank, cell) order.
+    for (uint32_t r0 = 0; r0 < count; r0 += 64) {
+      const uint32_t pos = r0 + (uint32_t)lane;
+      const bool valid = pos < count;
+      const uint32_t ord = valid ? order[pos] : 0u;
+      const uint32_t slot = start + (ord & 0xFFFFu);
+      const uint32_t myrank = ord >> 16;
+      const uint32_t i = min(s.perm[valid ? slot : start], (uint32_t)s.N - 1u);
+      float xp[3], vp[3], Cp[9];
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        xp[a] = in.x[a * Np + i];
+        vp[a] = in.v[a * Np + i];
+      }
+#pragma unroll
+      for (int k = 0; k < 9; ++k) Cp[k] = in.C[k * Np + i];
+
+      float tau_diag = 0.f;
+      float tau[9];
+      if (MAT == MPM_J_FLUID) {
+        float J = in.F[i];
+        if (pending) {
+          const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
+                              dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
+          J = J * det3(G);
+        }
+        const float K = HAS_E ? in.E[i] : s.E;
+        if (valid) {
+          out.F[slot] = J;
+          if (HAS_E) out.E[slot] = K;
+          if (!(J > 0.f)) flag_status(s, MPM_STATUS_INVERTED, 2);
+        }
+        tau_diag = K * J * (J - 1.f);
+      } else {
+        float Fp[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) Fp[k] = in.F[k * Np + i];
+        if (pending) {
+          float Fn[9];
+#pragma unroll
+          for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+            for (int c2 = 0; c2 < 3; ++c2)
+              Fn[r2 * 3 + c2] = Fp[r2 * 3 + c2] + dt * (Cp[r2 * 3 + 0] * Fp[0 * 3 + c2] + Cp[r2 * 3 + 1] * Fp[1 * 3 + c2] +
+                                                        Cp[r2 * 3 + 2] * Fp[2 * 3 + c2]);
+#pragma unroll
+          for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
+        }
+        const float E = HAS_E ? in.E[i] : s.E;
+        if (valid) {
+#pragma unroll
+          for (int k = 0; k < 9; ++k) out.F[k * Np + slot] = Fp[k];
+          if (HAS_E) out.E[slot] = E;
+        }
+        const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
+        float R[9];
+        const uint32_t st = rotation_of(Fp, R);
+        if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
+        const float J = det3(Fp);
+        float D[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) D[k] = 2.f * mu * (Fp[k] - R[k]);
+        const float vl = lam * (J - 1.f) * J;
+#pragma unroll
+        for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+          for (int c2 = 0; c2 < 3; ++c2)
+            tau[r2 * 3 + c2] = D[r2 * 3 + 0] * Fp[c2 * 3 + 0] + D[r2 * 3 + 1] * Fp[c2 * 3 + 1] +
+                               D[r2 * 3 + 2] * Fp[c2 * 3 + 2] + (r2 == c2 ? vl : 0.f);
+      }
+      // APIC affine momentum matrix A = m C - dt V0 (4/dx^2) tau.
+      float A[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const float t = (MAT == MPM_J_FLUID) ? ((k % 4 == 0) ? tau_diag : 0.f) : tau[k];
+        A[k] = mass * Cp[k] - s.stress_k * t;
+      }
+      int b[3];
+      float f[3], w[3][3];
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        const float xn = xp[a] * fn;
+        b[a] = base_node(xn);
+        f[a] = xn - (float)b[a];
+        bspline_weights(f[a], w[a]);
+      }
+      // momentum at node o: m v + A (o - f) dx
+      float q0[3], Ad[9];
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        q0[a] = mass * vp[a] - dx * (A[a * 3 + 0] * f[0] + A[a * 3 + 1] * f[1] + A[a * 3 + 2] * f[2]);
+#pragma unroll
+        for (int c2 = 0; c2 < 3; ++c2) Ad[a * 3 + c2] = dx * A[a * 3 + c2];
+      }
+      const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
+                lz = min(max(b[2] - oz0, 0), CB - 1);
+      const int li0 = (lz * PW + ly) * PW + lx;
+
+      // One pass per distinct rank present in this round.
+      bool todo = valid;
+      for (;;) {
+        const uint64_t tm = __ballot(todo);
+        if (tm == 0ull) break;
+        const uint32_t rnow = (uint32_t)__builtin_amdgcn_readlane((int)myrank, __ffsll((unsigned long long)tm) - 1);
+        if (todo && myrank == rnow) {
+#pragma unroll
+          for (int oz = 0; oz < 3; ++oz)
+#pragma unroll
+            for (int oy = 0; oy < 3; ++oy) {
+              const float wyz = w[1][oy] * w[2][oz];
+#pragma unroll
+              for (int ox = 0; ox < 3; ++ox) {
+                const float wt = w[0][ox] * wyz;
+                const int li = li0 + (oz * PW + oy) * PW + ox;
+                float4 g = win[li];
+                g.x += wt * mass;
+                g.y += wt * (q0[0] + Ad[0] * ox + Ad[1] * oy + Ad[2] * oz);
+                g.z += wt * (q0[1] + Ad[3] * ox + Ad[4] * oy + Ad[5] * oz);
+                g.w += wt * (q0[2] + Ad[6] * ox + Ad[7] * oy + Ad[8] * oz);
+                win[li] = g;
+                // keep this read-modify-write ahead of the next one in issue order
+                __asm__ __volatile__("" ::: "memory");
+              }
+            }
+          todo = false;
+        }
+      }
+    }
+    __syncthreads();
+
+    // Flush: one native global float atomic per nonzero window value.
+    uint32_t mark = 0u;
+    for (int k = lane; k < PW3; k += 64) {
+      const float4 g = win[k];
+      const int wx = k % PW, wy = (k / PW) % PW, wz = k / (PW * PW);
+      const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+      if (g.x != 0.f && gx < s.n && gy < s.n && gz < s.n) {
+        float *dst = reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz));
+        unsafeAtomicAdd(dst + 0, g.x);
+        unsafeAtomicAdd(dst + 1, g.y);
+        unsafeAtomicAdd(dst + 2, g.z);
+        unsafeAtomicAdd(dst + 3, g.w);
+        const int bit = (((gz >> 3) - (oz0 >> 3)) << 2) | (((gy >> 3) - (oy0 >> 3)) << 1) | ((gx >> 3) - (ox0 >> 3));
+        mark |= 1u << bit;
+      }
+    }
+    for (int d = 32; d >= 1; d >>= 1) mark |= (uint32_t)__shfl_xor((int)mark, d);
+    if (lane < 8 && ((mark >> lane) & 1u)) {
+      const uint32_t nbk = ((uint32_t)((oz0 >> 3) + (lane >> 2)) * s.nb + (uint32_t)((oy0 >> 3) + ((lane >> 1) & 1))) * s.nb +
+                           (uint32_t)((ox0 >> 3) + (lane & 1));
+      if (atomicExch(&s.active_flag[nbk], 1u) == 0u) s.active_list[atomicAdd(&s.ctr[CTR_NACTIVE], 1u)] = nbk;
+    }
+    __syncthreads();
+  }
+}
+
+// Grid update over the active node-blocks: v = p/m + dt g where m > 0, sticky
+// walls, store (v, m), clear the accumulator and the block's flag.
+__global__ __launch_bounds__(WG) void k_grid_update(SimDev s) {
+  const uint32_t nact = s.ctr[CTR_NACTIVE];
+  const int n = s.n, wall = s.wall;
+  for (uint32_t a = blockIdx.x; a < nact; a += gridDim.x) {
+    const uint32_t blk = s.active_list[a];
+    const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
+              bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
+#pragma unroll
+    for (int j = 0; j < 512 / WG; ++j) {
+      const int local = threadIdx.x + WG * j;
+      const int gx = bx * NB + (local & 7), gy = by * NB + ((local >> 3) & 7), gz = bz * NB + (local >> 6);
+      const size_t gi = ((size_t)blk << 9) + local;
+      const float4 acc = s.gridA[gi];
+      float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
+      const bool in_wall = gx < wall || gy < wall || gz < wall || gx >= n - wall || gy >= n - wall || gz >= n - wall;
+      if (acc.x > 0.f && !in_wall) {
+        o.x = acc.y / acc.x + s.dt * s.g[0];
+        o.y = acc.z / acc.x + s.dt * s.g[1];
+        o.z = acc.w / acc.x + s.dt * s.g[2];
+      }
+      s.gridV[gi] = o;
+      s.gridA[gi] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (threadIdx.x == 0) s.active_flag[blk] = 0u;
+  }
+}
+
+// G2P: gather, APIC C, advection and clamp; writes the new state in sorted
+// (slot) order and the next step's block key and count.
+template <int MAT>
+__global__ __launch_bounds__(WG) void k_g2p(SimDev s, int src) {
+  const PBuf in = s.buf[src], out = s.buf[src ^ 1];
+  const uint32_t slot = xcd_local_block(blockIdx.x, gridDim.x) * WG + threadIdx.x;
+  const bool valid = slot < (uint32_t)s.N;
+  const int Np = s.Np;
+  const float fn = s.fn;
+  uint32_t key = 0;
+  if (valid) {
+    const uint32_t i = min(s.perm[slot], (uint32_t)s.N - 1u);
+    float xp[3];
+    int b[3];
+    float w[3][3], d[3][3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      xp[a] = in.x[a * Np + i];
+      const float xn = xp[a] * fn;
+      b[a] = base_node(xn);
+      const float f = xn - (float)b[a];
+      bspline_weights(f, w[a]);
+      d[a][0] = -f;
+      d[a][1] = 1.f - f;
+      d[a][2] = 2.f - f;
+    }
+    float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int oz = 0; oz < 3; ++oz)
+#pragma unroll
+      for (int oy = 0; oy < 3; ++oy) {
+        const float wyz = w[1][oy] * w[2][oz];
+#pragma unroll
+        for (int ox = 0; ox < 3; ++ox) {
+          const float4 g = s.gridV[node_index(s, b[0] + ox, b[1] + oy, b[2] + oz)];
+          const float wt = w[0][ox] * wyz;
+          const float wv[3] = {wt * g.x, wt * g.y, wt * g.z};
+#pragma unroll
+          for (int a = 0; a < 3; ++a) {
+            v[a] += wv[a];
+            B[a * 3 + 0] += wv[a] * d[0][ox];
+            B[a * 3 + 1] += wv[a] * d[1][oy];
+            B[a * 3 + 2] += wv[a] * d[2][oz];
+          }
+        }
+      }
+    bool clamped = false, nonfinite = false;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      float xa = xp[a] + s.dt * v[a];
+      if (!isfinite(xa) || !isfinite(v[a])) nonfinite = true;
+      if (xa < s.lo || xa > s.hi) clamped = true;
+      xa = fminf(fmaxf(xa, s.lo), s.hi);
+      out.x[a * Np + slot] = xa;
+      out.v[a * Np + slot] = v[a];
+      b[a] = base_node(xa * fn);
+    }
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const float ck = s.c_scale * B[k];
+      if (!isfinite(ck)) nonfinite = true;
+      out.C[k * Np + slot] = ck;
+    }
+    out.id[slot] = in.id[i];
+    key = bin_key(s, b[0], b[1], b[2]);
+    s.key[slot] = key;
+    if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
+    if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
+  }
+  wave_aggregated_increment(s.bin_count, key, valid);
+  if (blockIdx.x == 0 && threadIdx.x == 0) s.ctr[CTR_PENDING] = 1u;
+}
+
+// Readback: unpermute to creation order, apply the pending F (or J) update.
+template <int MAT>
+__global__ __launch_bounds__(WG) void k_read_particles(SimDev s, int cur, float *__restrict__ x, float *__restrict__ v,
+                                                       float *__restrict__ C, float *__restrict__ F) {
+  const uint32_t slot = blockIdx.x * WG + threadIdx.x;
+  if (slot >= (uint32_t)s.N) return;
+  const PBuf b = s.buf[cur];
+  const int Np = s.Np;
+  const size_t id = b.id[slot];
+  if (id >= (size_t)s.N) return;
+  const bool pending = s.ctr[CTR_PENDING] != 0u;
+  float Cp[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) Cp[k] = b.C[k * Np + slot];
+  for (int a = 0; a < 3; ++a) {
+    if (x) x[3 * id + a] = b.x[a * Np + slot];
+    if (v) v[3 * id + a] = b.v[a * Np + slot];
+  }
+  if (C)
+    for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
+  if (!F) return;
+  const float dt = s.dt;
+  if (MAT == MPM_J_FLUID) {
+    float J = b.F[slot];
+    if (pending) {
+      const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
+                          dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
+      J = J * det3(G);
+    }
+    F[id] = J;
+  } else {
+    float Fp[9];
+    for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
+    for (int r = 0; r < 3; ++r)
+      for (int c = 0; c < 3; ++c) {
+        float val = Fp[r * 3 + c];
+        if (pending)
+          val += dt * (Cp[r * 3 + 0] * Fp[0 * 3 + c] + Cp[r * 3 + 1] * Fp[1 * 3 + c] + Cp[r * 3 + 2] * Fp[2 * 3 + c]);
+        F[9 * id + r * 3 + c] = val;
+      }
+  }
+}
+
+// Readback of the grid: active blocks -> dense (i + n (j + n k)) arrays.
+__global__ __launch_bounds__(WG) void k_read_grid(SimDev s, float *__restrict__ mass, float *__restrict__ mom) {
+  const uint32_t nact = s.ctr[CTR_NACTIVE];
+  const int n = s.n;
+  for (uint32_t a = blockIdx.x; a < nact; a += gridDim.x) {
+    const uint32_t blk = s.active_list[a];
+    const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
+              bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
+    for (int local = threadIdx.x; local < 512; local += WG) {
+      const int gx = bx * NB + (local & 7), gy = by * NB + ((local >> 3) & 7), gz = bz * NB + (local >> 6);
+      if (gx >= n || gy >= n || gz >= n) continue;
+      const float4 g = s.gridV[((size_t)blk << 9) + local];
+      const size_t lin = (size_t)gx + (size_t)n * ((size_t)gy + (size_t)n * gz);
+      if (mass) mass[lin] = g.w;
+      if (mom) {
+        mom[3 * lin + 0] = g.w * g.x;
+        mom[3 * lin + 1] = g.w * g.y;
+        mom[3 * lin + 2] = g.w * g.z;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- host side
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool valid_params(const mpm_params *p) {
+  if (!p || p->struct_size < sizeof(mpm_params)) return false;
+  if (p->grid_n < 8 || p->grid_n > 1024) return false;
+  if (!(p->dt > 0.f) || !std::isfinite(p->dt)) return false;
+  for (int a = 0; a < 3; ++a)
+    if (!std::isfinite(p->gravity[a])) return false;
+  if (p->wall_nodes < 0 || p->wall_nodes > p->grid_n / 2) return false;
+  if (p->material != MPM_FIXED_COROTATED && p->material != MPM_J_FLUID) return false;
+  if (!(p->E >= 0.f) || !std::isfinite(p->E)) return false;
+  if (p->material == MPM_FIXED_COROTATED && !(p->nu >= 0.f && p->nu < 0.5f)) return false;
+  if (!(p->rho > 0.f) || !std::isfinite(p->rho)) return false;
+  if (!(p->p_vol > 0.f) || !std::isfinite(p->p_vol)) return false;
+  return true;
+}
+
+// Workspace layout; with base == nullptr only the size is computed.
+size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d) {
+  const int64_t Np = ((N + 63) / 64) * 64;
+  const int n = p->grid_n, nb = (n + NB - 1) / NB;
+  const int64_t nblk = (int64_t)nb * nb * nb;
+  const int nbin = (n + CB - 1) / CB;
+  const int64_t nbins = (int64_t)nbin * nbin * nbin;
+  const int64_t max_chunks = (N + KMAX - 1) / KMAX + nbins;
+  const int fw = p->material == MPM_J_FLUID ? 1 : 9;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char * {
+    char *ptr = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  PBuf bufs[2];
+  for (int k = 0; k < 2; ++k) {
+    bufs[k].x = (float *)take(sizeof(float) * 3 * Np);
+    bufs[k].v = (float *)take(sizeof(float) * 3 * Np);
+    bufs[k].C = (float *)take(sizeof(float) * 9 * Np);
+    bufs[k].F = (float *)take(sizeof(float) * fw * Np);
+    bufs[k].E = has_E ? (float *)take(sizeof(float) * Np) : nullptr;
+    bufs[k].id = (uint32_t *)take(sizeof(uint32_t) * Np);
+  }
+  uint32_t *perm = (uint32_t *)take(sizeof(uint32_t) * Np);
+  uint32_t *key = (uint32_t *)take(sizeof(uint32_t) * Np);
+  uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
+  uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
+  const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
+  uint32_t *tiles = (uint32_t *)take(sizeof(uint32_t) * 2 * ntiles);
+  uint32_t *aflag = (uint32_t *)take(sizeof(uint32_t) * nblk);
+  uint32_t *alist = (uint32_t *)take(sizeof(uint32_t) * nblk);
+  uint4 *chunks = (uint4 *)take(sizeof(uint4) * max_chunks);
+  uint32_t *ctr = (uint32_t *)take(sizeof(uint32_t) * CTR_WORDS);
+  uint32_t *status = (uint32_t *)take(sizeof(uint32_t) * MPM_STATUS_WORDS);
+  float4 *gA = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  float4 *gV = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  if (d) {
+    d->N = (int32_t)N;
+    d->Np = (int32_t)Np;
+    d->n = n;
+    d->nb = nb;
+    d->nblk = (int32_t)nblk;
+    d->nbin = nbin;
+    d->nbins = (int32_t)nbins;
+    d->wall = p->wall_nodes;
+    d->material = p->material;
+    d->has_E = has_E ? 1 : 0;
+    d->dx = 1.0f / (float)n;
+    d->fn = (float)n;
+    d->dt = p->dt;
+    for (int a = 0; a < 3; ++a) d->g[a] = p->gravity[a];
+    d->mass = p->rho * p->p_vol;
+    d->vol = p->p_vol;
+    d->E = p->E;
+    const double nu = p->material == MPM_J_FLUID ? 0.0 : (double)p->nu;
+    // Fluid: tau = K J (J-1) I uses E as K directly; mu/lam unused.
+    d->mu_per_E = (float)(1.0 / (2.0 * (1.0 + nu)));
+    d->lam_per_E = (float)(nu / ((1.0 + nu) * (1.0 - 2.0 * nu)));
+    d->stress_k = (float)((double)p->dt * (double)p->p_vol * 4.0 * (double)n * (double)n);
+    d->c_scale = (float)(4.0 * n);
+    d->lo = 2.0f * d->dx;
+    d->hi = (float)(n - 2) * d->dx;
+    d->max_chunks = (uint32_t)max_chunks;
+    d->buf[0] = bufs[0];
+    d->buf[1] = bufs[1];
+    d->perm = perm;
+    d->key = key;
+    d->bin_count = cnt;
+    d->bin_cursor = cur;
+    d->tile_sum = tiles;
+    d->ntiles = (int32_t)ntiles;
+    d->active_flag = aflag;
+    d->active_list = alist;
+    d->chunks = chunks;
+    d->ctr = ctr;
+    d->status = status;
+    d->gridA = gA;
+    d->gridV = gV;
+  }
+  return off;
+}
+
+const char *const KERNEL_NAMES[NUM_KERNELS] = {"k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g", "k_grid_update",
+                                               "k_g2p"};
+
+}  // namespace
+
+struct mpm_sim {
+  SimDev d;
+  int device = 0;
+  int cur = 0;  // buffer holding the current state
+  int64_t steps = 0;
+  hipStream_t cap = nullptr;
+  hipGraph_t graph[2] = {nullptr, nullptr};
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
+  int grid_p2g = 0;
+  int grid_update = 0;
+};
+
+namespace {
+
+#define HIP_TRY(expr)                        \
+  do {                                       \
+    if ((expr) != hipSuccess) return MPM_ERR_HIP; \
+  } while (0)
+
+int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
+  const SimDev &d = sim->d;
+  switch (k) {
+    case 0:
+      k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
+      break;
+    case 1:
+      k_scan_bins<<<d.ntiles, WG, 0, st>>>(d);
+      break;
+    case 2:
+      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
+      break;
+    case 3:
+      if (d.material == MPM_J_FLUID) {
+        if (d.has_E) k_p2g<MPM_J_FLUID, true><<<sim->grid_p2g, 64, 0, st>>>(d, src);
+        else k_p2g<MPM_J_FLUID, false><<<sim->grid_p2g, 64, 0, st>>>(d, src);
+      } else {
+        if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true><<<sim->grid_p2g, 64, 0, st>>>(d, src);
+        else k_p2g<MPM_FIXED_COROTATED, false><<<sim->grid_p2g, 64, 0, st>>>(d, src);
+      }
+      break;
+    case 4:
+      k_grid_update<<<sim->grid_update, WG, 0, st>>>(d);
+      break;
+    case 5:
+      if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_particles, WG, 0, st>>>(d, src);
+      else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_particles, WG, 0, st>>>(d, src);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
+int enqueue_step(mpm_sim *sim, hipStream_t st, int src) {
+  for (int k = 0; k < NUM_KERNELS; ++k) {
+    const int rc = launch_kernel(sim, k, st, src);
+    if (rc) return rc;
+  }
+  return MPM_OK;
+}
+
+int build_graphs(mpm_sim *sim) {
+  for (int src = 0; src < 2; ++src) {
+    HIP_TRY(hipStreamBeginCapture(sim->cap, hipStreamCaptureModeThreadLocal));
+    const int rc = enqueue_step(sim, sim->cap, src);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(sim->cap, &g);
+    if (rc || e != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      return MPM_ERR_HIP;
+    }
+    sim->graph[src] = g;
+    HIP_TRY(hipGraphInstantiate(&sim->exec[src], g, nullptr, nullptr, 0));
+  }
+  return MPM_OK;
+}
+
+void release(mpm_sim *sim) {
+  if (!sim) return;
+  for (int k = 0; k < 2; ++k) {
+    if (sim->exec[k]) (void)hipGraphExecDestroy(sim->exec[k]);
+    if (sim->graph[k]) (void)hipGraphDestroy(sim->graph[k]);
+  }
+  if (sim->cap) {
+    (void)hipStreamSynchronize(sim->cap);
+    (void)hipStreamDestroy(sim->cap);
+  }
+  delete sim;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles) {
+  if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 31)) return 0;
+  // The per-particle modulus array is always reserved so that one size fits
+  // both the uniform and the per-particle case.
+  return layout(params, n_particles, true, nullptr, nullptr);
+}
+
+int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, const float *v0, const float *C0,
+               const float *F0, const float *E_p, void *workspace, size_t workspace_bytes, void *stream,
+               mpm_sim **out) {
+  if (!out) return MPM_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 31)) return MPM_ERR_INVALID_ARG;
+  if (n_particles > 0 && !x0) return MPM_ERR_INVALID_ARG;
+  const size_t need = mpm_workspace_bytes(params, n_particles);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+    return MPM_ERR_WORKSPACE;
+
+  mpm_sim *sim = new (std::nothrow) mpm_sim();
+  if (!sim) return MPM_ERR_STATE;
+  const bool has_E = E_p != nullptr;
+  layout(params, n_particles, has_E, static_cast<char *>(workspace), &sim->d);
+  const SimDev &d = sim->d;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  int rc = MPM_OK;
+  do {
+    if (hipGetDevice(&sim->device) != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, sim->device) != hipSuccess || cus <= 0)
+      cus = 256;
+    sim->grid_particles = (int)(((d.N + WG - 1) / WG + 7) / 8 * 8);
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_p2g<MPM_FIXED_COROTATED, false>, 64, 0) != hipSuccess ||
+        occ <= 0)
+      occ = 16;
+    sim->grid_p2g = ((cus * occ + NQ - 1) / NQ) * NQ;
+    sim->grid_update = cus * 8;
+    if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
+
+    // Clear counters, flags, status and the P2G accumulator, then upload.
+    k_zero_u32<<<1, WG, 0, st>>>(d.ctr, CTR_WORDS);
+    k_zero_u32<<<1, WG, 0, st>>>(d.status, MPM_STATUS_WORDS);
+    const int zb = (int)std::min<int64_t>(((int64_t)d.nbins + WG - 1) / WG, 4096);
+    k_zero_u32<<<zb, WG, 0, st>>>(d.bin_count, (size_t)d.nbins);
+    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag, (size_t)d.nblk);
+    const int gb = (int)std::min<int64_t>(((int64_t)d.nblk * 512 * 4 + WG - 1) / WG, 16384);
+    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA), (size_t)d.nblk * 512 * 4);
+    // G2P may read a stencil node whose weight is exactly zero and that no
+    // particle marked active; it must hold a finite value, so start at zero.
+    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridV), (size_t)d.nblk * 512 * 4);
+    if (d.N > 0) k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
+    if (hipGetLastError() != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    if (d.N > 0) rc = build_graphs(sim);
+  } while (0);
+  if (rc != MPM_OK) {
+    release(sim);
+    return rc;
+  }
+  *out = sim;
+  return MPM_OK;
+}
+
+int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
+  if (!sim || n_steps < 0) return MPM_ERR_INVALID_ARG;
+  if (sim->d.N == 0) {
+    sim->steps += n_steps;
+    return MPM_OK;
+  }
+  if (!sim->exec[0] || !sim->exec[1]) return MPM_ERR_STATE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t k = 0; k < n_steps; ++k) {
+    if (hipGraphLaunch(sim->exec[sim->cur], st) != hipSuccess) return MPM_ERR_HIP;
+    sim->cur ^= 1;
+    sim->steps += 1;
+  }
+  return MPM_OK;
+}
+
+int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms) {
+  if (!sim || n_steps < 0 || !kernel_ms) return MPM_ERR_INVALID_ARG;
+  if (sim->d.N == 0) {
+    sim->steps += n_steps;
+    return MPM_OK;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[NUM_KERNELS + 1];
+  for (int k = 0; k <= NUM_KERNELS; ++k)
+    if (hipEventCreate(&ev[k]) != hipSuccess) return MPM_ERR_HIP;
+  int rc = MPM_OK;
+  for (int32_t s = 0; s < n_steps && rc == MPM_OK; ++s) {
+    if (hipEventRecord(ev[0], st) != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    for (int k = 0; k < NUM_KERNELS && rc == MPM_OK; ++k) {
+      rc = launch_kernel(sim, k, st, sim->cur);
+      if (rc == MPM_OK && hipEventRecord(ev[k + 1], st) != hipSuccess) rc = MPM_ERR_HIP;
+    }
+    if (rc != MPM_OK) break;
+    if (hipEventSynchronize(ev[NUM_KERNELS]) != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    for (int k = 0; k < NUM_KERNELS; ++k) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) { rc = MPM_ERR_HIP; break; }
+      kernel_ms[k] += ms;
+    }
+    sim->cur ^= 1;
+    sim->steps += 1;
+  }
+  for (int k = 0; k <= NUM_KERNELS; ++k) (void)hipEventDestroy(ev[k]);
+  return rc;
+}
+
+int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J, void *stream) {
+  if (!sim) return MPM_ERR_INVALID_ARG;
+  if (sim->d.N == 0) return MPM_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int g = (sim->d.N + WG - 1) / WG;
+  if (sim->d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, WG, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
+  else k_read_particles<MPM_FIXED_COROTATED><<<g, WG, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
+int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream) {
+  if (!sim) return MPM_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t nn = (size_t)sim->d.n * sim->d.n * sim->d.n;
+  const int zb = (int)std::min<size_t>((nn * 3 + WG - 1) / WG, 16384);
+  if (mass) k_zero_f32<<<zb, WG, 0, st>>>(mass, nn);
+  if (momentum) k_zero_f32<<<zb, WG, 0, st>>>(momentum, 3 * nn);
+  if (sim->d.N > 0 && sim->steps > 0) k_read_grid<<<sim->grid_update, WG, 0, st>>>(sim->d, mass, momentum);
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
+int mpm_status(mpm_sim *sim, uint32_t *status_device, void *stream) {
+  if (!sim || !status_device) return MPM_ERR_INVALID_ARG;
+  if (hipMemcpyAsync(status_device, sim->d.status, sizeof(uint32_t) * MPM_STATUS_WORDS, hipMemcpyDeviceToDevice,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MPM_ERR_HIP;
+  return MPM_OK;
+}
+
+int64_t mpm_steps_taken(const mpm_sim *sim) { return sim ? sim->steps : -1; }
+
+int32_t mpm_num_kernels(void) { return NUM_KERNELS; }
+
+const char *mpm_kernel_name(int32_t k) { return (k >= 0 && k < NUM_KERNELS) ? KERNEL_NAMES[k] : nullptr; }
+
+void mpm_destroy(mpm_sim *sim) { release(sim); }
+
+const char *mpm_error_string(int code) {
+  switch (code) {
+    case MPM_OK: return "ok";
+    case MPM_ERR_INVALID_ARG: return "invalid argument";
+    case MPM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MPM_ERR_HIP: return "HIP runtime error";
+    case MPM_ERR_STATE: return "simulation handle not usable";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

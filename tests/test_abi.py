@@ -1,0 +1,118 @@
+"""The C-ABI library loads on the CPU, exports every symbol include/mpm.h
+declares, and rejects invalid arguments on the host before any GPU work.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import material_point_physics_amd as mpm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(mpm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mpm.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {mpm.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_library_is_gfx950_only():
+    """The embedded offload bundle names gfx950 and no other GPU target."""
+    data = open(mpm.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[a-z-]*(gfx[0-9a-f]+)", data))
+    assert targets == {b"gfx950"}, targets
+
+
+def good_params(**kw):
+    d = dict(n=32, dt=1e-4, gravity=(0, -9.8, 0), wall=3, material=0, E=1e4, nu=0.2, rho=1.0, p_vol=1e-6)
+    d.update(kw)
+    return mpm.make_params(**d)
+
+
+def test_workspace_bytes_scales_and_rejects_bad_params():
+    a = mpm.mpm_workspace_bytes(good_params(), 1000)
+    b = mpm.mpm_workspace_bytes(good_params(), 2000)
+    c = mpm.mpm_workspace_bytes(good_params(n=64), 1000)
+    assert 0 < a < b and a < c
+    assert mpm.mpm_workspace_bytes(good_params(), 0) > 0
+    for bad in [dict(n=4), dict(n=2048), dict(dt=0.0), dict(dt=float("nan")), dict(wall=-1), dict(wall=20),
+                dict(material=7), dict(E=-1.0), dict(nu=0.5), dict(rho=0.0), dict(p_vol=0.0),
+                dict(gravity=(0, float("inf"), 0))]:
+        assert mpm.mpm_workspace_bytes(good_params(**bad), 1000) == 0, bad
+    assert mpm.mpm_workspace_bytes(good_params(), -1) == 0
+    assert mpm.mpm_workspace_bytes(good_params(), 1 << 31) == 0
+    p = good_params()
+    p.struct_size = 8
+    assert mpm.mpm_workspace_bytes(p, 10) == 0
+
+
+def test_create_rejects_bad_arguments_before_any_launch():
+    L = mpm.lib()
+    p = good_params()
+    need = mpm.mpm_workspace_bytes(p, 100)
+    out = ctypes.c_void_p(123)
+    fake = 1 << 40  # never dereferenced: every case below fails host validation
+    # NULL out pointer
+    assert L.mpm_create(ctypes.byref(p), 100, fake, None, None, None, None, fake, need, None, None) == mpm.MPM_ERR_INVALID_ARG
+    # invalid params
+    bad = good_params(n=3)
+    assert L.mpm_create(ctypes.byref(bad), 100, fake, None, None, None, None, fake, need, None,
+                        ctypes.byref(out)) == mpm.MPM_ERR_INVALID_ARG
+    assert out.value is None
+    # negative N, missing positions
+    assert L.mpm_create(ctypes.byref(p), -5, fake, None, None, None, None, fake, need, None,
+                        ctypes.byref(out)) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_create(ctypes.byref(p), 100, None, None, None, None, None, fake, need, None,
+                        ctypes.byref(out)) == mpm.MPM_ERR_INVALID_ARG
+    # workspace: missing, misaligned, too small
+    assert L.mpm_create(ctypes.byref(p), 100, fake, None, None, None, None, None, need, None,
+                        ctypes.byref(out)) == mpm.MPM_ERR_WORKSPACE
+    assert L.mpm_create(ctypes.byref(p), 100, fake, None, None, None, None, fake + 4, need, None,
+                        ctypes.byref(out)) == mpm.MPM_ERR_WORKSPACE
+    assert L.mpm_create(ctypes.byref(p), 100, fake, None, None, None, None, fake, need - 1, None,
+                        ctypes.byref(out)) == mpm.MPM_ERR_WORKSPACE
+    assert out.value is None
+
+
+def test_null_handle_calls_are_rejected():
+    L = mpm.lib()
+    assert L.mpm_step(None, 1, None) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_read_particles(None, None, None, None, None, None) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_read_grid(None, None, None, None) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_status(None, None, None) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_steps_taken(None) == -1
+    buf = (ctypes.c_float * 8)()
+    assert L.mpm_step_profiled(None, 1, None, buf) == mpm.MPM_ERR_INVALID_ARG
+    L.mpm_destroy(None)  # no-op
+
+
+def test_error_strings_and_kernel_names():
+    for code in [0, -1, -2, -3, -4]:
+        assert mpm.mpm_error_string(code) != "unknown error"
+    assert mpm.mpm_error_string(-99) == "unknown error"
+    nk = mpm.mpm_num_kernels()
+    assert nk == 6
+    names = [mpm.mpm_kernel_name(k) for k in range(nk)]
+    assert names == ["k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g", "k_grid_update", "k_g2p"]
+    assert mpm.mpm_kernel_name(nk) is None and mpm.mpm_kernel_name(-1) is None
+
+
+def test_params_struct_matches_header():
+    # uint32 + int32 + float + float[3] + int32 + int32 + 4 floats = 48 bytes
+    assert ctypes.sizeof(mpm.mpm_params) == 48

@@ -1,0 +1,113 @@
+"""GPU parity at the full workload sizes, in the benchmark's launch
+configuration, on outputs the oracle can compute one by one, plus properties
+that hold at any size.
+
+Sampled outputs: after one step, a grid node's mass and momentum depend only
+on particles within 2 cells of it, and a particle's new state only on grid
+nodes within 2 cells, hence on particles within 4 cells.  The oracle steps the
+neighbourhood subset (all particles within 4 cells of the sampled particles)
+on the full grid, which makes those sampled values exact.
+"""
+import numpy as np
+import pytest
+
+import material_point_physics_amd as mpm
+from material_point_physics_amd import scenes
+import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["slab_12m", "dambreak_4m"])
+def test_full_size_sampled_parity(name):
+    sc = scenes.SCENES[name]()
+    pu.log(f"full-size {name}: N={sc.N} n={sc.n}")
+    gpu = pu.gpu_run(sc, 1)
+    rng = np.random.default_rng(2024)
+    sample = rng.choice(sc.N, 48, replace=False)
+    idx = pu.neighbourhood(sc.x, sc.x[sample], sc.n, 4)
+    pu.log(f"oracle on a neighbourhood of {len(idx)} particles")
+    sub = pu.subset_scene(sc, idx)
+    orc = pu.oracle_run(sub, 1)
+    pos = {int(g): k for k, g in enumerate(idx)}
+    ks = np.array([pos[int(p)] for p in sample])
+    # particles
+    got = dict(x=gpu["x"][sample], v=gpu["v"][sample], C=gpu["C"][sample], F=gpu["F"][sample])
+    ref_v = orc.v[ks]
+    vs = max(np.abs(ref_v).max(), 1e-30)
+    ex = np.abs(got["x"] - orc.x[ks]).max()
+    ev = np.abs(got["v"] - ref_v).max() / vs
+    eC = np.abs(got["C"] - orc.C[ks]).max() / (4 * sc.n * vs + np.abs(orc.C[ks]).max())
+    refF = orc.J[ks] if sc.material == scenes.J_FLUID else orc.F[ks]
+    eF = np.abs(got["F"] - refF).max()
+    pu.log(f"{name} sampled particles: x {ex:.2e} v {ev:.2e} C {eC:.2e} F {eF:.2e}")
+    assert ex < 1e-6 and ev < 1e-5 and eC < 1e-5 and eF < 1e-6
+    # grid nodes in the stencils of the sampled particles
+    n = sc.n
+    b = np.floor(sc.x[sample].astype(np.float64) * n - 0.5).astype(int)
+    nodes = np.unique(np.concatenate([b + np.array([ox, oy, oz]) for ox in range(3) for oy in range(3)
+                                      for oz in range(3)]), axis=0)
+    m_ref = orc.grid_mass()[nodes[:, 2], nodes[:, 1], nodes[:, 0]]
+    p_ref = orc.grid_momentum()[nodes[:, 2], nodes[:, 1], nodes[:, 0]]
+    m_got = gpu["m"][nodes[:, 2], nodes[:, 1], nodes[:, 0]]
+    p_got = gpu["p"][nodes[:, 2], nodes[:, 1], nodes[:, 0]]
+    em = np.abs(m_got - m_ref).max() / np.abs(m_ref).max()
+    ep = np.abs(p_got - p_ref).max() / max(np.abs(p_ref).max(), 1e-30)
+    pu.log(f"{name} sampled nodes ({len(nodes)}): mass {em:.2e} momentum {ep:.2e}")
+    assert em <= 1e-5 and ep <= 1e-5
+    # mass total over the whole grid
+    m_p = np.float64(sc.params()["rho"]) * sc.params()["p_vol"]
+    assert abs(gpu["m"].astype(np.float64).sum() - m_p * sc.N) / (m_p * sc.N) < 1e-6
+    assert gpu["status"][0] == 0
+
+
+def test_conservation_100_steps():
+    """Colliding blocks with gravity off and no wall contact: grid mass equals
+    particle mass and total momentum is unchanged, within 1e-6 relative
+    (momentum normalised by sum m|v|, since the blocks' momenta cancel)."""
+    sc = scenes.blocks_1m(gravity=False)
+    pu.log("conservation over 100 steps")
+    sim = mpm.Simulation(sc)
+    try:
+        m_p = np.float64(sc.params()["rho"]) * sc.params()["p_vol"]
+        v0 = sc.v.astype(np.float64)
+        P0 = m_p * v0.sum(0)
+        scale = m_p * np.linalg.norm(v0, axis=1).sum()
+        for k in range(4):
+            sim.step(25)
+            m, _ = sim.read_grid()
+            x, v, C, F = sim.read_particles()
+            M = m.double().sum().item()
+            P = m_p * v.double().sum(0).cpu().numpy()
+            pu.log(f"step {25 * (k + 1)}: mass err {abs(M - m_p * sc.N) / (m_p * sc.N):.2e}, "
+                   f"momentum err {np.abs(P - P0).max() / scale:.2e}")
+            assert abs(M - m_p * sc.N) / (m_p * sc.N) < 1e-6
+            assert np.abs(P - P0).max() / scale < 1e-6
+        st = sim.status()
+        assert st[0] == 0, st
+    finally:
+        sim.close()
+
+
+def test_gravity_momentum_free_fall_totals():
+    """With gravity on and no wall contact, total momentum grows by M g t."""
+    sc = scenes.random_scene(200000, 64, 91, lo=[0.3] * 3, hi=[0.7] * 3, vscale=1.0, cscale=5.0,
+                             fstretch=0.05, dt=5e-5)
+    pu.log("momentum under gravity")
+    sim = mpm.Simulation(sc)
+    try:
+        prm = sc.params()
+        m_p = np.float64(prm["rho"]) * prm["p_vol"]
+        M = m_p * sc.N
+        P0 = m_p * sc.v.astype(np.float64).sum(0)
+        steps = 50
+        sim.step(steps)
+        _, v, _, _ = sim.read_particles()
+        P = m_p * v.double().sum(0).cpu().numpy()
+        expect = P0 + M * steps * prm["dt"] * np.array(prm["gravity"])
+        scale = m_p * np.linalg.norm(sc.v.astype(np.float64), axis=1).sum()
+        err = np.abs(P - expect).max() / scale
+        pu.log(f"momentum vs P0 + M g t: {err:.2e}")
+        assert err < 1e-6
+    finally:
+        sim.close()
