@@ -59,9 +59,7 @@ constexpr int NUM_KERNELS = 6;
 
 enum Ctr : int {
   CTR_NCHUNKS = 0,
-  CTR_NACTIVE = 1,
   CTR_PENDING = 2,
-  CTR_QHEAD = 8,   // NQ queue heads
   CTR_WORDS = 16,
 };
 
@@ -77,7 +75,7 @@ struct PBuf {
 struct SimDev {
   int32_t N, Np;
   int32_t n, nb, nblk;         // grid nodes per axis, node-blocks per axis, node-blocks
-  int32_t nbin, nbins;         // bins per axis, bins
+  int32_t nbin, nbins;         // bins per axis, bins (Morton-ordered: nbins = (2^ceil(log2 nbin))^3)
   int32_t wall, material, has_E;
   float dx, fn, dt;
   float g[3];
@@ -89,11 +87,12 @@ struct SimDev {
   uint32_t max_chunks;
   PBuf buf[2];
   uint32_t *perm, *key;
+  uint32_t *src_of;  // storage slot -> source index, in P2G processing order (read by G2P)
   uint32_t *bin_count, *bin_cursor;
   uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
   int32_t ntiles;
   uint4 *chunks;
-  uint32_t *active_flag, *active_list;
+  uint32_t *active_flag;  // per node-block state, see k_grid_update
   float4 *gridA;  // P2G accumulator per node: (m, p_x, p_y, p_z)
   float4 *gridV;  // updated grid per node: (v_x, v_y, v_z, m)
   uint32_t *ctr;
@@ -113,9 +112,29 @@ __device__ __forceinline__ uint32_t node_index(const SimDev &s, int gx, int gy, 
 // Base node floor(x/dx - 1/2) of a position already inside the clamp box.
 __device__ __forceinline__ int base_node(float xn) { return (int)floorf(xn - 0.5f); }
 
-// Bin of a base node: 4^3-cell bins, x fastest.
-__device__ __forceinline__ uint32_t bin_key(const SimDev &s, int bx, int by, int bz) {
-  return ((uint32_t)(bz >> 2) * s.nbin + (uint32_t)(by >> 2)) * s.nbin + (uint32_t)(bx >> 2);
+// Spread the low 10 bits of v to every third bit (Morton interleave).
+__device__ __forceinline__ uint32_t spread3(uint32_t v) {
+  v &= 0x3FFu;
+  v = (v | (v << 16)) & 0x030000FFu;
+  v = (v | (v << 8)) & 0x0300F00Fu;
+  v = (v | (v << 4)) & 0x030C30C3u;
+  v = (v | (v << 2)) & 0x09249249u;
+  return v;
+}
+__device__ __forceinline__ uint32_t compact3(uint32_t v) {
+  v &= 0x09249249u;
+  v = (v | (v >> 2)) & 0x030C30C3u;
+  v = (v | (v >> 4)) & 0x0300F00Fu;
+  v = (v | (v >> 8)) & 0x030000FFu;
+  v = (v | (v >> 16)) & 0x3FFu;
+  return v;
+}
+
+// Bin of a base node: 4^3-cell bins in Morton (Z-curve) order, so that bins
+// adjacent in space are close in processing order (L2 reuse of shared grid
+// nodes, compact per-XCD work ranges).
+__device__ __forceinline__ uint32_t bin_key(const SimDev &, int bx, int by, int bz) {
+  return spread3((uint32_t)bx >> 2) | (spread3((uint32_t)by >> 2) << 1) | (spread3((uint32_t)bz >> 2) << 2);
 }
 
 // Quadratic B-spline weights of nodes base+0,1,2 at fractional offset f in [0.5,1.5).
@@ -210,12 +229,12 @@ __device__ void smallest_eigvec_sym3(const float Hin[9], float v[3]) {
       }
     }
   }
-  int m = 0;
-  if (a[1][1] < a[m][m]) m = 1;
-  if (a[2][2] < a[m][m]) m = 2;
-  v[0] = W[0][m];
-  v[1] = W[1][m];
-  v[2] = W[2][m];
+  // column of the smallest diagonal entry (selects, no dynamic indexing)
+  const bool c1 = a[1][1] < a[0][0];
+  const float d01 = c1 ? a[1][1] : a[0][0];
+  const bool c2 = a[2][2] < d01;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) v[r] = c2 ? W[r][2] : (c1 ? W[r][1] : W[r][0]);
 }
 
 // Rotation R in SO(3) closest to F (the fixed-corotated model's rotation).
@@ -245,8 +264,12 @@ __device__ uint32_t rotation_of(const float F[9], float R[9]) {
     const float c20 = X[1] * X[5] - X[2] * X[4], c21 = X[2] * X[3] - X[0] * X[5], c22 = X[0] * X[4] - X[1] * X[3];
     const float det = X[0] * c00 + X[1] * c01 + X[2] * c02;
     const float ad = fabsf(det);
-    const float zeta = exp2f(-0.333333333f * log2f(ad));
-    const float a = 0.5f * zeta, b = 0.5f / (zeta * det);
+    // Determinant scaling speeds up the first iterations of a strongly
+    // stretched F; near a rotation it is ~1 and is skipped.
+    float zeta = 1.f;
+    if (fabsf(ad - 1.f) > 0.05f) zeta = exp2f(-0.333333333f * log2f(ad));
+    // the iteration is self-correcting, so the hardware reciprocal suffices
+    const float a = 0.5f * zeta, b = 0.5f * __builtin_amdgcn_rcpf(zeta * det);
     const float Y[9] = {a * X[0] + b * c00, a * X[1] + b * c01, a * X[2] + b * c02,
                         a * X[3] + b * c10, a * X[4] + b * c11, a * X[5] + b * c12,
                         a * X[6] + b * c20, a * X[7] + b * c21, a * X[8] + b * c22};
@@ -319,6 +342,35 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
     b.id[i] = i;
     key = bin_key(s, base[0], base[1], base[2]);
     s.key[i] = key;
+  }
+  wave_aggregated_increment(s.bin_count, key, valid);
+}
+
+// Creation: move the initial state (buffer 0, creation order) into bin order
+// in buffer 1, so that the first step's gathers are as local as any later
+// step's; recomputes the keys and counts for that order.
+__global__ __launch_bounds__(WG) void k_permute_init(SimDev s) {
+  const uint32_t slot = blockIdx.x * WG + threadIdx.x;
+  const bool valid = slot < (uint32_t)s.N;
+  const PBuf a = s.buf[0], b = s.buf[1];
+  const int Np = s.Np;
+  uint32_t key = 0;
+  if (valid) {
+    const uint32_t i = min(s.perm[slot], (uint32_t)s.N - 1u);
+    int base[3];
+    for (int c = 0; c < 3; ++c) {
+      const float xc = a.x[c * Np + i];
+      b.x[c * Np + slot] = xc;
+      b.v[c * Np + slot] = a.v[c * Np + i];
+      base[c] = base_node(xc * s.fn);
+    }
+    for (int k = 0; k < 9; ++k) b.C[k * Np + slot] = a.C[k * Np + i];
+    const int fw = s.material == MPM_J_FLUID ? 1 : 9;
+    for (int k = 0; k < fw; ++k) b.F[k * Np + slot] = a.F[k * Np + i];
+    if (s.has_E) b.E[slot] = a.E[i];
+    b.id[slot] = a.id[i];
+    key = bin_key(s, base[0], base[1], base[2]);
+    s.key[slot] = key;
   }
   wave_aggregated_increment(s.bin_count, key, valid);
 }
@@ -423,10 +475,6 @@ __global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
     chrun += ch[k];
   }
   if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS] = tile_base_ch + tch;
-  if (t == 0) {
-    if (threadIdx.x == 0) s.ctr[CTR_NACTIVE] = 0u;
-    if (threadIdx.x < NQ) s.ctr[CTR_QHEAD + threadIdx.x] = 0u;
-  }
 }
 
 // Bucket scatter: particle i of the current order goes to the next free slot
@@ -461,22 +509,19 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
   const int Np = s.Np;
-  const uint32_t q = blockIdx.x & (NQ - 1);
+  // Workgroup b runs on XCD b % 8 and takes every (grid/8)-th chunk of that
+  // XCD's contiguous (Morton-ordered, so spatially compact) share of the
+  // chunk list.  Static assignment: no contended atomics on a work queue.
+  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
   const uint32_t nch = s.ctr[CTR_NCHUNKS];
   const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
   const bool pending = s.ctr[CTR_PENDING] != 0u;
   const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
 
-  for (;;) {
-    uint32_t c = 0;
-    if (lane == 0) c = qbeg + atomicAdd(&s.ctr[CTR_QHEAD + q], 1u);
-    c = __builtin_amdgcn_readfirstlane(c);
-    if (c >= qend) break;
+  for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = s.chunks[c];
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
-    const int bxb = (int)(bin % (uint32_t)s.nbin), byb = (int)((bin / (uint32_t)s.nbin) % (uint32_t)s.nbin),
-              bzb = (int)(bin / ((uint32_t)s.nbin * (uint32_t)s.nbin));
-    const int ox0 = bxb * CB, oy0 = byb * CB, oz0 = bzb * CB;  // first base node of the bin = window origin
+    const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;  // first base node of the bin = window origin
 
     for (int k = lane; k < PW3; k += 64) win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     hist[lane] = 0u;
@@ -488,18 +533,24 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     // cells, so no atomics are needed).
     uint32_t packed[KMAX / 64];
     const uint64_t below = (1ull << lane) - 1ull;
+    // all global loads of the pass first, so their latencies overlap
+    uint32_t cells[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       const uint32_t qi = (uint32_t)(64 * j + lane);
-      const bool v = qi < count;
-      uint32_t cell = 0u;
-      if (v) {
+      cells[j] = 0u;
+      if (qi < count) {
         const uint32_t i = min(s.perm[start + qi], (uint32_t)s.N - 1u);
         const int cx = min(max(base_node(in.x[i] * fn) - ox0, 0), CB - 1);
         const int cy = min(max(base_node(in.x[Np + i] * fn) - oy0, 0), CB - 1);
         const int cz = min(max(base_node(in.x[2 * Np + i] * fn) - oz0, 0), CB - 1);
-        cell = (uint32_t)((cz * CB + cy) * CB + cx);
+        cells[j] = (uint32_t)((cz * CB + cy) * CB + cx);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      const bool v = (uint32_t)(64 * j + lane) < count;
+      const uint32_t cell = cells[j];
       uint64_t peers = __ballot(v);
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
@@ -549,6 +600,10 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       const uint32_t slot = start + (ord & 0xFFFFu);
       const uint32_t myrank = ord >> 16;
       const uint32_t i = min(s.perm[valid ? slot : start], (uint32_t)s.N - 1u);
+      // The new state is stored in this processing order, (bin, rank, cell):
+      // the next step's gathers then run over nearly consecutive addresses.
+      const uint32_t dst = start + min(pos, count - 1u);
+      if (valid) s.src_of[dst] = i;
       float xp[3], vp[3], Cp[9];
 #pragma unroll
       for (int a = 0; a < 3; ++a) {
@@ -569,8 +624,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         }
         const float K = HAS_E ? in.E[i] : s.E;
         if (valid) {
-          out.F[slot] = J;
-          if (HAS_E) out.E[slot] = K;
+          out.F[dst] = J;
+          if (HAS_E) out.E[dst] = K;
           if (!(J > 0.f)) flag_status(s, MPM_STATUS_INVERTED, 2);
         }
         tau_diag = K * J * (J - 1.f);
@@ -592,8 +647,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         const float E = HAS_E ? in.E[i] : s.E;
         if (valid) {
 #pragma unroll
-          for (int k = 0; k < 9; ++k) out.F[k * Np + slot] = Fp[k];
-          if (HAS_E) out.E[slot] = E;
+          for (int k = 0; k < 9; ++k) out.F[k * Np + dst] = Fp[k];
+          if (HAS_E) out.E[dst] = E;
         }
         const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
         float R[9];
@@ -646,43 +701,76 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         if (tm == 0ull) break;
         const uint32_t rnow = (uint32_t)__builtin_amdgcn_readlane((int)myrank, __ffsll((unsigned long long)tm) - 1);
         if (todo && myrank == rnow) {
+          // Form the 27 node contributions here rather than keeping all 108 of
+          // them live across the pass loop (register pressure limits occupancy).
 #pragma unroll
-          for (int oz = 0; oz < 3; ++oz)
+          for (int k = 0; k < 3; ++k) {
+            __asm__ __volatile__("" : "+v"(q0[k]), "+v"(w[0][k]), "+v"(w[1][k]), "+v"(w[2][k]));
+          }
+#pragma unroll
+          for (int k = 0; k < 9; ++k) __asm__ __volatile__("" : "+v"(Ad[k]));
+          // Momentum at node o is q0 + Ad (ox, oy, oz): running sums along z,
+          // y and x (one add per component per step; no multiplications by
+          // the constant offsets, which IEEE rules keep the compiler from
+          // folding).
+          float qz[3] = {q0[0], q0[1], q0[2]};
+#pragma unroll
+          for (int oz = 0; oz < 3; ++oz) {
+            if (oz > 0) {
+              qz[0] += Ad[2];
+              qz[1] += Ad[5];
+              qz[2] += Ad[8];
+            }
+            float qy[3] = {qz[0], qz[1], qz[2]};
 #pragma unroll
             for (int oy = 0; oy < 3; ++oy) {
+              if (oy > 0) {
+                qy[0] += Ad[1];
+                qy[1] += Ad[4];
+                qy[2] += Ad[7];
+              }
               const float wyz = w[1][oy] * w[2][oz];
+              float qx[3] = {qy[0], qy[1], qy[2]};
 #pragma unroll
               for (int ox = 0; ox < 3; ++ox) {
+                if (ox > 0) {
+                  qx[0] += Ad[0];
+                  qx[1] += Ad[3];
+                  qx[2] += Ad[6];
+                }
                 const float wt = w[0][ox] * wyz;
                 const int li = li0 + (oz * PW + oy) * PW + ox;
                 float4 g = win[li];
-                g.x += wt * mass;
-                g.y += wt * (q0[0] + Ad[0] * ox + Ad[1] * oy + Ad[2] * oz);
-                g.z += wt * (q0[1] + Ad[3] * ox + Ad[4] * oy + Ad[5] * oz);
-                g.w += wt * (q0[2] + Ad[6] * ox + Ad[7] * oy + Ad[8] * oz);
+                g.x = fmaf(wt, mass, g.x);
+                g.y = fmaf(wt, qx[0], g.y);
+                g.z = fmaf(wt, qx[1], g.z);
+                g.w = fmaf(wt, qx[2], g.w);
                 win[li] = g;
                 // keep this read-modify-write ahead of the next one in issue order
                 __asm__ __volatile__("" ::: "memory");
               }
             }
+          }
           todo = false;
         }
       }
     }
     __syncthreads();
 
-    // Flush: one native global float atomic per nonzero window value.
+    // Flush: one native global float atomic per nonzero window value.  Four
+    // lanes per node (one channel each), so each atomic instruction covers 16
+    // nodes' contiguous float4 records.
     uint32_t mark = 0u;
-    for (int k = lane; k < PW3; k += 64) {
-      const float4 g = win[k];
+    const float *winf = reinterpret_cast<const float *>(win);
+    for (int e = lane; e < 4 * PW3; e += 64) {
+      const int k = e >> 2, chn = e & 3;
+      const float mval = winf[4 * k];
+      const float val = winf[e];
       const int wx = k % PW, wy = (k / PW) % PW, wz = k / (PW * PW);
       const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-      if (g.x != 0.f && gx < s.n && gy < s.n && gz < s.n) {
-        float *dst = reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz));
-        unsafeAtomicAdd(dst + 0, g.x);
-        unsafeAtomicAdd(dst + 1, g.y);
-        unsafeAtomicAdd(dst + 2, g.z);
-        unsafeAtomicAdd(dst + 3, g.w);
+      if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n) {
+        float *dst = reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz)) + chn;
+        unsafeAtomicAdd(dst, val);
         const int bit = (((gz >> 3) - (oz0 >> 3)) << 2) | (((gy >> 3) - (oy0 >> 3)) << 1) | ((gx >> 3) - (ox0 >> 3));
         mark |= 1u << bit;
       }
@@ -691,19 +779,27 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     if (lane < 8 && ((mark >> lane) & 1u)) {
       const uint32_t nbk = ((uint32_t)((oz0 >> 3) + (lane >> 2)) * s.nb + (uint32_t)((oy0 >> 3) + ((lane >> 1) & 1))) * s.nb +
                            (uint32_t)((ox0 >> 3) + (lane & 1));
-      if (atomicExch(&s.active_flag[nbk], 1u) == 0u) s.active_list[atomicAdd(&s.ctr[CTR_NACTIVE], 1u)] = nbk;
+      s.active_flag[nbk] = 1u;  // plain store; the grid update scans the flags
     }
     __syncthreads();
   }
 }
 
-// Grid update over the active node-blocks: v = p/m + dt g where m > 0, sticky
-// walls, store (v, m), clear the accumulator and the block's flag.
+// Grid update over the node-blocks P2G touched (flag 1): v = p/m + dt g where
+// m > 0, sticky walls, store (v, m), clear the accumulator.  Block flags:
+// 1 = touched by this step's P2G, 2 = updated in the last step (read back by
+// mpm_read_grid), 0 = idle.  A block left at 2 by the previous step and not
+// touched now returns to 0.
 __global__ __launch_bounds__(WG) void k_grid_update(SimDev s) {
-  const uint32_t nact = s.ctr[CTR_NACTIVE];
   const int n = s.n, wall = s.wall;
-  for (uint32_t a = blockIdx.x; a < nact; a += gridDim.x) {
-    const uint32_t blk = s.active_list[a];
+  for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+    const uint32_t flag = s.active_flag[blk];
+    if (flag == 0u) continue;
+    __syncthreads();  // every thread has read the flag before it changes
+    if (flag == 2u) {
+      if (threadIdx.x == 0) s.active_flag[blk] = 0u;
+      continue;
+    }
     const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
               bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
 #pragma unroll
@@ -722,7 +818,7 @@ __global__ __launch_bounds__(WG) void k_grid_update(SimDev s) {
       s.gridV[gi] = o;
       s.gridA[gi] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (threadIdx.x == 0) s.active_flag[blk] = 0u;
+    if (threadIdx.x == 0) s.active_flag[blk] = 2u;
   }
 }
 
@@ -737,7 +833,7 @@ __global__ __launch_bounds__(WG) void k_g2p(SimDev s, int src) {
   const float fn = s.fn;
   uint32_t key = 0;
   if (valid) {
-    const uint32_t i = min(s.perm[slot], (uint32_t)s.N - 1u);
+    const uint32_t i = min(s.src_of[slot], (uint32_t)s.N - 1u);
     float xp[3];
     int b[3];
     float w[3][3], d[3][3];
@@ -752,24 +848,46 @@ __global__ __launch_bounds__(WG) void k_g2p(SimDev s, int src) {
       d[a][1] = 1.f - f;
       d[a][2] = 2.f - f;
     }
+    // The node-blocked index is additive per axis: node(b + o) = Z[oz] + Y[oy] + X[ox].
+    uint32_t X[3], Y[3], Z[3];
+    const uint32_t nb = (uint32_t)s.nb;
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {
+      const uint32_t gx = (uint32_t)(b[0] + o), gy = (uint32_t)(b[1] + o), gz = (uint32_t)(b[2] + o);
+      X[o] = ((gx >> 3) << 9) | (gx & 7u);
+      Y[o] = (((gy >> 3) * nb) << 9) + ((gy & 7u) << 3);
+      Z[o] = (((gz >> 3) * nb * nb) << 9) + ((gz & 7u) << 6);
+    }
+    // v = sum w v_i and B = sum w v_i (o - f)^T, reduced along x first for
+    // each (y, z) row: S = sum_x w_x v_i, T = sum_x w_x (ox - f_x) v_i.
+    float wd0[3];
+#pragma unroll
+    for (int o = 0; o < 3; ++o) wd0[o] = w[0][o] * d[0][o];
     float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int oz = 0; oz < 3; ++oz)
 #pragma unroll
       for (int oy = 0; oy < 3; ++oy) {
-        const float wyz = w[1][oy] * w[2][oz];
+        const uint32_t row = Z[oz] + Y[oy];
+        float S[3] = {0.f, 0.f, 0.f}, T[3] = {0.f, 0.f, 0.f};
 #pragma unroll
         for (int ox = 0; ox < 3; ++ox) {
-          const float4 g = s.gridV[node_index(s, b[0] + ox, b[1] + oy, b[2] + oz)];
-          const float wt = w[0][ox] * wyz;
-          const float wv[3] = {wt * g.x, wt * g.y, wt * g.z};
+          const float4 g = s.gridV[row + X[ox]];
+          S[0] = fmaf(w[0][ox], g.x, S[0]);
+          S[1] = fmaf(w[0][ox], g.y, S[1]);
+          S[2] = fmaf(w[0][ox], g.z, S[2]);
+          T[0] = fmaf(wd0[ox], g.x, T[0]);
+          T[1] = fmaf(wd0[ox], g.y, T[1]);
+          T[2] = fmaf(wd0[ox], g.z, T[2]);
+        }
+        const float wyz = w[1][oy] * w[2][oz];
+        const float wyz1 = wyz * d[1][oy], wyz2 = wyz * d[2][oz];
 #pragma unroll
-          for (int a = 0; a < 3; ++a) {
-            v[a] += wv[a];
-            B[a * 3 + 0] += wv[a] * d[0][ox];
-            B[a * 3 + 1] += wv[a] * d[1][oy];
-            B[a * 3 + 2] += wv[a] * d[2][oz];
-          }
+        for (int a = 0; a < 3; ++a) {
+          v[a] = fmaf(wyz, S[a], v[a]);
+          B[a * 3 + 0] = fmaf(wyz, T[a], B[a * 3 + 0]);
+          B[a * 3 + 1] = fmaf(wyz1, S[a], B[a * 3 + 1]);
+          B[a * 3 + 2] = fmaf(wyz2, S[a], B[a * 3 + 2]);
         }
       }
     bool clamped = false, nonfinite = false;
@@ -844,10 +962,9 @@ __global__ __launch_bounds__(WG) void k_read_particles(SimDev s, int cur, float 
 
 // Readback of the grid: active blocks -> dense (i + n (j + n k)) arrays.
 __global__ __launch_bounds__(WG) void k_read_grid(SimDev s, float *__restrict__ mass, float *__restrict__ mom) {
-  const uint32_t nact = s.ctr[CTR_NACTIVE];
   const int n = s.n;
-  for (uint32_t a = blockIdx.x; a < nact; a += gridDim.x) {
-    const uint32_t blk = s.active_list[a];
+  for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+    if (s.active_flag[blk] != 2u) continue;
     const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
               bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
     for (int local = threadIdx.x; local < 512; local += WG) {
@@ -890,7 +1007,9 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   const int n = p->grid_n, nb = (n + NB - 1) / NB;
   const int64_t nblk = (int64_t)nb * nb * nb;
   const int nbin = (n + CB - 1) / CB;
-  const int64_t nbins = (int64_t)nbin * nbin * nbin;
+  int nbin2 = 1;
+  while (nbin2 < nbin) nbin2 <<= 1;
+  const int64_t nbins = (int64_t)nbin2 * nbin2 * nbin2;
   const int64_t max_chunks = (N + KMAX - 1) / KMAX + nbins;
   const int fw = p->material == MPM_J_FLUID ? 1 : 9;
   size_t off = 0;
@@ -909,13 +1028,13 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     bufs[k].id = (uint32_t *)take(sizeof(uint32_t) * Np);
   }
   uint32_t *perm = (uint32_t *)take(sizeof(uint32_t) * Np);
+  uint32_t *src_of = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *key = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
   uint32_t *tiles = (uint32_t *)take(sizeof(uint32_t) * 2 * ntiles);
   uint32_t *aflag = (uint32_t *)take(sizeof(uint32_t) * nblk);
-  uint32_t *alist = (uint32_t *)take(sizeof(uint32_t) * nblk);
   uint4 *chunks = (uint4 *)take(sizeof(uint4) * max_chunks);
   uint32_t *ctr = (uint32_t *)take(sizeof(uint32_t) * CTR_WORDS);
   uint32_t *status = (uint32_t *)take(sizeof(uint32_t) * MPM_STATUS_WORDS);
@@ -951,13 +1070,13 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->buf[0] = bufs[0];
     d->buf[1] = bufs[1];
     d->perm = perm;
+    d->src_of = src_of;
     d->key = key;
     d->bin_count = cnt;
     d->bin_cursor = cur;
     d->tile_sum = tiles;
     d->ntiles = (int32_t)ntiles;
     d->active_flag = aflag;
-    d->active_list = alist;
     d->chunks = chunks;
     d->ctr = ctr;
     d->status = status;
@@ -1116,7 +1235,15 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     // G2P may read a stencil node whose weight is exactly zero and that no
     // particle marked active; it must hold a finite value, so start at zero.
     k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridV), (size_t)d.nblk * 512 * 4);
-    if (d.N > 0) k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
+    if (d.N > 0) {
+      k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
+      // one bucket pass to bring the initial state into bin order (buffer 1)
+      k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
+      k_scan_bins<<<d.ntiles, WG, 0, st>>>(d);
+      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
+      k_permute_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d);
+      sim->cur = 1;
+    }
     if (hipGetLastError() != hipSuccess) { rc = MPM_ERR_HIP; break; }
     if (d.N > 0) rc = build_graphs(sim);
   } while (0);
