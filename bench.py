@@ -46,13 +46,41 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
         "k_scan_tiles": 4 * nbins,
         "k_scan_bins": 12 * nbins,
         "k_scatter": 8 * N,
-        # reads perm, x, v, C, F(, E); writes F(, E); accumulator write per active node
-        "k_p2g": N * (4 + 12 + 12 + 36 + f + e + f + e) + 16 * active_nodes,
+        # reads perm, x, v, C, F(, E); writes F(, E) and the source map;
+        # accumulator write per active node
+        "k_p2g": N * (4 + 12 + 12 + 36 + f + e + f + e + 4) + 16 * active_nodes,
         # reads (m, p) and writes v per active node
         "k_grid_update": 28 * active_nodes,
-        # reads perm, x, id; writes x, v, C, id, key; reads grid v once per active node
+        # reads source map, x, id; writes x, v, C, id, key; reads grid v once per active node
         "k_g2p": N * (4 + 12 + 4 + 12 + 12 + 36 + 4 + 4) + 12 * active_nodes,
     }
+
+
+def source_sha1() -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "material_point_physics_amd", "csrc", "mpm.hip"), "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
+
+
+def committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
+    profiles/<workload>_all_kernels_traffic.txt (FETCH_SIZE and WRITE_SIZE runs, each
+    scaled by the calibration copy), or None when that summary is missing or
+    was taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_all_kernels_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha, val = None, None
+    for line in open(path):
+        if line.startswith("source_sha1:"):
+            sha = line.split(":", 1)[1].strip()
+        if line.startswith(f"traffic {kernel}"):
+            for tok in line.split():
+                if tok.startswith("total_bytes="):
+                    val = float(tok.split("=", 1)[1])
+    if sha != source_sha1() or val is None:
+        return None
+    return val
 
 
 def main():
@@ -123,6 +151,7 @@ def main():
                    "GBps": round(kb[k] / (kavg[k] * 1e-3) / 1e9, 1)} for k in kavg}
     dom = max(kavg, key=kavg.get)
     achieved = kb[dom] / (kavg[dom] * 1e-3) / 1e9
+    traffic = committed_traffic(sc.name, dom)
     step_bytes = sum(kb.values())
     log(f"kernels: {kernels}")
     log(f"active nodes {active_nodes}, active blocks {active_blocks}, status {status[:4]}")
@@ -158,7 +187,7 @@ def main():
         "config": {"workload": f"{sc.name}: {sc.description}", "particles": sc.N, "grid": f"{n}^3",
                    "dt": sc.dt, "material": "fixed-corotated" if sc.material == 0 else "J-fluid"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "step_hbm": {"alg_bytes_per_step": step_bytes,
                      "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},

@@ -2,6 +2,7 @@
 
 Usage:
     python -m material_point_physics_amd.profiling <results.db> [--kernels k_] [--title TEXT]
+    python -m material_point_physics_amd.profiling <fetch.db> --write-db <write.db>
 
 Prints, per kernel: number of dispatches, average / median / total duration
 (from the kernel trace), and the per-dispatch median of every collected
@@ -82,8 +83,55 @@ def main():
     ap.add_argument("db")
     ap.add_argument("--kernels", default="")
     ap.add_argument("--title", default="")
+    ap.add_argument("--write-db", default="", help="with a FETCH_SIZE db: print copy-calibrated traffic")
     a = ap.parse_args()
-    print(summarize(a.db, a.kernels, a.title))
+    if a.write_db:
+        t = traffic(a.db, a.write_db, a.kernels or "k_")
+        print(f"copy calibration: FETCH_SIZE x {t['fetch_factor']:.4f}, WRITE_SIZE x {t['write_factor']:.4f}")
+        for k, v in t["kernels"].items():
+            print(f"traffic {k} fetch_bytes={v['fetch_bytes']:.6g} write_bytes={v['write_bytes']:.6g} "
+                  f"total_bytes={v['total_bytes']:.6g}")
+    else:
+        print(summarize(a.db, a.kernels, a.title))
+
+
+
+# ------------------------------------------------------------ HBM traffic
+
+COPY_KIB = 262144  # the benchmark's calibration copy: 256 MiB read, 256 MiB written
+
+
+def copy_calibration(db: str, counter: str, known_kib: float = COPY_KIB) -> float:
+    """Scale factor for `counter` (FETCH_SIZE or WRITE_SIZE, KiB per dispatch):
+    known bytes of the benchmark's plain 256 MiB device copy divided by what
+    the counter reads for that copy (the copy dispatch with the largest value)."""
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select dispatch_id, kernel_name, value from counters_collection where counter_name = ?",
+                       (counter,)).fetchall()
+    per = collections.defaultdict(float)
+    for did, kn, val in rows:
+        if "copy" in kn.lower():
+            per[did] += float(val)
+    if not per:
+        raise ValueError(f"no copy dispatch with {counter} in {db}")
+    return known_kib / max(per.values())
+
+
+def traffic(fetch_db: str, write_db: str, kernels: str = "k_"):
+    """Per-kernel HBM bytes per dispatch (median), each counter scaled by its
+    copy calibration factor."""
+    fk = copy_calibration(fetch_db, "FETCH_SIZE")
+    wk = copy_calibration(write_db, "WRITE_SIZE")
+    fc = kernel_counters(fetch_db)
+    wc = kernel_counters(write_db)
+    out = {}
+    for k in sorted(set(fc) | set(wc)):
+        if kernels and kernels not in k:
+            continue
+        f = fc.get(k, {}).get("FETCH_SIZE", 0.0) * fk * 1024
+        w = wc.get(k, {}).get("WRITE_SIZE", 0.0) * wk * 1024
+        out[k] = {"fetch_bytes": f, "write_bytes": w, "total_bytes": f + w}
+    return {"fetch_factor": fk, "write_factor": wk, "kernels": out}
 
 
 if __name__ == "__main__":
