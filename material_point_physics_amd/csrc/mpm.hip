@@ -19,8 +19,8 @@
 //                 global atomic flush per window node
 //   k_grid_update active node-blocks only: v = p/m + dt g, sticky walls,
 //                 clears the P2G accumulator
-//   k_g2p         gather, APIC C, advection + clamp, writes the state in
-//                 sorted order, computes the next step's block keys/counts
+//   k_g2p         gather, APIC C, advection + clamp in the storage order P2G
+//                 chose; computes the next step's bin keys/counts
 //
 // Deferred deformation gradient: [RT-MPM] (kernel-merging discussion) notes
 // that the F update at the end of G2P can be postponed to the start of P2G
@@ -87,7 +87,6 @@ struct SimDev {
   uint32_t max_chunks;
   PBuf buf[2];
   uint32_t *perm, *key;
-  uint32_t *src_of;  // storage slot -> source index, in P2G processing order (read by G2P)
   uint32_t *bin_count, *bin_cursor;
   uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
   int32_t ntiles;
@@ -168,13 +167,6 @@ __device__ __forceinline__ uint32_t wave_aggregated_increment(uint32_t *counters
 __device__ __forceinline__ void flag_status(const SimDev &s, uint32_t bit, int counter_word) {
   atomicOr(&s.status[0], bit);
   if (counter_word > 0) atomicAdd(&s.status[counter_word], 1u);
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous range of logical blocks so that neighbouring particles (and the
-// grid nodes they share) stay in one XCD's L2.  grid must be a multiple of 8.
-__device__ __forceinline__ uint32_t xcd_local_block(uint32_t bid, uint32_t grid) {
-  return (bid & 7u) * (grid >> 3) + (bid >> 3);
 }
 
 // ------------------------------------------------------- 3x3 linear algebra
@@ -505,6 +497,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   __shared__ uint32_t rstart[KMAX + 1];
   __shared__ uint64_t rmask[KMAX];
   __shared__ uint32_t order[KMAX];
+  __shared__ uint32_t subcnt[KMAX / 64][CB3];  // per sub-round particle count of each cell
 
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
@@ -527,26 +520,38 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     hist[lane] = 0u;
     __syncthreads();
 
-    // Pass A: cell of each particle and its rank within the cell.  Lanes with
-    // the same cell are matched bit by bit with ballots; the lowest lane of
-    // each group updates the cell's running count (leaders have distinct
-    // cells, so no atomics are needed).
+    // Pass A: cell of each particle and its rank within the cell.  Ranks
+    // follow the particles' previous storage order (their source index), so
+    // the (rank, cell) order -- which is also the order the new state is
+    // stored in -- is stable from step to step and the gathers below run over
+    // nearly consecutive addresses.  The chunk is read as KMAX/64 sub-rounds
+    // of consecutive slots, each a run of consecutive sources; sub-rounds
+    // are ranked in the order of their smallest source.  Lanes with the same
+    // cell are matched bit by bit with ballots; the lowest lane of each group
+    // records the group's size (leaders have distinct cells: no atomics).
     uint32_t packed[KMAX / 64];
     const uint64_t below = (1ull << lane) - 1ull;
     // all global loads of the pass first, so their latencies overlap
-    uint32_t cells[KMAX / 64];
+    uint32_t cells[KMAX / 64], srcmin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       const uint32_t qi = (uint32_t)(64 * j + lane);
       cells[j] = 0u;
+      uint32_t src = 0xFFFFFFFFu;
       if (qi < count) {
         const uint32_t i = min(s.perm[start + qi], (uint32_t)s.N - 1u);
+        src = i;
         const int cx = min(max(base_node(in.x[i] * fn) - ox0, 0), CB - 1);
         const int cy = min(max(base_node(in.x[Np + i] * fn) - oy0, 0), CB - 1);
         const int cz = min(max(base_node(in.x[2 * Np + i] * fn) - oz0, 0), CB - 1);
         cells[j] = (uint32_t)((cz * CB + cy) * CB + cx);
       }
+      for (int d = 32; d >= 1; d >>= 1) src = min(src, (uint32_t)__shfl_xor((int)src, d));
+      srcmin[j] = src;
+      subcnt[j][lane] = 0u;
     }
+    __syncthreads();
+    uint32_t rin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       const bool v = (uint32_t)(64 * j + lane) < count;
@@ -557,11 +562,25 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         const uint64_t bk = __ballot((cell >> k) & 1u);
         peers &= ((cell >> k) & 1u) ? bk : ~bk;
       }
-      const uint32_t before = hist[cell];
-      const uint32_t rank = before + (uint32_t)__popcll(peers & below);
-      if (v && (peers & below) == 0ull) hist[cell] = before + (uint32_t)__popcll(peers);
-      __asm__ __volatile__("" ::: "memory");
-      packed[j] = cell | (rank << 8);
+      rin[j] = (uint32_t)__popcll(peers & below);
+      if (v && (peers & below) == 0ull) subcnt[j][cell] = (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      uint32_t before = 0u;
+#pragma unroll
+      for (int k = 0; k < KMAX / 64; ++k) {
+        const bool earlier = srcmin[k] < srcmin[j] || (srcmin[k] == srcmin[j] && k < j);
+        if (k != j && earlier) before += subcnt[k][cells[j]];
+      }
+      packed[j] = cells[j] | ((before + rin[j]) << 8);
+    }
+    {
+      uint32_t total = 0u;
+#pragma unroll
+      for (int k = 0; k < KMAX / 64; ++k) total += subcnt[k][lane];
+      hist[lane] = total;
     }
     __syncthreads();
     // Rank tables: rmask[r] = cells holding more than r particles (lane = cell),
@@ -602,8 +621,9 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       const uint32_t i = min(s.perm[valid ? slot : start], (uint32_t)s.N - 1u);
       // The new state is stored in this processing order, (bin, rank, cell):
       // the next step's gathers then run over nearly consecutive addresses.
+      // P2G writes x and id there; G2P reads x from the same slot, without
+      // an index indirection, and overwrites it with the advected position.
       const uint32_t dst = start + min(pos, count - 1u);
-      if (valid) s.src_of[dst] = i;
       float xp[3], vp[3], Cp[9];
 #pragma unroll
       for (int a = 0; a < 3; ++a) {
@@ -612,6 +632,11 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       }
 #pragma unroll
       for (int k = 0; k < 9; ++k) Cp[k] = in.C[k * Np + i];
+      if (valid) {
+#pragma unroll
+        for (int a = 0; a < 3; ++a) out.x[a * Np + dst] = xp[a];
+        out.id[dst] = in.id[i];
+      }
 
       float tau_diag = 0.f;
       float tau[9];
@@ -822,99 +847,114 @@ __global__ __launch_bounds__(WG) void k_grid_update(SimDev s) {
   }
 }
 
-// G2P: gather, APIC C, advection and clamp; writes the new state in sorted
-// (slot) order and the next step's block key and count.
+// G2P: gather, APIC C, advection and clamp.  Persistent single-wavefront
+// workgroups walk the same per-XCD chunk list as P2G.  A chunk's particles
+// occupy the consecutive slots [start, start + count) (P2G stored them
+// there), and all of their stencils lie in the bin's 6^3-node window, which
+// is loaded once into LDS; each particle then gathers its 27 nodes from LDS.
+// Writes x, v, C in place and the next step's bin key and count.
 template <int MAT>
-__global__ __launch_bounds__(WG) void k_g2p(SimDev s, int src) {
-  const PBuf in = s.buf[src], out = s.buf[src ^ 1];
-  const uint32_t slot = xcd_local_block(blockIdx.x, gridDim.x) * WG + threadIdx.x;
-  const bool valid = slot < (uint32_t)s.N;
+__global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
+  __shared__ float4 win[PW3];
+  const PBuf out = s.buf[src ^ 1];
+  const int lane = threadIdx.x;
   const int Np = s.Np;
   const float fn = s.fn;
-  uint32_t key = 0;
-  if (valid) {
-    const uint32_t i = min(s.src_of[slot], (uint32_t)s.N - 1u);
-    float xp[3];
-    int b[3];
-    float w[3][3], d[3][3];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      xp[a] = in.x[a * Np + i];
-      const float xn = xp[a] * fn;
-      b[a] = base_node(xn);
-      const float f = xn - (float)b[a];
-      bspline_weights(f, w[a]);
-      d[a][0] = -f;
-      d[a][1] = 1.f - f;
-      d[a][2] = 2.f - f;
+  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS];
+  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
+    const uint4 ch = s.chunks[c];
+    const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
+    const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
+    // window load (nodes outside the grid read as zero)
+    for (int k = lane; k < PW3; k += 64) {
+      const int gx = ox0 + k % PW, gy = oy0 + (k / PW) % PW, gz = oz0 + k / (PW * PW);
+      float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (gx < s.n && gy < s.n && gz < s.n) g = s.gridV[node_index(s, gx, gy, gz)];
+      win[k] = g;
     }
-    // The node-blocked index is additive per axis: node(b + o) = Z[oz] + Y[oy] + X[ox].
-    uint32_t X[3], Y[3], Z[3];
-    const uint32_t nb = (uint32_t)s.nb;
-#pragma unroll
-    for (int o = 0; o < 3; ++o) {
-      const uint32_t gx = (uint32_t)(b[0] + o), gy = (uint32_t)(b[1] + o), gz = (uint32_t)(b[2] + o);
-      X[o] = ((gx >> 3) << 9) | (gx & 7u);
-      Y[o] = (((gy >> 3) * nb) << 9) + ((gy & 7u) << 3);
-      Z[o] = (((gz >> 3) * nb * nb) << 9) + ((gz & 7u) << 6);
-    }
-    // v = sum w v_i and B = sum w v_i (o - f)^T, reduced along x first for
-    // each (y, z) row: S = sum_x w_x v_i, T = sum_x w_x (ox - f_x) v_i.
-    float wd0[3];
-#pragma unroll
-    for (int o = 0; o < 3; ++o) wd0[o] = w[0][o] * d[0][o];
-    float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int oz = 0; oz < 3; ++oz)
-#pragma unroll
-      for (int oy = 0; oy < 3; ++oy) {
-        const uint32_t row = Z[oz] + Y[oy];
-        float S[3] = {0.f, 0.f, 0.f}, T[3] = {0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ox = 0; ox < 3; ++ox) {
-          const float4 g = s.gridV[row + X[ox]];
-          S[0] = fmaf(w[0][ox], g.x, S[0]);
-          S[1] = fmaf(w[0][ox], g.y, S[1]);
-          S[2] = fmaf(w[0][ox], g.z, S[2]);
-          T[0] = fmaf(wd0[ox], g.x, T[0]);
-          T[1] = fmaf(wd0[ox], g.y, T[1]);
-          T[2] = fmaf(wd0[ox], g.z, T[2]);
-        }
-        const float wyz = w[1][oy] * w[2][oz];
-        const float wyz1 = wyz * d[1][oy], wyz2 = wyz * d[2][oz];
+    __syncthreads();
+    for (uint32_t r0 = 0; r0 < count; r0 += 64) {
+      const uint32_t slot = start + r0 + (uint32_t)lane;
+      const bool valid = r0 + (uint32_t)lane < count;
+      uint32_t key = 0;
+      if (valid) {
+        float xp[3];
+        int b[3];
+        float w[3][3], d[3][3];
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
-          v[a] = fmaf(wyz, S[a], v[a]);
-          B[a * 3 + 0] = fmaf(wyz, T[a], B[a * 3 + 0]);
-          B[a * 3 + 1] = fmaf(wyz1, S[a], B[a * 3 + 1]);
-          B[a * 3 + 2] = fmaf(wyz2, S[a], B[a * 3 + 2]);
+          xp[a] = out.x[a * Np + slot];  // written by this step's P2G in this order
+          const float xn = xp[a] * fn;
+          b[a] = base_node(xn);
+          const float f = xn - (float)b[a];
+          bspline_weights(f, w[a]);
+          d[a][0] = -f;
+          d[a][1] = 1.f - f;
+          d[a][2] = 2.f - f;
         }
+        const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
+                  lz = min(max(b[2] - oz0, 0), CB - 1);
+        const int li0 = (lz * PW + ly) * PW + lx;
+        // v = sum w v_i and B = sum w v_i (o - f)^T, reduced along x first for
+        // each (y, z) row: S = sum_x w_x v_i, T = sum_x w_x (ox - f_x) v_i.
+        float wd0[3];
+#pragma unroll
+        for (int o = 0; o < 3; ++o) wd0[o] = w[0][o] * d[0][o];
+        float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int oz = 0; oz < 3; ++oz)
+#pragma unroll
+          for (int oy = 0; oy < 3; ++oy) {
+            float S[3] = {0.f, 0.f, 0.f}, T[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ox = 0; ox < 3; ++ox) {
+              const float4 g = win[li0 + (oz * PW + oy) * PW + ox];
+              S[0] = fmaf(w[0][ox], g.x, S[0]);
+              S[1] = fmaf(w[0][ox], g.y, S[1]);
+              S[2] = fmaf(w[0][ox], g.z, S[2]);
+              T[0] = fmaf(wd0[ox], g.x, T[0]);
+              T[1] = fmaf(wd0[ox], g.y, T[1]);
+              T[2] = fmaf(wd0[ox], g.z, T[2]);
+            }
+            const float wyz = w[1][oy] * w[2][oz];
+            const float wyz1 = wyz * d[1][oy], wyz2 = wyz * d[2][oz];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+              v[a] = fmaf(wyz, S[a], v[a]);
+              B[a * 3 + 0] = fmaf(wyz, T[a], B[a * 3 + 0]);
+              B[a * 3 + 1] = fmaf(wyz1, S[a], B[a * 3 + 1]);
+              B[a * 3 + 2] = fmaf(wyz2, S[a], B[a * 3 + 2]);
+            }
+          }
+        bool clamped = false, nonfinite = false;
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          float xa = xp[a] + s.dt * v[a];
+          if (!isfinite(xa) || !isfinite(v[a])) nonfinite = true;
+          if (xa < s.lo || xa > s.hi) clamped = true;
+          xa = fminf(fmaxf(xa, s.lo), s.hi);
+          out.x[a * Np + slot] = xa;
+          out.v[a * Np + slot] = v[a];
+          b[a] = base_node(xa * fn);
+        }
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+          const float ck = s.c_scale * B[k];
+          if (!isfinite(ck)) nonfinite = true;
+          out.C[k * Np + slot] = ck;
+        }
+        key = bin_key(s, b[0], b[1], b[2]);
+        s.key[slot] = key;
+        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
+        if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
-    bool clamped = false, nonfinite = false;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      float xa = xp[a] + s.dt * v[a];
-      if (!isfinite(xa) || !isfinite(v[a])) nonfinite = true;
-      if (xa < s.lo || xa > s.hi) clamped = true;
-      xa = fminf(fmaxf(xa, s.lo), s.hi);
-      out.x[a * Np + slot] = xa;
-      out.v[a * Np + slot] = v[a];
-      b[a] = base_node(xa * fn);
+      wave_aggregated_increment(s.bin_count, key, valid);
     }
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const float ck = s.c_scale * B[k];
-      if (!isfinite(ck)) nonfinite = true;
-      out.C[k * Np + slot] = ck;
-    }
-    out.id[slot] = in.id[i];
-    key = bin_key(s, b[0], b[1], b[2]);
-    s.key[slot] = key;
-    if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
-    if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
+    __syncthreads();  // the window is reloaded for the next chunk
   }
-  wave_aggregated_increment(s.bin_count, key, valid);
-  if (blockIdx.x == 0 && threadIdx.x == 0) s.ctr[CTR_PENDING] = 1u;
+  if (blockIdx.x == 0 && lane == 0) s.ctr[CTR_PENDING] = 1u;
 }
 
 // Readback: unpermute to creation order, apply the pending F (or J) update.
@@ -1028,7 +1068,6 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     bufs[k].id = (uint32_t *)take(sizeof(uint32_t) * Np);
   }
   uint32_t *perm = (uint32_t *)take(sizeof(uint32_t) * Np);
-  uint32_t *src_of = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *key = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
@@ -1070,7 +1109,6 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->buf[0] = bufs[0];
     d->buf[1] = bufs[1];
     d->perm = perm;
-    d->src_of = src_of;
     d->key = key;
     d->bin_count = cnt;
     d->bin_cursor = cur;
@@ -1101,6 +1139,7 @@ struct mpm_sim {
   hipGraphExec_t exec[2] = {nullptr, nullptr};
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_p2g = 0;
+  int grid_g2p = 0;
   int grid_update = 0;
 };
 
@@ -1136,8 +1175,8 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
       k_grid_update<<<sim->grid_update, WG, 0, st>>>(d);
       break;
     case 5:
-      if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_particles, WG, 0, st>>>(d, src);
-      else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_particles, WG, 0, st>>>(d, src);
+      if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src);
+      else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_g2p, 64, 0, st>>>(d, src);
       break;
   }
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
@@ -1221,6 +1260,10 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
         occ <= 0)
       occ = 16;
     sim->grid_p2g = ((cus * occ + NQ - 1) / NQ) * NQ;
+    int occ_g = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
+      occ_g = 16;
+    sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
     sim->grid_update = cus * 8;
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
 
