@@ -483,21 +483,36 @@ __global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
 // of one 4^3-cell bin) from their XCD's queue.
 //
 // Accumulation without atomics: on gfx950, LDS float atomics serialise per
-// lane, so the window is private to the wavefront and updated with plain
-// read-modify-writes.  The chunk's particles are ordered by (rank within
-// their cell, cell): lanes that share a rank have distinct cells, so for a
-// fixed stencil offset their target nodes are distinct, and one masked
-// ds_read/ds_write pair per offset adds all of them.  A round of 64 lanes
-// that spans several ranks runs one pass per rank.  The LDS executes a
-// wavefront's accesses in issue order; compiler fences keep that order.
+// lane, so the windows are private to the wavefront and updated with plain
+// read-modify-writes.  There are NWIN windows; the particle of rank r in its
+// cell (r-th of that cell in the chunk) accumulates into window r % NWIN and
+// has super-rank r / NWIN.  The chunk's particles are ordered by (super-rank,
+// window, cell): lanes that share a super-rank differ in (window, cell), so
+// for a fixed stencil offset their target addresses are distinct, and one
+// masked ds_read/ds_write pair per offset adds all of them.  A round of 64
+// lanes that spans several super-ranks runs one pass per super-rank.  The LDS
+// executes a wavefront's accesses in issue order; compiler fences keep that
+// order.  The flush adds the windows and issues one native global atomic per
+// node and channel.
+constexpr int NWIN = 2;                  // accumulation windows per wavefront
+constexpr int KSR = KMAX / NWIN;         // super-ranks per chunk, at most
+
+struct P2GRankTables {                   // lives in the window space while a chunk is ordered
+  uint32_t hist[CB3];                    // particles per cell
+  uint32_t subcnt[KMAX / 64][CB3];       // particles per cell in each sub-round of 64
+  uint32_t rstart[KSR + 2];              // first position of each super-rank
+  uint64_t rmask[NWIN * KSR];            // per (super-rank, window): cells present (bit = cell)
+};
+static_assert(sizeof(P2GRankTables) <= sizeof(float4) * NWIN * PW3, "rank tables must fit the windows");
+
 template <int MAT, bool HAS_E>
 __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
-  __shared__ float4 win[PW3];
-  __shared__ uint32_t hist[CB3];
-  __shared__ uint32_t rstart[KMAX + 1];
-  __shared__ uint64_t rmask[KMAX];
-  __shared__ uint32_t order[KMAX];
-  __shared__ uint32_t subcnt[KMAX / 64][CB3];  // per sub-round particle count of each cell
+  __shared__ union P2GShared {
+    float4 win[NWIN * PW3];
+    P2GRankTables rk;
+  } sm;
+  __shared__ uint32_t order[KMAX];      // source index of each processing position
+  __shared__ uint8_t ordtag[KMAX];      // super-rank * NWIN + window of each position
 
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
@@ -516,23 +531,19 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;  // first base node of the bin = window origin
 
-    for (int k = lane; k < PW3; k += 64) win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    hist[lane] = 0u;
-    __syncthreads();
-
     // Pass A: cell of each particle and its rank within the cell.  Ranks
     // follow the particles' previous storage order (their source index), so
-    // the (rank, cell) order -- which is also the order the new state is
+    // the processing order -- which is also the order the new state is
     // stored in -- is stable from step to step and the gathers below run over
     // nearly consecutive addresses.  The chunk is read as KMAX/64 sub-rounds
     // of consecutive slots, each a run of consecutive sources; sub-rounds
     // are ranked in the order of their smallest source.  Lanes with the same
     // cell are matched bit by bit with ballots; the lowest lane of each group
     // records the group's size (leaders have distinct cells: no atomics).
-    uint32_t packed[KMAX / 64];
+    P2GRankTables &rk = sm.rk;
     const uint64_t below = (1ull << lane) - 1ull;
     // all global loads of the pass first, so their latencies overlap
-    uint32_t cells[KMAX / 64], srcmin[KMAX / 64];
+    uint32_t cells[KMAX / 64], srcs[KMAX / 64], srcmin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       const uint32_t qi = (uint32_t)(64 * j + lane);
@@ -546,9 +557,10 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         const int cz = min(max(base_node(in.x[2 * Np + i] * fn) - oz0, 0), CB - 1);
         cells[j] = (uint32_t)((cz * CB + cy) * CB + cx);
       }
+      srcs[j] = src;
       for (int d = 32; d >= 1; d >>= 1) src = min(src, (uint32_t)__shfl_xor((int)src, d));
       srcmin[j] = src;
-      subcnt[j][lane] = 0u;
+      rk.subcnt[j][lane] = 0u;
     }
     __syncthreads();
     uint32_t rin[KMAX / 64];
@@ -563,40 +575,45 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         peers &= ((cell >> k) & 1u) ? bk : ~bk;
       }
       rin[j] = (uint32_t)__popcll(peers & below);
-      if (v && (peers & below) == 0ull) subcnt[j][cell] = (uint32_t)__popcll(peers);
+      if (v && (peers & below) == 0ull) rk.subcnt[j][cell] = (uint32_t)__popcll(peers);
     }
     __syncthreads();
+    uint32_t rank[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       uint32_t before = 0u;
 #pragma unroll
       for (int k = 0; k < KMAX / 64; ++k) {
         const bool earlier = srcmin[k] < srcmin[j] || (srcmin[k] == srcmin[j] && k < j);
-        if (k != j && earlier) before += subcnt[k][cells[j]];
+        if (k != j && earlier) before += rk.subcnt[k][cells[j]];
       }
-      packed[j] = cells[j] | ((before + rin[j]) << 8);
+      rank[j] = before + rin[j];
     }
     {
       uint32_t total = 0u;
 #pragma unroll
-      for (int k = 0; k < KMAX / 64; ++k) total += subcnt[k][lane];
-      hist[lane] = total;
+      for (int k = 0; k < KMAX / 64; ++k) total += rk.subcnt[k][lane];
+      rk.hist[lane] = total;
     }
     __syncthreads();
-    // Rank tables: rmask[r] = cells holding more than r particles (lane = cell),
-    // rstart[r] = position of the first particle of rank r.
+    // Rank tables: rmask[NWIN sr + w] = cells holding a particle of rank
+    // NWIN sr + w (lane = cell), rstart[sr] = position of the first particle
+    // of super-rank sr.
     {
-      const uint32_t cnt = hist[lane];
+      const uint32_t cnt = rk.hist[lane];
       uint32_t mx = cnt;
       for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
       uint32_t run = 0;
-      for (uint32_t r = 0; r < mx; ++r) {
-        const uint64_t m = __ballot(cnt > r);
-        if (lane == 0) {
-          rstart[r] = run;
-          rmask[r] = m;
+      for (uint32_t sr = 0; NWIN * sr < mx; ++sr) {
+        uint32_t here = 0;
+#pragma unroll
+        for (int w = 0; w < NWIN; ++w) {
+          const uint64_t m = __ballot(cnt > NWIN * sr + w);
+          if (lane == 0) rk.rmask[NWIN * sr + w] = m;
+          here += (uint32_t)__popcll(m);
         }
-        run += (uint32_t)__popcll(m);
+        if (lane == 0) rk.rstart[sr] = run;
+        run += here;
       }
     }
     __syncthreads();
@@ -604,26 +621,33 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     for (int j = 0; j < KMAX / 64; ++j) {
       const uint32_t qi = (uint32_t)(64 * j + lane);
       if (qi < count) {
-        const uint32_t cell = packed[j] & 0xFFu, rank = packed[j] >> 8;
-        const uint32_t pos = rstart[rank] + (uint32_t)__popcll(rmask[rank] & ((1ull << cell) - 1ull));
-        order[min(pos, (uint32_t)KMAX - 1u)] = qi | (rank << 16);
+        const uint32_t cell = cells[j], sr = rank[j] / NWIN, w = rank[j] % NWIN;
+        uint32_t pos = rk.rstart[sr] + (uint32_t)__popcll(rk.rmask[NWIN * sr + w] & ((1ull << cell) - 1ull));
+        for (uint32_t w2 = 0; w2 < w; ++w2) pos += (uint32_t)__popcll(rk.rmask[NWIN * sr + w2]);
+        pos = min(pos, (uint32_t)KMAX - 1u);
+        order[pos] = srcs[j];
+        ordtag[pos] = (uint8_t)(sr * NWIN + w);
       }
     }
     __syncthreads();
+    // the tables are dead: clear the windows
+    for (int k = lane; k < NWIN * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
 
-    // Pass B: rounds of 64 particles in (rank, cell) order.
+    // Pass B: rounds of 64 particles in (super-rank, window, cell) order.
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
       const uint32_t pos = r0 + (uint32_t)lane;
       const bool valid = pos < count;
-      const uint32_t ord = valid ? order[pos] : 0u;
-      const uint32_t slot = start + (ord & 0xFFFFu);
-      const uint32_t myrank = ord >> 16;
-      const uint32_t i = min(s.perm[valid ? slot : start], (uint32_t)s.N - 1u);
-      // The new state is stored in this processing order, (bin, rank, cell):
-      // the next step's gathers then run over nearly consecutive addresses.
-      // P2G writes x and id there; G2P reads x from the same slot, without
-      // an index indirection, and overwrites it with the advected position.
-      const uint32_t dst = start + min(pos, count - 1u);
+      const uint32_t at = min(pos, count - 1u);
+      const uint32_t i = order[at];
+      const uint32_t tag = ordtag[at];
+      const uint32_t mysr = tag / NWIN;
+      // The new state is stored in this processing order, (bin, super-rank,
+      // window, cell): the next step's gathers then run over nearly
+      // consecutive addresses.  P2G writes x and id there; G2P reads x from
+      // the same slot, without an index indirection, and overwrites it with
+      // the advected position.
+      const uint32_t dst = start + at;
       float xp[3], vp[3], Cp[9];
 #pragma unroll
       for (int a = 0; a < 3; ++a) {
@@ -717,15 +741,15 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       }
       const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
                 lz = min(max(b[2] - oz0, 0), CB - 1);
-      const int li0 = (lz * PW + ly) * PW + lx;
+      const int li0 = (int)(tag % NWIN) * PW3 + (lz * PW + ly) * PW + lx;
 
-      // One pass per distinct rank present in this round.
+      // One pass per distinct super-rank present in this round.
       bool todo = valid;
       for (;;) {
         const uint64_t tm = __ballot(todo);
         if (tm == 0ull) break;
-        const uint32_t rnow = (uint32_t)__builtin_amdgcn_readlane((int)myrank, __ffsll((unsigned long long)tm) - 1);
-        if (todo && myrank == rnow) {
+        const uint32_t rnow = (uint32_t)__builtin_amdgcn_readlane((int)mysr, __ffsll((unsigned long long)tm) - 1);
+        if (todo && mysr == rnow) {
           // Form the 27 node contributions here rather than keeping all 108 of
           // them live across the pass loop (register pressure limits occupancy).
 #pragma unroll
@@ -765,12 +789,12 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
                 }
                 const float wt = w[0][ox] * wyz;
                 const int li = li0 + (oz * PW + oy) * PW + ox;
-                float4 g = win[li];
+                float4 g = sm.win[li];
                 g.x = fmaf(wt, mass, g.x);
                 g.y = fmaf(wt, qx[0], g.y);
                 g.z = fmaf(wt, qx[1], g.z);
                 g.w = fmaf(wt, qx[2], g.w);
-                win[li] = g;
+                sm.win[li] = g;
                 // keep this read-modify-write ahead of the next one in issue order
                 __asm__ __volatile__("" ::: "memory");
               }
@@ -782,22 +806,39 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     }
     __syncthreads();
 
-    // Flush: one native global float atomic per nonzero window value.  Four
-    // lanes per node (one channel each), so each atomic instruction covers 16
-    // nodes' contiguous float4 records.
+    // Flush: the windows' sum, one native global float atomic per nonzero
+    // value.  Four lanes per node (one channel each), so each atomic
+    // instruction covers 16 consecutive window nodes' float4 records; the
+    // node coordinate advances by 16 = 2 rows + 4 per step.
     uint32_t mark = 0u;
-    const float *winf = reinterpret_cast<const float *>(win);
-    for (int e = lane; e < 4 * PW3; e += 64) {
-      const int k = e >> 2, chn = e & 3;
-      const float mval = winf[4 * k];
-      const float val = winf[e];
-      const int wx = k % PW, wy = (k / PW) % PW, wz = k / (PW * PW);
-      const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-      if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n) {
-        float *dst = reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz)) + chn;
-        unsafeAtomicAdd(dst, val);
-        const int bit = (((gz >> 3) - (oz0 >> 3)) << 2) | (((gy >> 3) - (oy0 >> 3)) << 1) | ((gx >> 3) - (ox0 >> 3));
-        mark |= 1u << bit;
+    {
+      const float *winf = reinterpret_cast<const float *>(sm.win);
+      const int chn = lane & 3;
+      int k = lane >> 2, wx = k % PW, wy = k / PW, wz = 0;
+      for (; k < PW3; k += 16) {
+        float mval = 0.f, val = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWIN; ++w) {
+          mval += winf[4 * (w * PW3 + k)];
+          val += winf[4 * (w * PW3 + k) + chn];
+        }
+        const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+        if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n) {
+          float *dst = reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz)) + chn;
+          unsafeAtomicAdd(dst, val);
+          const int bit = (((gz >> 3) - (oz0 >> 3)) << 2) | (((gy >> 3) - (oy0 >> 3)) << 1) | ((gx >> 3) - (ox0 >> 3));
+          mark |= 1u << bit;
+        }
+        wx += 4;
+        wy += 2;
+        if (wx >= PW) {
+          wx -= PW;
+          ++wy;
+        }
+        if (wy >= PW) {
+          wy -= PW;
+          ++wz;
+        }
       }
     }
     for (int d = 32; d >= 1; d >>= 1) mark |= (uint32_t)__shfl_xor((int)mark, d);
