@@ -102,7 +102,8 @@ size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles);
  * page's problem statement: material points carried across a background
  * grid by explicit steps).
  *   params      : host, read during the call.
- *   n_particles : 0 <= n < 2^31.
+ *   n_particles : 0 <= n < 2^28 (element offsets inside the 9-component
+ *                 per-particle fields are 32-bit).
  *   x0          : device, (N,3) float32 row-major positions (required if N > 0).
  *   v0          : device, (N,3) velocities, or NULL for zero.
  *   C0          : device, (N,3,3) row-major APIC affine matrices, or NULL for zero.

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
   const PBuf b = s.buf[0];
-  const int Np = s.Np;
+  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
   uint32_t key = 0;
   if (valid) {
     bool bad = false;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(WG) void k_permute_init(SimDev s) {
   const uint32_t slot = blockIdx.x * WG + threadIdx.x;
   const bool valid = slot < (uint32_t)s.N;
   const PBuf a = s.buf[0], b = s.buf[1];
-  const int Np = s.Np;
+  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
   uint32_t key = 0;
   if (valid) {
     const uint32_t i = min(s.perm[slot], (uint32_t)s.N - 1u);
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
 
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
-  const int Np = s.Np;
+  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
   // Workgroup b runs on XCD b % 8 and takes every (grid/8)-th chunk of that
   // XCD's contiguous (Morton-ordered, so spatially compact) share of the
   // chunk list.  Static assignment: no contended atomics on a work queue.
@@ -899,7 +899,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
   __shared__ float4 win[PW3];
   const PBuf out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
-  const int Np = s.Np;
+  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
   const float fn = s.fn;
   const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
   const uint32_t nch = s.ctr[CTR_NCHUNKS];
@@ -1005,7 +1005,7 @@ __global__ __launch_bounds__(WG) void k_read_particles(SimDev s, int cur, float 
   const uint32_t slot = blockIdx.x * WG + threadIdx.x;
   if (slot >= (uint32_t)s.N) return;
   const PBuf b = s.buf[cur];
-  const int Np = s.Np;
+  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
   const size_t id = b.id[slot];
   if (id >= (size_t)s.N) return;
   const bool pending = s.ctr[CTR_PENDING] != 0u;
@@ -1265,7 +1265,7 @@ void release(mpm_sim *sim) {
 extern "C" {
 
 size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles) {
-  if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 31)) return 0;
+  if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 28)) return 0;
   // The per-particle modulus array is always reserved so that one size fits
   // both the uniform and the per-particle case.
   return layout(params, n_particles, true, nullptr, nullptr);
@@ -1276,7 +1276,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
                mpm_sim **out) {
   if (!out) return MPM_ERR_INVALID_ARG;
   *out = nullptr;
-  if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 31)) return MPM_ERR_INVALID_ARG;
+  if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 28)) return MPM_ERR_INVALID_ARG;
   if (n_particles > 0 && !x0) return MPM_ERR_INVALID_ARG;
   const size_t need = mpm_workspace_bytes(params, n_particles);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)

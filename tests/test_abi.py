@@ -57,6 +57,8 @@ def test_workspace_bytes_scales_and_rejects_bad_params():
         assert mpm.mpm_workspace_bytes(good_params(**bad), 1000) == 0, bad
     assert mpm.mpm_workspace_bytes(good_params(), -1) == 0
     assert mpm.mpm_workspace_bytes(good_params(), 1 << 31) == 0
+    assert mpm.mpm_workspace_bytes(good_params(), 1 << 28) == 0  # 32-bit element offsets
+    assert mpm.mpm_workspace_bytes(good_params(), (1 << 28) - 1) > 0
     p = good_params()
     p.struct_size = 8
     assert mpm.mpm_workspace_bytes(p, 10) == 0
