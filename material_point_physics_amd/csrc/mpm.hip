@@ -102,10 +102,23 @@ struct SimDev {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Node-blocked grid index: blocks of 8^3 nodes, x fastest inside and across blocks.
+// Node-blocked grid index: blocks of 8^3 nodes (x fastest across blocks);
+// inside a block, 4^3 cubes of 2x2x2 nodes (x fastest), and inside a cube
+// the 8 nodes with x fastest.  A cube's 8 float4 records fill one 128-byte
+// line, and every P2G/G2P window (6^3 nodes at an even origin) covers
+// exactly 27 whole cubes, so its flush and its load touch 27 lines.
 __device__ __forceinline__ uint32_t node_index(const SimDev &s, int gx, int gy, int gz) {
   const uint32_t blk = ((uint32_t)(gz >> 3) * s.nb + (uint32_t)(gy >> 3)) * s.nb + (uint32_t)(gx >> 3);
-  return (blk << 9) | ((uint32_t)(gz & 7) << 6) | ((uint32_t)(gy & 7) << 3) | (uint32_t)(gx & 7);
+  const uint32_t cube = ((uint32_t)((gz >> 1) & 3) << 4) | ((uint32_t)((gy >> 1) & 3) << 2) | (uint32_t)((gx >> 1) & 3);
+  const uint32_t in_cube = ((uint32_t)(gz & 1) << 2) | ((uint32_t)(gy & 1) << 1) | (uint32_t)(gx & 1);
+  return (blk << 9) | (cube << 3) | in_cube;
+}
+// Inverse of the in-block part of node_index: local index -> node offsets.
+__device__ __forceinline__ void block_local_coords(int local, int &lx, int &ly, int &lz) {
+  const int cube = local >> 3, in_cube = local & 7;
+  lx = ((cube & 3) << 1) | (in_cube & 1);
+  ly = (((cube >> 2) & 3) << 1) | ((in_cube >> 1) & 1);
+  lz = ((cube >> 4) << 1) | (in_cube >> 2);
 }
 
 // Base node floor(x/dx - 1/2) of a position already inside the clamp box.
@@ -807,45 +820,49 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     __syncthreads();
 
     // Flush: the windows' sum, one native global float atomic per nonzero
-    // value.  Four lanes per node (one channel each), so each atomic
-    // instruction covers 16 consecutive window nodes' float4 records; the
-    // node coordinate advances by 16 = 2 rows + 4 per step.
-    uint32_t mark = 0u;
+    // value, in whole cubes: lane = (cube, node in cube, channel), so each
+    // atomic instruction covers two cubes = two full 128-byte lines (the
+    // memory-side atomic units work per line).
     {
-      const float *winf = reinterpret_cast<const float *>(sm.win);
-      const int chn = lane & 3;
-      int k = lane >> 2, wx = k % PW, wy = k / PW, wz = 0;
-      for (; k < PW3; k += 16) {
+      // cube cb = 2t + lane / 32 at cube coordinates (cx, cy, cz), advanced
+      // by 2 cubes per step
+      const int j = (lane >> 2) & 7, chn = lane & 3;
+      int cb = lane >> 5, cx = cb, cy = 0, cz = 0;
+#pragma unroll 1
+      for (; cb < 27; cb += 2) {
+        const int wx = 2 * cx + (j & 1), wy = 2 * cy + ((j >> 1) & 1), wz = 2 * cz + (j >> 2);
+        const int k = (wz * PW + wy) * PW + wx;
+        const float *winf = reinterpret_cast<const float *>(sm.win) + 4 * k;
         float mval = 0.f, val = 0.f;
 #pragma unroll
         for (int w = 0; w < NWIN; ++w) {
-          mval += winf[4 * (w * PW3 + k)];
-          val += winf[4 * (w * PW3 + k) + chn];
+          mval += winf[4 * w * PW3];
+          val += winf[4 * w * PW3 + chn];
         }
         const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-        if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n) {
-          float *dst = reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz)) + chn;
-          unsafeAtomicAdd(dst, val);
-          const int bit = (((gz >> 3) - (oz0 >> 3)) << 2) | (((gy >> 3) - (oy0 >> 3)) << 1) | ((gx >> 3) - (ox0 >> 3));
-          mark |= 1u << bit;
+        if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n)
+          unsafeAtomicAdd(reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz)) + chn, val);
+        cx += 2;
+        if (cx >= 3) {
+          cx -= 3;
+          ++cy;
         }
-        wx += 4;
-        wy += 2;
-        if (wx >= PW) {
-          wx -= PW;
-          ++wy;
-        }
-        if (wy >= PW) {
-          wy -= PW;
-          ++wz;
+        if (cy >= 3) {
+          cy -= 3;
+          ++cz;
         }
       }
     }
-    for (int d = 32; d >= 1; d >>= 1) mark |= (uint32_t)__shfl_xor((int)mark, d);
-    if (lane < 8 && ((mark >> lane) & 1u)) {
-      const uint32_t nbk = ((uint32_t)((oz0 >> 3) + (lane >> 2)) * s.nb + (uint32_t)((oy0 >> 3) + ((lane >> 1) & 1))) * s.nb +
-                           (uint32_t)((ox0 >> 3) + (lane & 1));
-      s.active_flag[nbk] = 1u;  // plain store; the grid update scans the flags
+    // Mark the (at most 2x2x2) node-blocks the window overlaps; the grid
+    // update scans these flags.  A marked block whose nodes got no mass is
+    // updated to zero velocity, which is harmless.  Plain stores: every
+    // writer stores the same value.
+    if (lane < 8) {
+      const int bx = (ox0 >> 3) + (lane & 1), by = (oy0 >> 3) + ((lane >> 1) & 1), bz = (oz0 >> 3) + (lane >> 2);
+      const int ex = min(ox0 + PW - 1, s.n - 1) >> 3, ey = min(oy0 + PW - 1, s.n - 1) >> 3,
+                ez = min(oz0 + PW - 1, s.n - 1) >> 3;
+      if (bx <= ex && by <= ey && bz <= ez)
+        s.active_flag[((uint32_t)bz * (uint32_t)s.nb + (uint32_t)by) * (uint32_t)s.nb + (uint32_t)bx] = 1u;
     }
     __syncthreads();
   }
@@ -871,7 +888,9 @@ __global__ __launch_bounds__(WG) void k_grid_update(SimDev s) {
 #pragma unroll
     for (int j = 0; j < 512 / WG; ++j) {
       const int local = threadIdx.x + WG * j;
-      const int gx = bx * NB + (local & 7), gy = by * NB + ((local >> 3) & 7), gz = bz * NB + (local >> 6);
+      int lx, ly, lz;
+      block_local_coords(local, lx, ly, lz);
+      const int gx = bx * NB + lx, gy = by * NB + ly, gz = bz * NB + lz;
       const size_t gi = ((size_t)blk << 9) + local;
       const float4 acc = s.gridA[gi];
       float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
@@ -908,12 +927,32 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
     const uint4 ch = s.chunks[c];
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
-    // window load (nodes outside the grid read as zero)
-    for (int k = lane; k < PW3; k += 64) {
-      const int gx = ox0 + k % PW, gy = oy0 + (k / PW) % PW, gz = oz0 + k / (PW * PW);
-      float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (gx < s.n && gy < s.n && gz < s.n) g = s.gridV[node_index(s, gx, gy, gz)];
-      win[k] = g;
+    // Window load in whole cubes (one 128-byte line each): lane = (cube,
+    // node in cube), 8 cubes per load instruction.  Nodes outside the grid
+    // read as zero.
+    {
+      // cube cb = 8t + lane / 8 at cube coordinates (cx, cy, cz), advanced
+      // by 8 = 2 rows + 2 cubes per step
+      const int j = lane & 7;
+      int cb = lane >> 3, cx = cb % 3, cy = cb / 3, cz = 0;
+#pragma unroll 1
+      for (; cb < 27; cb += 8) {
+        const int wx = 2 * cx + (j & 1), wy = 2 * cy + ((j >> 1) & 1), wz = 2 * cz + (j >> 2);
+        const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gx < s.n && gy < s.n && gz < s.n) g = s.gridV[node_index(s, gx, gy, gz)];
+        win[(wz * PW + wy) * PW + wx] = g;
+        cx += 2;
+        cy += 2;
+        if (cx >= 3) {
+          cx -= 3;
+          ++cy;
+        }
+        if (cy >= 3) {
+          cy -= 3;
+          ++cz;
+        }
+      }
     }
     __syncthreads();
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
@@ -1049,7 +1088,9 @@ __global__ __launch_bounds__(WG) void k_read_grid(SimDev s, float *__restrict__ 
     const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
               bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
     for (int local = threadIdx.x; local < 512; local += WG) {
-      const int gx = bx * NB + (local & 7), gy = by * NB + ((local >> 3) & 7), gz = bz * NB + (local >> 6);
+      int lx, ly, lz;
+      block_local_coords(local, lx, ly, lz);
+      const int gx = bx * NB + lx, gy = by * NB + ly, gz = bz * NB + lz;
       if (gx >= n || gy >= n || gz >= n) continue;
       const float4 g = s.gridV[((size_t)blk << 9) + local];
       const size_t lin = (size_t)gx + (size_t)n * ((size_t)gy + (size_t)n * gz);
