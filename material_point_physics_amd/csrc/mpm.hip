@@ -1341,6 +1341,9 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_p2g<MPM_FIXED_COROTATED, false>, 64, 0) != hipSuccess ||
         occ <= 0)
       occ = 16;
+    // Measured: 4 waves per SIMD (16 single-wave workgroups per CU) is
+    // P2G's best launch; fewer expose latency and more slowed the kernel.
+    occ = occ < 16 ? occ : 16;
     sim->grid_p2g = ((cus * occ + NQ - 1) / NQ) * NQ;
     int occ_g = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
