@@ -86,7 +86,8 @@ struct SimDev {
   float lo, hi;               // position clamp
   uint32_t max_chunks;
   PBuf buf[2];
-  uint32_t *perm, *key;
+  uint32_t *perm, *key;         // key = bin | cell << KEY_CELL_SHIFT (cell of the base node in its bin)
+  uint8_t *cellp;              // cell of the base node in its bin, in perm (sorted) order
   uint32_t *bin_count, *bin_cursor;
   uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
   int32_t ntiles;
@@ -147,6 +148,13 @@ __device__ __forceinline__ uint32_t compact3(uint32_t v) {
 // nodes, compact per-XCD work ranges).
 __device__ __forceinline__ uint32_t bin_key(const SimDev &, int bx, int by, int bz) {
   return spread3((uint32_t)bx >> 2) | (spread3((uint32_t)by >> 2) << 1) | (spread3((uint32_t)bz >> 2) << 2);
+}
+
+// Cell of a base node within its 4^3-cell bin (x fastest), and the key word
+// that carries it above the bin index.  grid_n <= 1024 keeps bins below 2^24.
+constexpr int KEY_CELL_SHIFT = 24;
+__device__ __forceinline__ uint32_t cell_in_bin(int bx, int by, int bz) {
+  return ((uint32_t)(bz & 3) << 4) | ((uint32_t)(by & 3) << 2) | (uint32_t)(bx & 3);
 }
 
 // Quadratic B-spline weights of nodes base+0,1,2 at fractional offset f in [0.5,1.5).
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
     if (s.has_E) b.E[i] = E_p[i];
     b.id[i] = i;
     key = bin_key(s, base[0], base[1], base[2]);
-    s.key[i] = key;
+    s.key[i] = key | (cell_in_bin(base[0], base[1], base[2]) << KEY_CELL_SHIFT);
   }
   wave_aggregated_increment(s.bin_count, key, valid);
 }
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(WG) void k_permute_init(SimDev s) {
     if (s.has_E) b.E[slot] = a.E[i];
     b.id[slot] = a.id[i];
     key = bin_key(s, base[0], base[1], base[2]);
-    s.key[slot] = key;
+    s.key[slot] = key | (cell_in_bin(base[0], base[1], base[2]) << KEY_CELL_SHIFT);
   }
   wave_aggregated_increment(s.bin_count, key, valid);
 }
@@ -487,9 +495,13 @@ __global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
 __global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
-  const uint32_t key = valid ? s.key[i] : 0u;
+  const uint32_t kc = valid ? s.key[i] : 0u;
+  const uint32_t key = kc & ((1u << KEY_CELL_SHIFT) - 1u);
   const uint32_t slot = wave_aggregated_increment(s.bin_cursor, key, valid);
-  if (valid && slot < (uint32_t)s.N) s.perm[slot] = i;
+  if (valid && slot < (uint32_t)s.N) {
+    s.perm[slot] = i;
+    s.cellp[slot] = (uint8_t)(kc >> KEY_CELL_SHIFT);
+  }
 }
 
 // P2G.  Persistent single-wavefront workgroups take chunks (<= KMAX particles
@@ -539,10 +551,34 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   const bool pending = s.ctr[CTR_PENDING] != 0u;
   const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
 
+  // A chunk's sorted source indices and cells are loaded one chunk ahead,
+  // during the previous chunk's pass B, so pass A starts with them in
+  // registers (lanes past the count get an invalid source and cell 0).
+  uint32_t pf_src[KMAX / 64], pf_cell[KMAX / 64];
+  auto prefetch = [&](const uint4 &chrec) {
+    const uint32_t pstart = chrec.x, pcount = min(chrec.y, (uint32_t)KMAX);
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      const uint32_t qi = (uint32_t)(64 * j + lane);
+      pf_src[j] = 0xFFFFFFFFu;
+      pf_cell[j] = 0u;
+      if (qi < pcount) {
+        pf_src[j] = min(s.perm[pstart + qi], (uint32_t)s.N - 1u);
+        pf_cell[j] = (uint32_t)s.cellp[pstart + qi] & (uint32_t)(CB3 - 1);
+      }
+    }
+  };
+  uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
+  if (qbeg + wq < qend) {
+    ch_next = s.chunks[qbeg + wq];
+    prefetch(ch_next);
+  }
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
-    const uint4 ch = s.chunks[c];
+    const uint4 ch = ch_next;
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;  // first base node of the bin = window origin
+    const bool has_next = c + nwq < qend;
+    if (has_next) ch_next = s.chunks[c + nwq];
 
     // Pass A: cell of each particle and its rank within the cell.  Ranks
     // follow the particles' previous storage order (their source index), so
@@ -555,21 +591,13 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     // records the group's size (leaders have distinct cells: no atomics).
     P2GRankTables &rk = sm.rk;
     const uint64_t below = (1ull << lane) - 1ull;
-    // all global loads of the pass first, so their latencies overlap
+    // (source index and cell come in sorted order: the scatter carried the
+    // cell that G2P computed with the key, so no position gather is needed)
     uint32_t cells[KMAX / 64], srcs[KMAX / 64], srcmin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
-      const uint32_t qi = (uint32_t)(64 * j + lane);
-      cells[j] = 0u;
-      uint32_t src = 0xFFFFFFFFu;
-      if (qi < count) {
-        const uint32_t i = min(s.perm[start + qi], (uint32_t)s.N - 1u);
-        src = i;
-        const int cx = min(max(base_node(in.x[i] * fn) - ox0, 0), CB - 1);
-        const int cy = min(max(base_node(in.x[Np + i] * fn) - oy0, 0), CB - 1);
-        const int cz = min(max(base_node(in.x[2 * Np + i] * fn) - oz0, 0), CB - 1);
-        cells[j] = (uint32_t)((cz * CB + cy) * CB + cx);
-      }
+      cells[j] = pf_cell[j];
+      uint32_t src = pf_src[j];
       srcs[j] = src;
       for (int d = 32; d >= 1; d >>= 1) src = min(src, (uint32_t)__shfl_xor((int)src, d));
       srcmin[j] = src;
@@ -646,6 +674,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     // the tables are dead: clear the windows
     for (int k = lane; k < NWIN * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
+
+    if (has_next) prefetch(ch_next);
 
     // Pass B: rounds of 64 particles in (super-rank, window, cell) order.
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
@@ -1026,7 +1056,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
           out.C[k * Np + slot] = ck;
         }
         key = bin_key(s, b[0], b[1], b[2]);
-        s.key[slot] = key;
+        s.key[slot] = key | (cell_in_bin(b[0], b[1], b[2]) << KEY_CELL_SHIFT);
         if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
@@ -1110,6 +1140,8 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool valid_params(const mpm_params *p) {
   if (!p || p->struct_size < sizeof(mpm_params)) return false;
+  // grid_n <= 1024: at most 256^3 bins, so a bin index fits below the cell
+  // bits of the key word (KEY_CELL_SHIFT)
   if (p->grid_n < 8 || p->grid_n > 1024) return false;
   if (!(p->dt > 0.f) || !std::isfinite(p->dt)) return false;
   for (int a = 0; a < 3; ++a)
@@ -1151,6 +1183,7 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   }
   uint32_t *perm = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *key = (uint32_t *)take(sizeof(uint32_t) * Np);
+  uint8_t *cellp = (uint8_t *)take(Np);
   uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
@@ -1192,6 +1225,7 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->buf[1] = bufs[1];
     d->perm = perm;
     d->key = key;
+    d->cellp = cellp;
     d->bin_count = cnt;
     d->bin_cursor = cur;
     d->tile_sum = tiles;
