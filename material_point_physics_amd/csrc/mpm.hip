@@ -1183,7 +1183,6 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   }
   uint32_t *perm = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *key = (uint32_t *)take(sizeof(uint32_t) * Np);
-  uint8_t *cellp = (uint8_t *)take(Np);
   uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
@@ -1194,6 +1193,9 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   uint32_t *status = (uint32_t *)take(sizeof(uint32_t) * MPM_STATUS_WORDS);
   float4 *gA = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
   float4 *gV = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  // (last: placed before the grid it shifted the grid arrays and measurably
+  // slowed the grid update)
+  uint8_t *cellp = (uint8_t *)take(Np);
   if (d) {
     d->N = (int32_t)N;
     d->Np = (int32_t)Np;
