@@ -11,16 +11,18 @@
 //   k_scan_*      two-phase exclusive scan of per-bin counts -> bin starts,
 //                 chunk list (<= KMAX particles of one bin per chunk)
 //   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), wave-
-//                 aggregated atomic cursors -> perm[slot] = source index
+//                 aggregated atomic cursors -> perm[slot] = source index, and
+//                 the particle's cell within its bin at the same position
 //   k_p2g         one wavefront per chunk: in-LDS counting sort by cell (second
 //                 radix digit, 64 cells = 64 lanes), deferred F update, polar
 //                 decomposition, Kirchhoff stress, APIC momentum, conflict-free
-//                 accumulation into a private 6^3-node LDS window, one native
-//                 global atomic flush per window node
+//                 accumulation into two private 6^3-node LDS windows, one
+//                 native global atomic flush per window node and channel
 //   k_grid_update active node-blocks only: v = p/m + dt g, sticky walls,
 //                 clears the P2G accumulator
-//   k_g2p         gather, APIC C, advection + clamp in the storage order P2G
-//                 chose; computes the next step's bin keys/counts
+//   k_g2p         one wavefront per chunk: the bin's 6^3-node velocity window
+//                 staged in LDS; gather, APIC C, advection + clamp in the
+//                 storage order P2G chose; the next step's bin keys/counts
 //
 // Deferred deformation gradient: [RT-MPM] (kernel-merging discussion) notes
 // that the F update at the end of G2P can be postponed to the start of P2G
@@ -53,7 +55,9 @@ constexpr int CB = 4;            // bin edge in cells: particles are bucketed by
 constexpr int CB3 = CB * CB * CB;  // 64 cells per bin = one wavefront
 constexpr int PW = CB + 2;       // P2G window edge: base nodes of a bin + stencil reach
 constexpr int PW3 = PW * PW * PW;  // 216 window nodes
-constexpr int KMAX = 256;        // particles per P2G chunk (4 rounds of one wavefront)
+constexpr int KMAX_SHIFT = 8;
+constexpr int KMAX = 1 << KMAX_SHIFT;  // particles per P2G chunk at most (4 rounds of one wavefront)
+constexpr int KMIN_SHIFT = 6;    // smallest chunk size: 64 particles (see mpm_create)
 constexpr int NQ = 8;            // P2G work queues, one per XCD
 constexpr int NUM_KERNELS = 6;
 
@@ -85,6 +89,7 @@ struct SimDev {
   float c_scale;              // 4 / dx (G2P: C = 4/dx^2 * sum w v (x_i - x_p), offsets in cells)
   float lo, hi;               // position clamp
   uint32_t max_chunks;
+  int32_t chunk_shift;        // chunks hold up to 2^chunk_shift (64..KMAX) particles of one bin
   PBuf buf[2];
   uint32_t *perm, *key;         // key = bin | cell << KEY_CELL_SHIFT (cell of the base node in its bin)
   uint8_t *cellp;              // cell of the base node in its bin, in perm (sorted) order
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
   for (int k = 0; k < SCAN_PER; ++k) {
     const uint32_t cnt = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
     c += cnt;
-    ch += (cnt + KMAX - 1) / KMAX;
+    ch += (cnt + (1u << s.chunk_shift) - 1u) >> s.chunk_shift;
   }
   uint32_t tc, tch;
   block_scan_incl<WG>(c, wsum, &tc);
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
 #pragma unroll
   for (int k = 0; k < SCAN_PER; ++k) {
     c[k] = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
-    ch[k] = (c[k] + KMAX - 1) / KMAX;
+    ch[k] = (c[k] + (1u << s.chunk_shift) - 1u) >> s.chunk_shift;
     csum += c[k];
     chsum += ch[k];
   }
@@ -479,8 +484,8 @@ __global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
     if (b < nbins) {
       s.bin_cursor[b] = run;
       for (uint32_t j = 0; j < ch[k]; ++j) {
-        const uint32_t off = j * KMAX;
-        s.chunks[chrun + j] = make_uint4(run + off, min((uint32_t)KMAX, c[k] - off), b, 0u);
+        const uint32_t off = j << s.chunk_shift;
+        s.chunks[chrun + j] = make_uint4(run + off, min(1u << s.chunk_shift, c[k] - off), b, 0u);
       }
       s.bin_count[b] = 0u;
     }
@@ -593,12 +598,16 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     const uint64_t below = (1ull << lane) - 1ull;
     // (source index and cell come in sorted order: the scatter carried the
     // cell that G2P computed with the key, so no position gather is needed)
+    // (sub-rounds past the chunk's count are skipped with uniform branches)
+    const uint32_t nsub = (count + 63u) / 64u;
     uint32_t cells[KMAX / 64], srcs[KMAX / 64], srcmin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       cells[j] = pf_cell[j];
       uint32_t src = pf_src[j];
       srcs[j] = src;
+      srcmin[j] = 0xFFFFFFFFu;
+      if ((uint32_t)j >= nsub) continue;
       for (int d = 32; d >= 1; d >>= 1) src = min(src, (uint32_t)__shfl_xor((int)src, d));
       srcmin[j] = src;
       rk.subcnt[j][lane] = 0u;
@@ -607,6 +616,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     uint32_t rin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
+      rin[j] = 0u;
+      if ((uint32_t)j >= nsub) continue;
       const bool v = (uint32_t)(64 * j + lane) < count;
       const uint32_t cell = cells[j];
       uint64_t peers = __ballot(v);
@@ -622,9 +633,12 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     uint32_t rank[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
+      rank[j] = 0u;
+      if ((uint32_t)j >= nsub) continue;
       uint32_t before = 0u;
 #pragma unroll
       for (int k = 0; k < KMAX / 64; ++k) {
+        if ((uint32_t)k >= nsub) continue;
         const bool earlier = srcmin[k] < srcmin[j] || (srcmin[k] == srcmin[j] && k < j);
         if (k != j && earlier) before += rk.subcnt[k][cells[j]];
       }
@@ -633,7 +647,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     {
       uint32_t total = 0u;
 #pragma unroll
-      for (int k = 0; k < KMAX / 64; ++k) total += rk.subcnt[k][lane];
+      for (int k = 0; k < KMAX / 64; ++k)
+        if ((uint32_t)k < nsub) total += rk.subcnt[k][lane];
       rk.hist[lane] = total;
     }
     __syncthreads();
@@ -661,7 +676,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       const uint32_t qi = (uint32_t)(64 * j + lane);
-      if (qi < count) {
+      if ((uint32_t)j < nsub && qi < count) {
         const uint32_t cell = cells[j], sr = rank[j] / NWIN, w = rank[j] % NWIN;
         uint32_t pos = rk.rstart[sr] + (uint32_t)__popcll(rk.rmask[NWIN * sr + w] & ((1ull << cell) - 1ull));
         for (uint32_t w2 = 0; w2 < w; ++w2) pos += (uint32_t)__popcll(rk.rmask[NWIN * sr + w2]);
@@ -1164,7 +1179,7 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   int nbin2 = 1;
   while (nbin2 < nbin) nbin2 <<= 1;
   const int64_t nbins = (int64_t)nbin2 * nbin2 * nbin2;
-  const int64_t max_chunks = (N + KMAX - 1) / KMAX + nbins;
+  const int64_t max_chunks = (N + (1 << KMIN_SHIFT) - 1) / (1 << KMIN_SHIFT) + nbins;
   const int fw = p->material == MPM_J_FLUID ? 1 : 9;
   size_t off = 0;
   auto take = [&](size_t bytes) -> char * {
@@ -1172,6 +1187,10 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     off += align_up(bytes);
     return ptr;
   };
+  // The grid first: its placement then does not depend on N or on the other
+  // arrays (shifting it by tens of MB measurably changed the grid update).
+  float4 *gA = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  float4 *gV = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
   PBuf bufs[2];
   for (int k = 0; k < 2; ++k) {
     bufs[k].x = (float *)take(sizeof(float) * 3 * Np);
@@ -1191,10 +1210,6 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   uint4 *chunks = (uint4 *)take(sizeof(uint4) * max_chunks);
   uint32_t *ctr = (uint32_t *)take(sizeof(uint32_t) * CTR_WORDS);
   uint32_t *status = (uint32_t *)take(sizeof(uint32_t) * MPM_STATUS_WORDS);
-  float4 *gA = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
-  float4 *gV = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
-  // (last: placed before the grid it shifted the grid arrays and measurably
-  // slowed the grid update)
   uint8_t *cellp = (uint8_t *)take(Np);
   if (d) {
     d->N = (int32_t)N;
@@ -1223,6 +1238,7 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->lo = 2.0f * d->dx;
     d->hi = (float)(n - 2) * d->dx;
     d->max_chunks = (uint32_t)max_chunks;
+    d->chunk_shift = KMAX_SHIFT;
     d->buf[0] = bufs[0];
     d->buf[1] = bufs[1];
     d->perm = perm;
@@ -1381,6 +1397,15 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     // P2G's best launch; fewer expose latency and more slowed the kernel.
     occ = occ < 16 ? occ : 16;
     sim->grid_p2g = ((cus * occ + NQ - 1) / NQ) * NQ;
+    // Chunk size: KMAX particles when there is enough work for every P2G
+    // wavefront, else smaller (down to 64), so that a small scene's few bins
+    // still spread over many wavefronts: the step time of small scenes is
+    // the latency of one wavefront's chunks.
+    {
+      int shift = KMAX_SHIFT;
+      while (shift > KMIN_SHIFT && ((int64_t)d.N >> shift) < (int64_t)sim->grid_p2g) --shift;
+      sim->d.chunk_shift = shift;
+    }
     int occ_g = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
       occ_g = 16;
