@@ -1022,37 +1022,51 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
         const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
                   lz = min(max(b[2] - oz0, 0), CB - 1);
         const int li0 = (lz * PW + ly) * PW + lx;
-        // v = sum w v_i and B = sum w v_i (o - f)^T, reduced along x first for
-        // each (y, z) row: S = sum_x w_x v_i, T = sum_x w_x (ox - f_x) v_i.
-        float wd0[3];
-#pragma unroll
-        for (int o = 0; o < 3; ++o) wd0[o] = w[0][o] * d[0][o];
+        // v = sum w v_i and B = sum w v_i (o - f)^T.  The quadratic B-spline's
+        // first moment sum_o w_o (o - f) = 0 gives the columns as
+        // B_a = sum w o_a v_i - f_a v.  Reduced along x first for each (y, z)
+        // row: S = sum_x w_x v_i and U = sum_x w_x ox v_i; offsets equal to
+        // zero add nothing, so rows with oy = 0 (oz = 0) skip the y (z)
+        // column.
+        const float w2x = 2.f * w[0][2];
         float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int oz = 0; oz < 3; ++oz)
 #pragma unroll
           for (int oy = 0; oy < 3; ++oy) {
-            float S[3] = {0.f, 0.f, 0.f}, T[3] = {0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ox = 0; ox < 3; ++ox) {
-              const float4 g = win[li0 + (oz * PW + oy) * PW + ox];
-              S[0] = fmaf(w[0][ox], g.x, S[0]);
-              S[1] = fmaf(w[0][ox], g.y, S[1]);
-              S[2] = fmaf(w[0][ox], g.z, S[2]);
-              T[0] = fmaf(wd0[ox], g.x, T[0]);
-              T[1] = fmaf(wd0[ox], g.y, T[1]);
-              T[2] = fmaf(wd0[ox], g.z, T[2]);
-            }
+            float S[3], U[3];
+            const float4 g0 = win[li0 + (oz * PW + oy) * PW + 0];
+            const float4 g1 = win[li0 + (oz * PW + oy) * PW + 1];
+            const float4 g2 = win[li0 + (oz * PW + oy) * PW + 2];
+            S[0] = w[0][0] * g0.x;
+            S[1] = w[0][0] * g0.y;
+            S[2] = w[0][0] * g0.z;
+            U[0] = w[0][1] * g1.x;
+            U[1] = w[0][1] * g1.y;
+            U[2] = w[0][1] * g1.z;
+            S[0] = fmaf(w[0][1], g1.x, S[0]);
+            S[1] = fmaf(w[0][1], g1.y, S[1]);
+            S[2] = fmaf(w[0][1], g1.z, S[2]);
+            S[0] = fmaf(w[0][2], g2.x, S[0]);
+            S[1] = fmaf(w[0][2], g2.y, S[1]);
+            S[2] = fmaf(w[0][2], g2.z, S[2]);
+            U[0] = fmaf(w2x, g2.x, U[0]);
+            U[1] = fmaf(w2x, g2.y, U[1]);
+            U[2] = fmaf(w2x, g2.z, U[2]);
             const float wyz = w[1][oy] * w[2][oz];
-            const float wyz1 = wyz * d[1][oy], wyz2 = wyz * d[2][oz];
+            const float wyz2 = wyz + wyz;
 #pragma unroll
             for (int a = 0; a < 3; ++a) {
               v[a] = fmaf(wyz, S[a], v[a]);
-              B[a * 3 + 0] = fmaf(wyz, T[a], B[a * 3 + 0]);
-              B[a * 3 + 1] = fmaf(wyz1, S[a], B[a * 3 + 1]);
-              B[a * 3 + 2] = fmaf(wyz2, S[a], B[a * 3 + 2]);
+              B[a * 3 + 0] = fmaf(wyz, U[a], B[a * 3 + 0]);
+              if (oy > 0) B[a * 3 + 1] = fmaf(oy == 1 ? wyz : wyz2, S[a], B[a * 3 + 1]);
+              if (oz > 0) B[a * 3 + 2] = fmaf(oz == 1 ? wyz : wyz2, S[a], B[a * 3 + 2]);
             }
           }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+          for (int k = 0; k < 3; ++k) B[a * 3 + k] = fmaf(d[k][0], v[a], B[a * 3 + k]);  // d[k][0] = -f_k
         bool clamped = false, nonfinite = false;
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
@@ -1070,7 +1084,10 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
           if (!isfinite(ck)) nonfinite = true;
           out.C[k * Np + slot] = ck;
         }
-        key = bin_key(s, b[0], b[1], b[2]);
+        // the next bin: nearly always the chunk's own (Morton encoding only
+        // when some lane of the wavefront left it)
+        const bool same_bin = (b[0] >> 2) == (ox0 >> 2) && (b[1] >> 2) == (oy0 >> 2) && (b[2] >> 2) == (oz0 >> 2);
+        key = (__ballot(!same_bin) == 0ull) ? bin : bin_key(s, b[0], b[1], b[2]);
         s.key[slot] = key | (cell_in_bin(b[0], b[1], b[2]) << KEY_CELL_SHIFT);
         if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
@@ -1409,6 +1426,9 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     int occ_g = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
       occ_g = 16;
+    // Measured: 5 waves per SIMD (20 workgroups per CU) is G2P's best launch;
+    // 24 per CU, which 74 VGPRs would allow, was slower.
+    occ_g = occ_g < 20 ? occ_g : 20;
     sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
     sim->grid_update = cus * 8;
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
