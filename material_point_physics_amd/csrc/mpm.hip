@@ -7,22 +7,22 @@
 // B-splines, APIC transfer and the fixed-corotated model (Hu et al. 2018;
 // Jiang et al. 2015; Stomakhin et al. 2012).
 //
-// Step = 6 kernels, captured once into a HIP graph per buffer parity:
+// Step = 5 kernels, captured once into a HIP graph per buffer parity:
 //   k_scan_*      two-phase exclusive scan of per-bin counts -> bin starts,
 //                 chunk list (<= KMAX particles of one bin per chunk)
 //   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), wave-
 //                 aggregated atomic cursors -> perm[slot] = source index, and
-//                 the particle's cell within its bin at the same position
+//                 the particle's cell within its bin at the same position;
+//                 also clears the previous step's grid accumulator
 //   k_p2g         one wavefront per chunk: in-LDS counting sort by cell (second
 //                 radix digit, 64 cells = 64 lanes), deferred F update, polar
 //                 decomposition, Kirchhoff stress, APIC momentum, conflict-free
 //                 accumulation into two private 6^3-node LDS windows, one
 //                 native global atomic flush per window node and channel
-//   k_grid_update active node-blocks only: v = p/m + dt g, sticky walls,
-//                 clears the P2G accumulator
-//   k_g2p         one wavefront per chunk: the bin's 6^3-node velocity window
-//                 staged in LDS; gather, APIC C, advection + clamp in the
-//                 storage order P2G chose; the next step's bin keys/counts
+//   k_g2p         one wavefront per chunk: the grid update (v = p/m + dt g,
+//                 sticky walls) of the bin's 6^3-node window, staged in LDS;
+//                 gather, APIC C, advection + clamp in the storage order P2G
+//                 chose; the next step's bin keys/counts
 //
 // Deferred deformation gradient: [RT-MPM] (kernel-merging discussion) notes
 // that the F update at the end of G2P can be postponed to the start of P2G
@@ -59,7 +59,7 @@ constexpr int KMAX_SHIFT = 8;
 constexpr int KMAX = 1 << KMAX_SHIFT;  // particles per P2G chunk at most (4 rounds of one wavefront)
 constexpr int KMIN_SHIFT = 6;    // smallest chunk size: 64 particles (see mpm_create)
 constexpr int NQ = 8;            // P2G work queues, one per XCD
-constexpr int NUM_KERNELS = 6;
+constexpr int NUM_KERNELS = 5;
 
 enum Ctr : int {
   CTR_NCHUNKS = 0,
@@ -97,9 +97,12 @@ struct SimDev {
   uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
   int32_t ntiles;
   uint4 *chunks;
-  uint32_t *active_flag;  // per node-block state, see k_grid_update
-  float4 *gridA;  // P2G accumulator per node: (m, p_x, p_y, p_z)
-  float4 *gridV;  // updated grid per node: (v_x, v_y, v_z, m)
+  // Grid, double-buffered by step parity (the particle buffer the step reads):
+  // the step with parity q accumulates into gridA[q] and marks the node-blocks
+  // it touched in active_flag[q]; its G2P reads gridA[q]; the next step's
+  // scatter clears them (and their flags) while it accumulates into the other.
+  uint32_t *active_flag[2];  // per node-block: 1 = touched by that step's P2G
+  float4 *gridA[2];          // P2G accumulator per node: (m, p_x, p_y, p_z)
   uint32_t *ctr;
   uint32_t *status;
 };
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
 
 // Bucket scatter: particle i of the current order goes to the next free slot
 // of its block.  One atomic per distinct block per wavefront.
-__global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
+__global__ __launch_bounds__(WG) void k_scatter(SimDev s, int src) {
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
   const uint32_t kc = valid ? s.key[i] : 0u;
@@ -506,6 +509,16 @@ __global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
   if (valid && slot < (uint32_t)s.N) {
     s.perm[slot] = i;
     s.cellp[slot] = (uint8_t)(kc >> KEY_CELL_SHIFT);
+  }
+  // Clear the previous step's accumulator: the node-blocks it marked (the
+  // other parity), and their marks.  Its G2P has finished reading them.
+  const int prev = src ^ 1;
+  for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+    if (s.active_flag[prev][blk] == 0u) continue;  // the same word for the whole workgroup
+    float4 *g = s.gridA[prev] + ((size_t)blk << 9);
+    for (int k = threadIdx.x; k < 512; k += WG) g[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();  // every thread has read the mark before it is reset
+    if (threadIdx.x == 0) s.active_flag[prev][blk] = 0u;
   }
 }
 
@@ -886,7 +899,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         }
         const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
         if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n)
-          unsafeAtomicAdd(reinterpret_cast<float *>(s.gridA + node_index(s, gx, gy, gz)) + chn, val);
+          unsafeAtomicAdd(reinterpret_cast<float *>(s.gridA[src] + node_index(s, gx, gy, gz)) + chn, val);
         cx += 2;
         if (cx >= 3) {
           cx -= 3;
@@ -898,58 +911,35 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         }
       }
     }
-    // Mark the (at most 2x2x2) node-blocks the window overlaps; the grid
-    // update scans these flags.  A marked block whose nodes got no mass is
-    // updated to zero velocity, which is harmless.  Plain stores: every
-    // writer stores the same value.
+    // Mark the (at most 2x2x2) node-blocks the window overlaps: the next
+    // step's scatter clears exactly these (and mpm_read_grid reads them).  A
+    // marked block whose nodes got no mass is cleared for nothing, which is
+    // harmless.  Plain stores: every writer stores the same value.
     if (lane < 8) {
       const int bx = (ox0 >> 3) + (lane & 1), by = (oy0 >> 3) + ((lane >> 1) & 1), bz = (oz0 >> 3) + (lane >> 2);
       const int ex = min(ox0 + PW - 1, s.n - 1) >> 3, ey = min(oy0 + PW - 1, s.n - 1) >> 3,
                 ez = min(oz0 + PW - 1, s.n - 1) >> 3;
       if (bx <= ex && by <= ey && bz <= ez)
-        s.active_flag[((uint32_t)bz * (uint32_t)s.nb + (uint32_t)by) * (uint32_t)s.nb + (uint32_t)bx] = 1u;
+        s.active_flag[src][((uint32_t)bz * (uint32_t)s.nb + (uint32_t)by) * (uint32_t)s.nb + (uint32_t)bx] = 1u;
     }
     __syncthreads();
   }
 }
 
-// Grid update over the node-blocks P2G touched (flag 1): v = p/m + dt g where
-// m > 0, sticky walls, store (v, m), clear the accumulator.  Block flags:
-// 1 = touched by this step's P2G, 2 = updated in the last step (read back by
-// mpm_read_grid), 0 = idle.  A block left at 2 by the previous step and not
-// touched now returns to 0.
-__global__ __launch_bounds__(WG) void k_grid_update(SimDev s) {
+// The grid update (a4) -- v = p/m + dt g where m > 0, sticky walls -- is
+// evaluated by G2P on its window nodes as it loads them (grid_velocity), and
+// the accumulator is cleared by the next step's scatter, so the step needs no
+// separate pass over the grid.
+__device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int gx, int gy, int gz) {
   const int n = s.n, wall = s.wall;
-  for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
-    const uint32_t flag = s.active_flag[blk];
-    if (flag == 0u) continue;
-    __syncthreads();  // every thread has read the flag before it changes
-    if (flag == 2u) {
-      if (threadIdx.x == 0) s.active_flag[blk] = 0u;
-      continue;
-    }
-    const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
-              bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
-#pragma unroll
-    for (int j = 0; j < 512 / WG; ++j) {
-      const int local = threadIdx.x + WG * j;
-      int lx, ly, lz;
-      block_local_coords(local, lx, ly, lz);
-      const int gx = bx * NB + lx, gy = by * NB + ly, gz = bz * NB + lz;
-      const size_t gi = ((size_t)blk << 9) + local;
-      const float4 acc = s.gridA[gi];
-      float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
-      const bool in_wall = gx < wall || gy < wall || gz < wall || gx >= n - wall || gy >= n - wall || gz >= n - wall;
-      if (acc.x > 0.f && !in_wall) {
-        o.x = acc.y / acc.x + s.dt * s.g[0];
-        o.y = acc.z / acc.x + s.dt * s.g[1];
-        o.z = acc.w / acc.x + s.dt * s.g[2];
-      }
-      s.gridV[gi] = o;
-      s.gridA[gi] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (threadIdx.x == 0) s.active_flag[blk] = 2u;
+  float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
+  const bool in_wall = gx < wall || gy < wall || gz < wall || gx >= n - wall || gy >= n - wall || gz >= n - wall;
+  if (acc.x > 0.f && !in_wall) {
+    o.x = acc.y / acc.x + s.dt * s.g[0];
+    o.y = acc.z / acc.x + s.dt * s.g[1];
+    o.z = acc.w / acc.x + s.dt * s.g[2];
   }
+  return o;
 }
 
 // G2P: gather, APIC C, advection and clamp.  Persistent single-wavefront
@@ -985,7 +975,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
         const int wx = 2 * cx + (j & 1), wy = 2 * cy + ((j >> 1) & 1), wz = 2 * cz + (j >> 2);
         const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
         float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gx < s.n && gy < s.n && gz < s.n) g = s.gridV[node_index(s, gx, gy, gz)];
+        if (gx < s.n && gy < s.n && gz < s.n) g = grid_velocity(s, s.gridA[src][node_index(s, gx, gy, gz)], gx, gy, gz);
         win[(wz * PW + wy) * PW + wx] = g;
         cx += 2;
         cy += 2;
@@ -1142,11 +1132,13 @@ __global__ __launch_bounds__(WG) void k_read_particles(SimDev s, int cur, float 
   }
 }
 
-// Readback of the grid: active blocks -> dense (i + n (j + n k)) arrays.
-__global__ __launch_bounds__(WG) void k_read_grid(SimDev s, float *__restrict__ mass, float *__restrict__ mom) {
+// Readback of the grid after the last step (parity q): the node-blocks it
+// marked, updated as G2P saw them (v = p/m + dt g, walls) -> dense
+// (i + n (j + n k)) arrays of m and m v.
+__global__ __launch_bounds__(WG) void k_read_grid(SimDev s, int q, float *__restrict__ mass, float *__restrict__ mom) {
   const int n = s.n;
   for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
-    if (s.active_flag[blk] != 2u) continue;
+    if (s.active_flag[q][blk] == 0u) continue;
     const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
               bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
     for (int local = threadIdx.x; local < 512; local += WG) {
@@ -1154,7 +1146,7 @@ __global__ __launch_bounds__(WG) void k_read_grid(SimDev s, float *__restrict__ 
       block_local_coords(local, lx, ly, lz);
       const int gx = bx * NB + lx, gy = by * NB + ly, gz = bz * NB + lz;
       if (gx >= n || gy >= n || gz >= n) continue;
-      const float4 g = s.gridV[((size_t)blk << 9) + local];
+      const float4 g = grid_velocity(s, s.gridA[q][((size_t)blk << 9) + local], gx, gy, gz);
       const size_t lin = (size_t)gx + (size_t)n * ((size_t)gy + (size_t)n * gz);
       if (mass) mass[lin] = g.w;
       if (mom) {
@@ -1206,8 +1198,8 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   };
   // The grid first: its placement then does not depend on N or on the other
   // arrays (shifting it by tens of MB measurably changed the grid update).
-  float4 *gA = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
-  float4 *gV = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  float4 *gA0 = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  float4 *gA1 = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
   PBuf bufs[2];
   for (int k = 0; k < 2; ++k) {
     bufs[k].x = (float *)take(sizeof(float) * 3 * Np);
@@ -1223,7 +1215,8 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
   uint32_t *tiles = (uint32_t *)take(sizeof(uint32_t) * 2 * ntiles);
-  uint32_t *aflag = (uint32_t *)take(sizeof(uint32_t) * nblk);
+  uint32_t *aflag0 = (uint32_t *)take(sizeof(uint32_t) * nblk);
+  uint32_t *aflag1 = (uint32_t *)take(sizeof(uint32_t) * nblk);
   uint4 *chunks = (uint4 *)take(sizeof(uint4) * max_chunks);
   uint32_t *ctr = (uint32_t *)take(sizeof(uint32_t) * CTR_WORDS);
   uint32_t *status = (uint32_t *)take(sizeof(uint32_t) * MPM_STATUS_WORDS);
@@ -1265,17 +1258,18 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->bin_cursor = cur;
     d->tile_sum = tiles;
     d->ntiles = (int32_t)ntiles;
-    d->active_flag = aflag;
+    d->active_flag[0] = aflag0;
+    d->active_flag[1] = aflag1;
     d->chunks = chunks;
     d->ctr = ctr;
     d->status = status;
-    d->gridA = gA;
-    d->gridV = gV;
+    d->gridA[0] = gA0;
+    d->gridA[1] = gA1;
   }
   return off;
 }
 
-const char *const KERNEL_NAMES[NUM_KERNELS] = {"k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g", "k_grid_update",
+const char *const KERNEL_NAMES[NUM_KERNELS] = {"k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g",
                                                "k_g2p"};
 
 }  // namespace
@@ -1291,7 +1285,8 @@ struct mpm_sim {
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_p2g = 0;
   int grid_g2p = 0;
-  int grid_update = 0;
+  int grid_scatter = 0;  // particles / WG, and at least 8 per CU (it also clears the grid)
+  int grid_blocks = 0;   // node-block loops (grid readback)
 };
 
 namespace {
@@ -1311,7 +1306,7 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
       k_scan_bins<<<d.ntiles, WG, 0, st>>>(d);
       break;
     case 2:
-      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
+      k_scatter<<<sim->grid_scatter, WG, 0, st>>>(d, src);
       break;
     case 3:
       if (d.material == MPM_J_FLUID) {
@@ -1323,9 +1318,6 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
       }
       break;
     case 4:
-      k_grid_update<<<sim->grid_update, WG, 0, st>>>(d);
-      break;
-    case 5:
       if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src);
       else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_g2p, 64, 0, st>>>(d, src);
       break;
@@ -1430,7 +1422,8 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     // 24 per CU, which 74 VGPRs would allow, was slower.
     occ_g = occ_g < 20 ? occ_g : 20;
     sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
-    sim->grid_update = cus * 8;
+    sim->grid_blocks = cus * 8;
+    sim->grid_scatter = std::max(sim->grid_particles, cus * 8);
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
 
     // Clear counters, flags, status and the P2G accumulator, then upload.
@@ -1438,18 +1431,19 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     k_zero_u32<<<1, WG, 0, st>>>(d.status, MPM_STATUS_WORDS);
     const int zb = (int)std::min<int64_t>(((int64_t)d.nbins + WG - 1) / WG, 4096);
     k_zero_u32<<<zb, WG, 0, st>>>(d.bin_count, (size_t)d.nbins);
-    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag, (size_t)d.nblk);
+    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[0], (size_t)d.nblk);
+    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[1], (size_t)d.nblk);
     const int gb = (int)std::min<int64_t>(((int64_t)d.nblk * 512 * 4 + WG - 1) / WG, 16384);
-    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA), (size_t)d.nblk * 512 * 4);
+    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[0]), (size_t)d.nblk * 512 * 4);
     // G2P may read a stencil node whose weight is exactly zero and that no
     // particle marked active; it must hold a finite value, so start at zero.
-    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridV), (size_t)d.nblk * 512 * 4);
+    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[1]), (size_t)d.nblk * 512 * 4);
     if (d.N > 0) {
       k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
       // one bucket pass to bring the initial state into bin order (buffer 1)
       k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
       k_scan_bins<<<d.ntiles, WG, 0, st>>>(d);
-      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
+      k_scatter<<<sim->grid_scatter, WG, 0, st>>>(d, 0);  // (no marks yet: clears nothing)
       k_permute_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d);
       sim->cur = 1;
     }
@@ -1528,7 +1522,8 @@ int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream) {
   const int zb = (int)std::min<size_t>((nn * 3 + WG - 1) / WG, 16384);
   if (mass) k_zero_f32<<<zb, WG, 0, st>>>(mass, nn);
   if (momentum) k_zero_f32<<<zb, WG, 0, st>>>(momentum, 3 * nn);
-  if (sim->d.N > 0 && sim->steps > 0) k_read_grid<<<sim->grid_update, WG, 0, st>>>(sim->d, mass, momentum);
+  // the last step read buffer cur ^ 1 and used grid parity cur ^ 1
+  if (sim->d.N > 0 && sim->steps > 0) k_read_grid<<<sim->grid_blocks, WG, 0, st>>>(sim->d, sim->cur ^ 1, mass, momentum);
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 

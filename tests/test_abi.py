@@ -109,9 +109,9 @@ def test_error_strings_and_kernel_names():
         assert mpm.mpm_error_string(code) != "unknown error"
     assert mpm.mpm_error_string(-99) == "unknown error"
     nk = mpm.mpm_num_kernels()
-    assert nk == 6
+    assert nk == 5
     names = [mpm.mpm_kernel_name(k) for k in range(nk)]
-    assert names == ["k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g", "k_grid_update", "k_g2p"]
+    assert names == ["k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g", "k_g2p"]
     assert mpm.mpm_kernel_name(nk) is None and mpm.mpm_kernel_name(-1) is None
 
 
