@@ -431,6 +431,8 @@ __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t *wsum, 
 
 constexpr int SCAN_PER = 8;                  // bins per thread
 constexpr int SCAN_TILE = WG * SCAN_PER;     // bins per scan tile
+constexpr int SCAN_SMALL_NT = 1024;          // grids of at most this many x SCAN_PER bins
+                                             // scan in one workgroup, without k_scan_tiles
 
 // Scan, phase 1: per-tile totals of particle counts and chunk counts.
 __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
@@ -456,44 +458,79 @@ __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
 // Scan, phase 2: each tile adds the totals of the tiles before it, scans its
 // bins and writes the bin cursors for k_scatter, the chunk list for k_p2g, and
 // zeroes the counts for k_g2p; the last tile publishes the chunk total.
-__global__ __launch_bounds__(WG) void k_scan_bins(SimDev s) {
-  __shared__ uint32_t wsum[WG / 64];
+// NT threads per workgroup, one tile of NT * SCAN_PER bins per workgroup.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_scan_bins(SimDev s) {
+  constexpr int TILE = NT * SCAN_PER;
+  __shared__ uint32_t wsum[NT / 64];
+  constexpr int LTAB = (NT == SCAN_SMALL_NT) ? TILE + 1 : 1;
+  __shared__ uint32_t cfirst[LTAB];  // tile-relative first chunk of each bin (+ the tile's total)
+  __shared__ uint32_t pfirst[LTAB];  // tile-relative first slot of each bin (+ the tile's total)
   const uint32_t nbins = (uint32_t)s.nbins;
   const uint32_t t = blockIdx.x;
+  const uint32_t shift = (uint32_t)s.chunk_shift;
   uint32_t pc = 0, pch = 0;
-  for (uint32_t k = threadIdx.x; k < t; k += WG) {
+  for (uint32_t k = threadIdx.x; k < t; k += NT) {
     pc += s.tile_sum[2 * k];
     pch += s.tile_sum[2 * k + 1];
   }
   uint32_t tile_base_c, tile_base_ch;
-  block_scan_incl<WG>(pc, wsum, &tile_base_c);
-  block_scan_incl<WG>(pch, wsum, &tile_base_ch);
-  const uint32_t b0 = t * SCAN_TILE + threadIdx.x * SCAN_PER;
+  block_scan_incl<NT>(pc, wsum, &tile_base_c);
+  block_scan_incl<NT>(pch, wsum, &tile_base_ch);
+  const uint32_t lb0 = threadIdx.x * SCAN_PER, b0 = t * TILE + lb0;
   uint32_t c[SCAN_PER], ch[SCAN_PER], csum = 0, chsum = 0;
 #pragma unroll
   for (int k = 0; k < SCAN_PER; ++k) {
     c[k] = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
-    ch[k] = (c[k] + (1u << s.chunk_shift) - 1u) >> s.chunk_shift;
+    ch[k] = (c[k] + (1u << shift) - 1u) >> shift;
     csum += c[k];
     chsum += ch[k];
   }
   uint32_t tc, tch;
-  const uint32_t ic = block_scan_incl<WG>(csum, wsum, &tc);
-  const uint32_t ich = block_scan_incl<WG>(chsum, wsum, &tch);
-  uint32_t run = tile_base_c + ic - csum, chrun = tile_base_ch + ich - chsum;
+  const uint32_t ic = block_scan_incl<NT>(csum, wsum, &tc);
+  const uint32_t ich = block_scan_incl<NT>(chsum, wsum, &tch);
+  uint32_t run = ic - csum, chrun = ich - chsum;  // tile-relative
+  // Many-tile grids are sparse per bin (a chunk or two): each thread writes
+  // its bins' chunk records.  The one-workgroup path (small, often dense
+  // scenes, many chunks per bin) spreads the records over all threads.
+  constexpr bool spread = NT == SCAN_SMALL_NT;
 #pragma unroll
   for (int k = 0; k < SCAN_PER; ++k) {
     const uint32_t b = b0 + k;
+    if (spread) {
+      cfirst[lb0 + k] = chrun;
+      pfirst[lb0 + k] = run;
+    }
     if (b < nbins) {
-      s.bin_cursor[b] = run;
-      for (uint32_t j = 0; j < ch[k]; ++j) {
-        const uint32_t off = j << s.chunk_shift;
-        s.chunks[chrun + j] = make_uint4(run + off, min(1u << s.chunk_shift, c[k] - off), b, 0u);
-      }
+      s.bin_cursor[b] = tile_base_c + run;
       s.bin_count[b] = 0u;
+      if (!spread)
+        for (uint32_t j = 0; j < ch[k]; ++j) {
+          const uint32_t off = j << shift;
+          s.chunks[tile_base_ch + chrun + j] = make_uint4(tile_base_c + run + off, min(1u << shift, c[k] - off), b, 0u);
+        }
     }
     run += c[k];
     chrun += ch[k];
+  }
+  if (spread && threadIdx.x == 0) {
+    cfirst[TILE] = tch;
+    pfirst[TILE] = tc;
+  }
+  __syncthreads();
+  // (spread) chunk c belongs to the last bin whose first chunk is <= c
+  // (binary search in LDS)
+  for (uint32_t cc = threadIdx.x; spread && cc < tch; cc += NT) {
+    uint32_t lo = 0, hi = TILE - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1u) >> 1;
+      if (cfirst[mid] <= cc) lo = mid;
+      else hi = mid - 1u;
+    }
+    const uint32_t off = (cc - cfirst[lo]) << shift;
+    const uint32_t pcount = pfirst[lo + 1] - pfirst[lo];
+    s.chunks[tile_base_ch + cc] =
+        make_uint4(tile_base_c + pfirst[lo] + off, min(1u << shift, pcount - off), t * TILE + lo, 0u);
   }
   if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS] = tile_base_ch + tch;
 }
@@ -1300,10 +1337,12 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
   const SimDev &d = sim->d;
   switch (k) {
     case 0:
-      k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
+      // (a small grid's bins are scanned by one workgroup, without tile totals)
+      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
       break;
     case 1:
-      k_scan_bins<<<d.ntiles, WG, 0, st>>>(d);
+      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_bins<WG><<<d.ntiles, WG, 0, st>>>(d);
+      else k_scan_bins<SCAN_SMALL_NT><<<1, SCAN_SMALL_NT, 0, st>>>(d);
       break;
     case 2:
       k_scatter<<<sim->grid_scatter, WG, 0, st>>>(d, src);
@@ -1441,8 +1480,8 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     if (d.N > 0) {
       k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
       // one bucket pass to bring the initial state into bin order (buffer 1)
-      k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
-      k_scan_bins<<<d.ntiles, WG, 0, st>>>(d);
+      launch_kernel(sim, 0, st, 0);
+      launch_kernel(sim, 1, st, 0);
       k_scatter<<<sim->grid_scatter, WG, 0, st>>>(d, 0);  // (no marks yet: clears nothing)
       k_permute_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d);
       sim->cur = 1;

@@ -188,7 +188,9 @@ def test_profiled_steps_match_graph_steps():
         a.step(3)
         ms = mpm.mpm_step_profiled(b.handle, 3, b.stream)
         assert set(ms) == {"k_scan_tiles", "k_scan_bins", "k_scatter", "k_p2g", "k_g2p"}
-        assert all(v > 0 for v in ms.values())
+        # (a grid whose bins fit one scan tile skips k_scan_tiles: about 0 ms)
+        assert all(v >= 0 for v in ms.values())
+        assert all(ms[k] > 0 for k in ("k_scan_bins", "k_scatter", "k_p2g", "k_g2p"))
         assert mpm.mpm_steps_taken(a.handle) == mpm.mpm_steps_taken(b.handle) == 3
         xa, va, Ca, Fa = a.read_particles()
         xb, vb, Cb, Fb = b.read_particles()
