@@ -972,9 +972,12 @@ __device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int
   float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
   const bool in_wall = gx < wall || gy < wall || gz < wall || gx >= n - wall || gy >= n - wall || gz >= n - wall;
   if (acc.x > 0.f && !in_wall) {
-    o.x = acc.y / acc.x + s.dt * s.g[0];
-    o.y = acc.z / acc.x + s.dt * s.g[1];
-    o.z = acc.w / acc.x + s.dt * s.g[2];
+    // one division per node (G2P evaluates each node once per window that
+    // covers it): p (1/m) is within an ulp of p/m
+    const float inv = 1.f / acc.x;
+    o.x = acc.y * inv + s.dt * s.g[0];
+    o.y = acc.z * inv + s.dt * s.g[1];
+    o.z = acc.w * inv + s.dt * s.g[2];
   }
   return o;
 }
