@@ -12,8 +12,7 @@
 //                 chunk list (<= KMAX particles of one bin per chunk)
 //   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), wave-
 //                 aggregated atomic cursors -> perm[slot] = source index, and
-//                 the particle's cell within its bin at the same position;
-//                 also clears the previous step's grid accumulator
+//                 the particle's cell within its bin at the same position
 //   k_p2g         one wavefront per chunk: in-LDS counting sort by cell (second
 //                 radix digit, 64 cells = 64 lanes), deferred F update, polar
 //                 decomposition, Kirchhoff stress, APIC momentum, conflict-free
@@ -100,7 +99,7 @@ struct SimDev {
   // Grid, double-buffered by step parity (the particle buffer the step reads):
   // the step with parity q accumulates into gridA[q] and marks the node-blocks
   // it touched in active_flag[q]; its G2P reads gridA[q]; the next step's
-  // scatter clears them (and their flags) while it accumulates into the other.
+  // P2G clears them (and their flags) while it accumulates into the other.
   uint32_t *active_flag[2];  // per node-block: 1 = touched by that step's P2G
   float4 *gridA[2];          // P2G accumulator per node: (m, p_x, p_y, p_z)
   uint32_t *ctr;
@@ -537,7 +536,7 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s) {
 
 // Bucket scatter: particle i of the current order goes to the next free slot
 // of its block.  One atomic per distinct block per wavefront.
-__global__ __launch_bounds__(WG) void k_scatter(SimDev s, int src) {
+__global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
   const uint32_t kc = valid ? s.key[i] : 0u;
@@ -546,16 +545,6 @@ __global__ __launch_bounds__(WG) void k_scatter(SimDev s, int src) {
   if (valid && slot < (uint32_t)s.N) {
     s.perm[slot] = i;
     s.cellp[slot] = (uint8_t)(kc >> KEY_CELL_SHIFT);
-  }
-  // Clear the previous step's accumulator: the node-blocks it marked (the
-  // other parity), and their marks.  Its G2P has finished reading them.
-  const int prev = src ^ 1;
-  for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
-    if (s.active_flag[prev][blk] == 0u) continue;  // the same word for the whole workgroup
-    float4 *g = s.gridA[prev] + ((size_t)blk << 9);
-    for (int k = threadIdx.x; k < 512; k += WG) g[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();  // every thread has read the mark before it is reset
-    if (threadIdx.x == 0) s.active_flag[prev][blk] = 0u;
   }
 }
 
@@ -623,6 +612,20 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       }
     }
   };
+  // Clear the previous step's accumulator (the other parity): the
+  // node-blocks it marked, and their marks; its G2P has finished reading
+  // them, and the next step accumulates there.  Workgroup b takes blocks
+  // b, b + grid, ...; the stores drain while it works on its chunks.
+  {
+    const int prev = src ^ 1;
+    for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+      if (s.active_flag[prev][blk] == 0u) continue;
+      float4 *g = s.gridA[prev] + ((size_t)blk << 9);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k * 64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (lane == 0) s.active_flag[prev][blk] = 0u;
+    }
+  }
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
   if (qbeg + wq < qend) {
     ch_next = s.chunks[qbeg + wq];
@@ -949,7 +952,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       }
     }
     // Mark the (at most 2x2x2) node-blocks the window overlaps: the next
-    // step's scatter clears exactly these (and mpm_read_grid reads them).  A
+    // step's P2G clears exactly these (and mpm_read_grid reads them).  A
     // marked block whose nodes got no mass is cleared for nothing, which is
     // harmless.  Plain stores: every writer stores the same value.
     if (lane < 8) {
@@ -965,7 +968,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
 
 // The grid update (a4) -- v = p/m + dt g where m > 0, sticky walls -- is
 // evaluated by G2P on its window nodes as it loads them (grid_velocity), and
-// the accumulator is cleared by the next step's scatter, so the step needs no
+// the accumulator is cleared by the next step's P2G, so the step needs no
 // separate pass over the grid.
 __device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int gx, int gy, int gz) {
   const int n = s.n, wall = s.wall;
@@ -1325,7 +1328,6 @@ struct mpm_sim {
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_p2g = 0;
   int grid_g2p = 0;
-  int grid_scatter = 0;  // particles / WG, and at least 8 per CU (it also clears the grid)
   int grid_blocks = 0;   // node-block loops (grid readback)
 };
 
@@ -1348,7 +1350,7 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
       else k_scan_bins<SCAN_SMALL_NT><<<1, SCAN_SMALL_NT, 0, st>>>(d);
       break;
     case 2:
-      k_scatter<<<sim->grid_scatter, WG, 0, st>>>(d, src);
+      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
       break;
     case 3:
       if (d.material == MPM_J_FLUID) {
@@ -1465,7 +1467,6 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     occ_g = occ_g < 20 ? occ_g : 20;
     sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
     sim->grid_blocks = cus * 8;
-    sim->grid_scatter = std::max(sim->grid_particles, cus * 8);
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
 
     // Clear counters, flags, status and the P2G accumulator, then upload.
@@ -1485,7 +1486,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
       // one bucket pass to bring the initial state into bin order (buffer 1)
       launch_kernel(sim, 0, st, 0);
       launch_kernel(sim, 1, st, 0);
-      k_scatter<<<sim->grid_scatter, WG, 0, st>>>(d, 0);  // (no marks yet: clears nothing)
+      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
       k_permute_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d);
       sim->cur = 1;
     }
