@@ -45,12 +45,12 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
         # bin counts read twice, cursors written, counts zeroed
         "k_scan_tiles": 4 * nbins,
         "k_scan_bins": 12 * nbins,
-        # reads the key word, writes perm and the cell byte; clears the
-        # previous step's accumulator (one float4 per active node)
-        "k_scatter": 9 * N + 16 * active_nodes,
+        # reads the key word, writes perm and the cell byte
+        "k_scatter": 9 * N,
         # reads perm, cell byte, x, v, C, F(, E), id; writes F(, E), x, id in
-        # the new order; accumulator write per active node
-        "k_p2g": N * (4 + 1 + 12 + 12 + 36 + f + e + 4 + f + e + 12 + 4) + 16 * active_nodes,
+        # the new order; accumulator write per active node, and the clear of
+        # the previous step's accumulator (one float4 per active node)
+        "k_p2g": N * (4 + 1 + 12 + 12 + 36 + f + e + 4 + f + e + 12 + 4) + 32 * active_nodes,
         # reads x; writes x, v, C, key; reads the accumulator (m, p) once per
         # active node and applies the grid update to it
         "k_g2p": N * (12 + 12 + 12 + 36 + 4) + 16 * active_nodes,
