@@ -752,7 +752,6 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       const uint32_t at = min(pos, count - 1u);
       const uint32_t i = order[at];
       const uint32_t tag = ordtag[at];
-      const uint32_t mysr = tag / NWIN;
       // The new state is stored in this processing order, (bin, super-rank,
       // window, cell): the next step's gathers then run over nearly
       // consecutive addresses.  P2G writes x and id there; G2P reads x from
@@ -854,13 +853,28 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
                 lz = min(max(b[2] - oz0, 0), CB - 1);
       const int li0 = (int)(tag % NWIN) * PW3 + (lz * PW + ly) * PW + lx;
 
-      // One pass per distinct super-rank present in this round.
+      // Passes: lanes conflict only when they share (window, cell).  The
+      // lane's pass is its occurrence index among the earlier lanes of the
+      // round with the same (window, cell) (ballot-matched, 7 bits), which
+      // gives the fewest conflict-free passes; lanes of one super-rank never
+      // share (window, cell), so this is at most one pass per super-rank.
+      uint32_t pass_id;
+      {
+        const uint32_t wc = (tag % NWIN) * (uint32_t)CB3 + (uint32_t)((lz * CB + ly) * CB + lx);
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int k = 0; k < 7; ++k) {
+          const uint64_t bk = __ballot((wc >> k) & 1u);
+          peers &= ((wc >> k) & 1u) ? bk : ~bk;
+        }
+        pass_id = (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
+      }
       bool todo = valid;
-      for (;;) {
-        const uint64_t tm = __ballot(todo);
-        if (tm == 0ull) break;
-        const uint32_t rnow = (uint32_t)__builtin_amdgcn_readlane((int)mysr, __ffsll((unsigned long long)tm) - 1);
-        if (todo && mysr == rnow) {
+      for (uint32_t pnow = 0;; ++pnow) {
+        // (occurrence indices of a key are 0, 1, ..., so no lane waits for a
+        // pass after an empty one)
+        if (__ballot(todo && pass_id == pnow) == 0ull) break;
+        if (todo && pass_id == pnow) {
           // Form the 27 node contributions here rather than keeping all 108 of
           // them live across the pass loop (register pressure limits occupancy).
 #pragma unroll
