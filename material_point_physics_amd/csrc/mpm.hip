@@ -10,9 +10,12 @@
 // Step = 5 kernels, captured once into a HIP graph per buffer parity:
 //   k_scan_*      two-phase exclusive scan of per-bin counts -> bin starts,
 //                 chunk list (<= KMAX particles of one bin per chunk)
-//   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), wave-
-//                 aggregated atomic cursors -> perm[slot] = source index, and
-//                 the particle's cell within its bin at the same position
+//   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), one
+//                 wavefront per chunk of the previous layout: particles that
+//                 stay in their bin keep their order (ballot prefix counts),
+//                 the few that change bin take wave-aggregated atomic cursors
+//                 -> perm[slot] = source index, and the particle's cell
+//                 within its bin at the same position
 //   k_p2g         one wavefront per chunk: in-LDS counting sort by cell (second
 //                 radix digit, 64 cells = 64 lanes), deferred F update, polar
 //                 decomposition, Kirchhoff stress, APIC momentum, conflict-free
@@ -61,7 +64,7 @@ constexpr int NQ = 8;            // P2G work queues, one per XCD
 constexpr int NUM_KERNELS = 5;
 
 enum Ctr : int {
-  CTR_NCHUNKS = 0,
+  CTR_NCHUNKS = 0,  // + layout parity: chunks of each layout
   CTR_PENDING = 2,
   CTR_WORDS = 16,
 };
@@ -92,10 +95,16 @@ struct SimDev {
   PBuf buf[2];
   uint32_t *perm, *key;         // key = bin | cell << KEY_CELL_SHIFT (cell of the base node in its bin)
   uint8_t *cellp;              // cell of the base node in its bin, in perm (sorted) order
-  uint32_t *bin_count, *bin_cursor;
+  uint32_t *bin_count;         // particles per bin in the next layout (G2P counts)
+  uint32_t *stay_count;        // of those, particles already in that bin (G2P counts)
+  uint32_t *bin_start, *bin_cursor;  // first slot of each bin; next slot for particles entering it
   uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
   int32_t ntiles;
-  uint4 *chunks;
+  // Chunk lists, one per layout (particle buffer) q: chunks[q][c] = (first
+  // slot, count, bin, particles that stay in the bin at the next sort);
+  // ctr[CTR_NCHUNKS + q] chunks.  The step that reads buffer q builds
+  // layout q ^ 1; its scatter walks layout q.
+  uint4 *chunks[2];
   // Grid, double-buffered by step parity (the particle buffer the step reads):
   // the step with parity q accumulates into gridA[q] and marks the node-blocks
   // it touched in active_flag[q]; its G2P reads gridA[q]; the next step's
@@ -109,6 +118,15 @@ struct SimDev {
 // ------------------------------------------------------------ device utils
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Element of a particle field at a 32-bit byte offset from a uniform base
+// (a component's first element).  All fields of one particle share the
+// offset register, and each access takes the scalar-base global form: no
+// per-access 64-bit address arithmetic.  Offsets are below 2^30 (N < 2^28).
+template <typename T>
+__device__ __forceinline__ T &at_byte(T *base, uint32_t off) {
+  return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
+}
 
 // Node-blocked grid index: blocks of 8^3 nodes (x fastest across blocks);
 // inside a block, 4^3 cubes of 2x2x2 nodes (x fastest), and inside a cube
@@ -392,7 +410,10 @@ __global__ __launch_bounds__(WG) void k_permute_init(SimDev s) {
     key = bin_key(s, base[0], base[1], base[2]);
     s.key[slot] = key | (cell_in_bin(base[0], base[1], base[2]) << KEY_CELL_SHIFT);
   }
+  // every particle stays in its bin here: the chunk records already count
+  // them all as stayers
   wave_aggregated_increment(s.bin_count, key, valid);
+  wave_aggregated_increment(s.stay_count, key, valid);
 }
 
 // Zero a uint32 range (fill kernel; graphs avoid memset nodes).
@@ -455,11 +476,14 @@ __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
 }
 
 // Scan, phase 2: each tile adds the totals of the tiles before it, scans its
-// bins and writes the bin cursors for k_scatter, the chunk list for k_p2g, and
-// zeroes the counts for k_g2p; the last tile publishes the chunk total.
-// NT threads per workgroup, one tile of NT * SCAN_PER bins per workgroup.
+// bins and writes the bin starts and cursors for k_scatter, the chunk list of
+// layout lay for k_p2g, and zeroes the counts for k_g2p; the last tile
+// publishes the chunk total.  A bin's particles that stay in it are placed
+// first (in their previous order), so the cursor for the others starts after
+// them.  NT threads per workgroup, one tile of NT * SCAN_PER bins per
+// workgroup.
 template <int NT>
-__global__ __launch_bounds__(NT) void k_scan_bins(SimDev s) {
+__global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
   constexpr int TILE = NT * SCAN_PER;
   __shared__ uint32_t wsum[NT / 64];
   constexpr int LTAB = (NT == SCAN_SMALL_NT) ? TILE + 1 : 1;
@@ -501,12 +525,17 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s) {
       pfirst[lb0 + k] = run;
     }
     if (b < nbins) {
-      s.bin_cursor[b] = tile_base_c + run;
       s.bin_count[b] = 0u;
+      if (c[k] > 0u) {  // (stay_count <= bin_count: both are zero otherwise)
+        const uint32_t stay = min(s.stay_count[b], c[k]);
+        s.stay_count[b] = 0u;
+        s.bin_start[b] = tile_base_c + run;
+        s.bin_cursor[b] = tile_base_c + run + stay;
+      }
       if (!spread)
         for (uint32_t j = 0; j < ch[k]; ++j) {
-          const uint32_t off = j << shift;
-          s.chunks[tile_base_ch + chrun + j] = make_uint4(tile_base_c + run + off, min(1u << shift, c[k] - off), b, 0u);
+          const uint32_t off = j << shift, cnt = min(1u << shift, c[k] - off);
+          s.chunks[lay][tile_base_ch + chrun + j] = make_uint4(tile_base_c + run + off, cnt, b, cnt);
         }
     }
     run += c[k];
@@ -527,16 +556,16 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s) {
       else hi = mid - 1u;
     }
     const uint32_t off = (cc - cfirst[lo]) << shift;
-    const uint32_t pcount = pfirst[lo + 1] - pfirst[lo];
-    s.chunks[tile_base_ch + cc] =
-        make_uint4(tile_base_c + pfirst[lo] + off, min(1u << shift, pcount - off), t * TILE + lo, 0u);
+    const uint32_t pcount = pfirst[lo + 1] - pfirst[lo], cnt = min(1u << shift, pcount - off);
+    s.chunks[lay][tile_base_ch + cc] = make_uint4(tile_base_c + pfirst[lo] + off, cnt, t * TILE + lo, cnt);
   }
-  if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS] = tile_base_ch + tch;
+  if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS + lay] = tile_base_ch + tch;
 }
 
-// Bucket scatter: particle i of the current order goes to the next free slot
-// of its block.  One atomic per distinct block per wavefront.
-__global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
+// Bucket scatter at creation: particle i of the creation order goes to the
+// next free slot of its bin (one atomic per distinct bin per wavefront; the
+// order within a bin is the order the atomics happen to run in).
+__global__ __launch_bounds__(WG) void k_scatter_init(SimDev s) {
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
   const uint32_t kc = valid ? s.key[i] : 0u;
@@ -545,6 +574,80 @@ __global__ __launch_bounds__(WG) void k_scatter(SimDev s) {
   if (valid && slot < (uint32_t)s.N) {
     s.perm[slot] = i;
     s.cellp[slot] = (uint8_t)(kc >> KEY_CELL_SHIFT);
+  }
+}
+
+// Bucket scatter of a step that reads buffer (layout) src.  Persistent
+// single-wavefront workgroups walk the chunks of layout src.  A particle that
+// stays in its chunk's bin goes to bin_start + (stayers of the bin's earlier
+// chunks, recorded by G2P) + (stayers before it in the chunk): the bin's
+// stayers keep their previous order, so P2G's processing order, and with it
+// the storage order, repeats from step to step and its gathers read
+// consecutive addresses.  A particle that changes bin takes the bin's atomic
+// cursor, which starts after the bin's stayers.
+__global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
+  const int lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + src];
+  const uint4 *chunks = s.chunks[src];
+  // The record of the next chunk, and the bin of the chunk before it, are
+  // loaded one chunk ahead.
+  uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t prev_next = 0xFFFFFFFFu;
+  if (blockIdx.x < nch) {
+    ch_next = chunks[blockIdx.x];
+    if (blockIdx.x > 0) prev_next = chunks[blockIdx.x - 1].z;
+  }
+  for (uint32_t c = blockIdx.x; c < nch; c += gridDim.x) {
+    const uint4 ch = ch_next;
+    const uint32_t prev_bin = prev_next;
+    const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
+    if (c + gridDim.x < nch) {
+      ch_next = chunks[c + gridDim.x];
+      prev_next = chunks[c + gridDim.x - 1].z;
+    }
+    // all of the chunk's keys at once (lanes past the count read none)
+    uint32_t kc[KMAX / 64];
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      const uint32_t r = (uint32_t)(64 * j + lane);
+      kc[j] = r < count ? s.key[start + r] : 0u;
+    }
+    uint32_t base = s.bin_start[bin];
+    // stayers of the bin's earlier chunks (a bin's chunks are consecutive;
+    // nearly always none, or a few records)
+    for (uint32_t c0 = c; prev_bin == bin && c0 > 0;) {
+      const uint32_t lo = c0 > 64u ? c0 - 64u : 0u;
+      const uint32_t cj = lo + (uint32_t)lane;
+      uint4 r = make_uint4(0u, 0u, 0xFFFFFFFFu, 0u);
+      if (cj < c0) r = chunks[cj];
+      const bool same = cj < c0 && r.z == bin;
+      uint32_t add = same ? r.w : 0u;
+      for (int d = 32; d >= 1; d >>= 1) add += (uint32_t)__shfl_xor((int)add, d);
+      base += add;
+      // all 64 earlier records belong to the bin: keep walking back
+      if (__ballot(same) != ~0ull || lo == 0u) break;
+      c0 = lo;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) {
+      const uint32_t r = (uint32_t)(64 * j + lane);
+      if ((uint32_t)(64 * j) >= count) break;
+      const bool valid = r < count;
+      const uint32_t key = kc[j] & ((1u << KEY_CELL_SHIFT) - 1u);
+      const bool stay = valid && key == bin;
+      const uint64_t sm = __ballot(stay);
+      uint32_t slot = base + (uint32_t)__popcll(sm & below);
+      base += (uint32_t)__popcll(sm);
+      if (__ballot(valid && !stay) != 0ull) {
+        const uint32_t mslot = wave_aggregated_increment(s.bin_cursor, key, valid && !stay);
+        if (!stay) slot = mslot;
+      }
+      if (valid && slot < (uint32_t)s.N) {
+        s.perm[slot] = start + r;
+        s.cellp[slot] = (uint8_t)(kc[j] >> KEY_CELL_SHIFT);
+      }
+    }
   }
 }
 
@@ -590,7 +693,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   // XCD's contiguous (Morton-ordered, so spatially compact) share of the
   // chunk list.  Static assignment: no contended atomics on a work queue.
   const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
-  const uint32_t nch = s.ctr[CTR_NCHUNKS];
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + (src ^ 1)];
+  const uint4 *chunks = s.chunks[src ^ 1];  // the layout this step builds
   const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
   const bool pending = s.ctr[CTR_PENDING] != 0u;
   const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
@@ -628,7 +732,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   }
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
   if (qbeg + wq < qend) {
-    ch_next = s.chunks[qbeg + wq];
+    ch_next = chunks[qbeg + wq];
     prefetch(ch_next);
   }
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
@@ -636,7 +740,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;  // first base node of the bin = window origin
     const bool has_next = c + nwq < qend;
-    if (has_next) ch_next = s.chunks[c + nwq];
+    if (has_next) ch_next = chunks[c + nwq];
 
     // Pass A: cell of each particle and its rank within the cell.  Ranks
     // follow the particles' previous storage order (their source index), so
@@ -758,40 +862,41 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       // the same slot, without an index indirection, and overwrites it with
       // the advected position.
       const uint32_t dst = start + at;
+      const uint32_t io = 4u * i, od = 4u * dst;  // byte offsets of the source and destination slots
       float xp[3], vp[3], Cp[9];
 #pragma unroll
       for (int a = 0; a < 3; ++a) {
-        xp[a] = in.x[a * Np + i];
-        vp[a] = in.v[a * Np + i];
+        xp[a] = at_byte(in.x + a * Np, io);
+        vp[a] = at_byte(in.v + a * Np, io);
       }
 #pragma unroll
-      for (int k = 0; k < 9; ++k) Cp[k] = in.C[k * Np + i];
+      for (int k = 0; k < 9; ++k) Cp[k] = at_byte(in.C + k * Np, io);
       if (valid) {
 #pragma unroll
-        for (int a = 0; a < 3; ++a) out.x[a * Np + dst] = xp[a];
-        out.id[dst] = in.id[i];
+        for (int a = 0; a < 3; ++a) at_byte(out.x + a * Np, od) = xp[a];
+        at_byte(out.id, od) = at_byte(in.id, io);
       }
 
       float tau_diag = 0.f;
       float tau[9];
       if (MAT == MPM_J_FLUID) {
-        float J = in.F[i];
+        float J = at_byte(in.F, io);
         if (pending) {
           const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
                               dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
           J = J * det3(G);
         }
-        const float K = HAS_E ? in.E[i] : s.E;
+        const float K = HAS_E ? at_byte(in.E, io) : s.E;
         if (valid) {
-          out.F[dst] = J;
-          if (HAS_E) out.E[dst] = K;
+          at_byte(out.F, od) = J;
+          if (HAS_E) at_byte(out.E, od) = K;
           if (!(J > 0.f)) flag_status(s, MPM_STATUS_INVERTED, 2);
         }
         tau_diag = K * J * (J - 1.f);
       } else {
         float Fp[9];
 #pragma unroll
-        for (int k = 0; k < 9; ++k) Fp[k] = in.F[k * Np + i];
+        for (int k = 0; k < 9; ++k) Fp[k] = at_byte(in.F + k * Np, io);
         if (pending) {
           float Fn[9];
 #pragma unroll
@@ -803,11 +908,11 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
 #pragma unroll
           for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
         }
-        const float E = HAS_E ? in.E[i] : s.E;
+        const float E = HAS_E ? at_byte(in.E, io) : s.E;
         if (valid) {
 #pragma unroll
-          for (int k = 0; k < 9; ++k) out.F[k * Np + dst] = Fp[k];
-          if (HAS_E) out.E[dst] = E;
+          for (int k = 0; k < 9; ++k) at_byte(out.F + k * Np, od) = Fp[k];
+          if (HAS_E) at_byte(out.E, od) = E;
         }
         const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
         float R[9];
@@ -932,37 +1037,51 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     __syncthreads();
 
     // Flush: the windows' sum, one native global float atomic per nonzero
-    // value, in whole cubes: lane = (cube, node in cube, channel), so each
-    // atomic instruction covers two cubes = two full 128-byte lines (the
-    // memory-side atomic units work per line).
+    // value (adding zero changes nothing), in whole cubes: lane = (cube of
+    // the pair, node in cube, channel), so each atomic instruction covers two
+    // cubes = two full 128-byte lines (the memory-side atomic units work per
+    // line).  A window cube's node index is separable per axis; with the
+    // window origin a multiple of 4, the axis terms of cube coordinate 0..2
+    // are uniform (relative to the origin's node-block: at most one block
+    // step per axis), so a lane's address is a uniform block pointer plus the
+    // cube offset of its half of the wavefront plus its node and channel.
     {
-      // cube cb = 2t + lane / 32 at cube coordinates (cx, cy, cz), advanced
-      // by 2 cubes per step
-      const int j = (lane >> 2) & 7, chn = lane & 3;
-      int cb = lane >> 5, cx = cb, cy = 0, cz = 0;
-#pragma unroll 1
-      for (; cb < 27; cb += 2) {
-        const int wx = 2 * cx + (j & 1), wy = 2 * cy + ((j >> 1) & 1), wz = 2 * cz + (j >> 2);
-        const int k = (wz * PW + wy) * PW + wx;
-        const float *winf = reinterpret_cast<const float *>(sm.win) + 4 * k;
-        float mval = 0.f, val = 0.f;
+      const int h = lane >> 5, j = (lane >> 2) & 7, chn = lane & 3;
+      const int jx = j & 1, jy = (j >> 1) & 1, jz = j >> 2;
+      const uint32_t nbs = (uint32_t)s.nb;
+      uint32_t XC[3], YC[3], ZC[3];  // node offsets of cube coordinate 0..2 per axis
 #pragma unroll
-        for (int w = 0; w < NWIN; ++w) {
-          mval += winf[4 * w * PW3];
-          val += winf[4 * w * PW3 + chn];
+      for (int k = 0; k < 3; ++k) {
+        const uint32_t ux = (uint32_t)(ox0 >> 1) + (uint32_t)k, uy = (uint32_t)(oy0 >> 1) + (uint32_t)k,
+                       uz = (uint32_t)(oz0 >> 1) + (uint32_t)k;
+        XC[k] = (((ux >> 2) - (uint32_t)(ox0 >> 3)) << 9) + ((ux & 3u) << 3);
+        YC[k] = (((uy >> 2) - (uint32_t)(oy0 >> 3)) * nbs << 9) + ((uy & 3u) << 5);
+        ZC[k] = (((uz >> 2) - (uint32_t)(oz0 >> 3)) * nbs * nbs << 9) + ((uz & 3u) << 7);
+      }
+      float4 *gblk = s.gridA[src] +
+                     (((size_t)(oz0 >> 3) * nbs + (size_t)(oy0 >> 3)) * nbs + (size_t)(ox0 >> 3)) * 512u;
+      const uint32_t lane_b = (uint32_t)(16 * j + 4 * chn);
+      const float *winl = reinterpret_cast<const float *>(sm.win) + 4 * ((jz * PW + jy) * PW + jx) + chn;
+      // the window reaches past the grid only at the grid's upper faces
+      const bool interior = ox0 + PW <= s.n && oy0 + PW <= s.n && oz0 + PW <= s.n;
+#pragma unroll
+      for (int t = 0; t < 14; ++t) {
+        const int c0 = 2 * t, c1 = 2 * t + 1;  // the two cubes of this step
+        const int x0 = c0 % 3, y0 = (c0 / 3) % 3, z0 = c0 / 9;
+        const int x1 = c1 % 3, y1 = (c1 / 3) % 3, z1 = (c1 < 27) ? c1 / 9 : 0;
+        const uint32_t o0 = XC[x0] + YC[y0] + ZC[z0], o1 = XC[x1] + YC[y1] + ZC[z1];
+        const int kw0 = ((2 * z0) * PW + 2 * y0) * PW + 2 * x0, kw1 = ((2 * z1) * PW + 2 * y1) * PW + 2 * x1;
+        if (c1 >= 27 && h) continue;
+        const int kw = h ? kw1 : kw0;
+        float val = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWIN; ++w) val += winl[4 * (kw + w * PW3)];
+        bool inb = val != 0.f;
+        if (!interior) {
+          const int cx = h ? x1 : x0, cy = h ? y1 : y0, cz = h ? z1 : z0;
+          inb = inb && ox0 + 2 * cx + jx < s.n && oy0 + 2 * cy + jy < s.n && oz0 + 2 * cz + jz < s.n;
         }
-        const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-        if (mval != 0.f && gx < s.n && gy < s.n && gz < s.n)
-          unsafeAtomicAdd(reinterpret_cast<float *>(s.gridA[src] + node_index(s, gx, gy, gz)) + chn, val);
-        cx += 2;
-        if (cx >= 3) {
-          cx -= 3;
-          ++cy;
-        }
-        if (cy >= 3) {
-          cy -= 3;
-          ++cz;
-        }
+        if (inb) unsafeAtomicAdd(&at_byte(reinterpret_cast<float *>(gblk), 16u * (h ? o1 : o0) + lane_b), val);
       }
     }
     // Mark the (at most 2x2x2) node-blocks the window overlaps: the next
@@ -1013,10 +1132,11 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
   const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
   const float fn = s.fn;
   const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
-  const uint32_t nch = s.ctr[CTR_NCHUNKS];
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + (src ^ 1)];
+  uint4 *chunks = s.chunks[src ^ 1];
   const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
-    const uint4 ch = s.chunks[c];
+    const uint4 ch = chunks[c];
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
     // Window load in whole cubes (one 128-byte line each): lane = (cube,
@@ -1047,8 +1167,9 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
       }
     }
     __syncthreads();
+    uint32_t nstay = 0;
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
-      const uint32_t slot = start + r0 + (uint32_t)lane;
+      const uint32_t slot = start + r0 + (uint32_t)lane, so = 4u * slot;
       const bool valid = r0 + (uint32_t)lane < count;
       uint32_t key = 0;
       if (valid) {
@@ -1057,7 +1178,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
         float w[3][3], d[3][3];
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
-          xp[a] = out.x[a * Np + slot];  // written by this step's P2G in this order
+          xp[a] = at_byte(out.x + a * Np, so);  // written by this step's P2G in this order
           const float xn = xp[a] * fn;
           b[a] = base_node(xn);
           const float f = xn - (float)b[a];
@@ -1121,25 +1242,32 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
           if (!isfinite(xa) || !isfinite(v[a])) nonfinite = true;
           if (xa < s.lo || xa > s.hi) clamped = true;
           xa = fminf(fmaxf(xa, s.lo), s.hi);
-          out.x[a * Np + slot] = xa;
-          out.v[a * Np + slot] = v[a];
+          at_byte(out.x + a * Np, so) = xa;
+          at_byte(out.v + a * Np, so) = v[a];
           b[a] = base_node(xa * fn);
         }
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
           const float ck = s.c_scale * B[k];
           if (!isfinite(ck)) nonfinite = true;
-          out.C[k * Np + slot] = ck;
+          at_byte(out.C + k * Np, so) = ck;
         }
         // the next bin: nearly always the chunk's own (Morton encoding only
         // when some lane of the wavefront left it)
         const bool same_bin = (b[0] >> 2) == (ox0 >> 2) && (b[1] >> 2) == (oy0 >> 2) && (b[2] >> 2) == (oz0 >> 2);
         key = (__ballot(!same_bin) == 0ull) ? bin : bin_key(s, b[0], b[1], b[2]);
-        s.key[slot] = key | (cell_in_bin(b[0], b[1], b[2]) << KEY_CELL_SHIFT);
+        at_byte(s.key, so) = key | (cell_in_bin(b[0], b[1], b[2]) << KEY_CELL_SHIFT);
         if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
       wave_aggregated_increment(s.bin_count, key, valid);
+      nstay += (uint32_t)__popcll(__ballot(valid && key == bin));
+    }
+    // The chunk's particles that stay in its bin: the next scatter keeps them
+    // in this order, after the stayers of the bin's earlier chunks.
+    if (lane == 0) {
+      chunks[c].w = nstay;
+      if (nstay) atomicAdd(s.stay_count + bin, nstay);
     }
     __syncthreads();  // the window is reloaded for the next chunk
   }
@@ -1269,12 +1397,15 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   uint32_t *perm = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *key = (uint32_t *)take(sizeof(uint32_t) * Np);
   uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
+  uint32_t *stay = (uint32_t *)take(sizeof(uint32_t) * nbins);
+  uint32_t *bstart = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
   uint32_t *tiles = (uint32_t *)take(sizeof(uint32_t) * 2 * ntiles);
   uint32_t *aflag0 = (uint32_t *)take(sizeof(uint32_t) * nblk);
   uint32_t *aflag1 = (uint32_t *)take(sizeof(uint32_t) * nblk);
-  uint4 *chunks = (uint4 *)take(sizeof(uint4) * max_chunks);
+  uint4 *chunks0 = (uint4 *)take(sizeof(uint4) * max_chunks);
+  uint4 *chunks1 = (uint4 *)take(sizeof(uint4) * max_chunks);
   uint32_t *ctr = (uint32_t *)take(sizeof(uint32_t) * CTR_WORDS);
   uint32_t *status = (uint32_t *)take(sizeof(uint32_t) * MPM_STATUS_WORDS);
   uint8_t *cellp = (uint8_t *)take(Np);
@@ -1312,12 +1443,15 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->key = key;
     d->cellp = cellp;
     d->bin_count = cnt;
+    d->stay_count = stay;
+    d->bin_start = bstart;
     d->bin_cursor = cur;
     d->tile_sum = tiles;
     d->ntiles = (int32_t)ntiles;
     d->active_flag[0] = aflag0;
     d->active_flag[1] = aflag1;
-    d->chunks = chunks;
+    d->chunks[0] = chunks0;
+    d->chunks[1] = chunks1;
     d->ctr = ctr;
     d->status = status;
     d->gridA[0] = gA0;
@@ -1340,6 +1474,7 @@ struct mpm_sim {
   hipGraph_t graph[2] = {nullptr, nullptr};
   hipGraphExec_t exec[2] = {nullptr, nullptr};
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
+  int grid_scatter = 0;
   int grid_p2g = 0;
   int grid_g2p = 0;
   int grid_blocks = 0;   // node-block loops (grid readback)
@@ -1360,11 +1495,11 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
       if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
       break;
     case 1:
-      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_bins<WG><<<d.ntiles, WG, 0, st>>>(d);
-      else k_scan_bins<SCAN_SMALL_NT><<<1, SCAN_SMALL_NT, 0, st>>>(d);
+      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_bins<WG><<<d.ntiles, WG, 0, st>>>(d, src ^ 1);
+      else k_scan_bins<SCAN_SMALL_NT><<<1, SCAN_SMALL_NT, 0, st>>>(d, src ^ 1);
       break;
     case 2:
-      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
+      k_scatter<<<sim->grid_scatter, 64, 0, st>>>(d, src);
       break;
     case 3:
       if (d.material == MPM_J_FLUID) {
@@ -1481,6 +1616,9 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     occ_g = occ_g < 20 ? occ_g : 20;
     sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
     sim->grid_blocks = cus * 8;
+    // single-wavefront workgroups, 8 per SIMD: the scatter is a chain of
+    // short dependent loads per chunk, so it wants many chunks in flight
+    sim->grid_scatter = cus * 32;
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
 
     // Clear counters, flags, status and the P2G accumulator, then upload.
@@ -1488,6 +1626,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     k_zero_u32<<<1, WG, 0, st>>>(d.status, MPM_STATUS_WORDS);
     const int zb = (int)std::min<int64_t>(((int64_t)d.nbins + WG - 1) / WG, 4096);
     k_zero_u32<<<zb, WG, 0, st>>>(d.bin_count, (size_t)d.nbins);
+    k_zero_u32<<<zb, WG, 0, st>>>(d.stay_count, (size_t)d.nbins);
     k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[0], (size_t)d.nblk);
     k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[1], (size_t)d.nblk);
     const int gb = (int)std::min<int64_t>(((int64_t)d.nblk * 512 * 4 + WG - 1) / WG, 16384);
@@ -1497,10 +1636,11 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[1]), (size_t)d.nblk * 512 * 4);
     if (d.N > 0) {
       k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
-      // one bucket pass to bring the initial state into bin order (buffer 1)
+      // one bucket pass to bring the initial state into bin order (buffer 1,
+      // whose chunk list the scan writes)
       launch_kernel(sim, 0, st, 0);
       launch_kernel(sim, 1, st, 0);
-      k_scatter<<<sim->grid_particles, WG, 0, st>>>(d);
+      k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
       k_permute_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d);
       sim->cur = 1;
     }
