@@ -102,8 +102,12 @@ size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles);
  * page's problem statement: material points carried across a background
  * grid by explicit steps).
  *   params      : host, read during the call.
- *   n_particles : 0 <= n < 2^28 (element offsets inside the 9-component
- *                 per-particle fields are 32-bit).
+ *   n_particles : 0 <= n < 2^28, and the particle buffers' slot capacity
+ *                 n + 31 min(n, ceil(grid_n / 4)^3), rounded up to 64, below
+ *                 2^29 (each 4^3-cell bin's slots start on a 32-particle
+ *                 boundary; component offsets inside the 9-component fields
+ *                 are 32-bit).  Larger requests return MPM_ERR_INVALID_ARG
+ *                 (and mpm_workspace_bytes returns 0).
  *   x0          : device, (N,3) float32 row-major positions (required if N > 0).
  *   v0          : device, (N,3) velocities, or NULL for zero.
  *   C0          : device, (N,3,3) row-major APIC affine matrices, or NULL for zero.

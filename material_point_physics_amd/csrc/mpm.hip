@@ -42,6 +42,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -61,6 +62,11 @@ constexpr int KMAX_SHIFT = 8;
 constexpr int KMAX = 1 << KMAX_SHIFT;  // particles per P2G chunk at most (4 rounds of one wavefront)
 constexpr int KMIN_SHIFT = 6;    // smallest chunk size: 64 particles (see mpm_create)
 constexpr int NQ = 8;            // P2G work queues, one per XCD
+// Each bin's slot range starts at a multiple of SLOT_ALIGN particles, so a
+// particle field's 128-byte lines (32 fp32 values) never straddle two bins:
+// chunks and their 64-particle rounds read and write whole lines.  The
+// padding slots (holes) are never read: every kernel walks the chunk list.
+constexpr int SLOT_ALIGN = 32;
 constexpr int NUM_KERNELS = 5;
 
 enum Ctr : int {
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
   const PBuf b = s.buf[0];
-  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
+  const size_t Np = (size_t)s.Np;
   uint32_t key = 0;
   if (valid) {
     bool bad = false;
@@ -379,41 +385,8 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
     if (s.has_E) b.E[i] = E_p[i];
     b.id[i] = i;
     key = bin_key(s, base[0], base[1], base[2]);
-    s.key[i] = key | (cell_in_bin(base[0], base[1], base[2]) << KEY_CELL_SHIFT);
   }
   wave_aggregated_increment(s.bin_count, key, valid);
-}
-
-// Creation: move the initial state (buffer 0, creation order) into bin order
-// in buffer 1, so that the first step's gathers are as local as any later
-// step's; recomputes the keys and counts for that order.
-__global__ __launch_bounds__(WG) void k_permute_init(SimDev s) {
-  const uint32_t slot = blockIdx.x * WG + threadIdx.x;
-  const bool valid = slot < (uint32_t)s.N;
-  const PBuf a = s.buf[0], b = s.buf[1];
-  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
-  uint32_t key = 0;
-  if (valid) {
-    const uint32_t i = min(s.perm[slot], (uint32_t)s.N - 1u);
-    int base[3];
-    for (int c = 0; c < 3; ++c) {
-      const float xc = a.x[c * Np + i];
-      b.x[c * Np + slot] = xc;
-      b.v[c * Np + slot] = a.v[c * Np + i];
-      base[c] = base_node(xc * s.fn);
-    }
-    for (int k = 0; k < 9; ++k) b.C[k * Np + slot] = a.C[k * Np + i];
-    const int fw = s.material == MPM_J_FLUID ? 1 : 9;
-    for (int k = 0; k < fw; ++k) b.F[k * Np + slot] = a.F[k * Np + i];
-    if (s.has_E) b.E[slot] = a.E[i];
-    b.id[slot] = a.id[i];
-    key = bin_key(s, base[0], base[1], base[2]);
-    s.key[slot] = key | (cell_in_bin(base[0], base[1], base[2]) << KEY_CELL_SHIFT);
-  }
-  // every particle stays in its bin here: the chunk records already count
-  // them all as stayers
-  wave_aggregated_increment(s.bin_count, key, valid);
-  wave_aggregated_increment(s.stay_count, key, valid);
 }
 
 // Zero a uint32 range (fill kernel; graphs avoid memset nodes).
@@ -454,7 +427,12 @@ constexpr int SCAN_TILE = WG * SCAN_PER;     // bins per scan tile
 constexpr int SCAN_SMALL_NT = 1024;          // grids of at most this many x SCAN_PER bins
                                              // scan in one workgroup, without k_scan_tiles
 
-// Scan, phase 1: per-tile totals of particle counts and chunk counts.
+// A bin's slot range: its count rounded up to whole SLOT_ALIGN groups.
+__device__ __forceinline__ uint32_t padded(uint32_t count) {
+  return (count + (uint32_t)SLOT_ALIGN - 1u) & ~(uint32_t)(SLOT_ALIGN - 1);
+}
+
+// Scan, phase 1: per-tile totals of (padded) slot counts and chunk counts.
 __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
   __shared__ uint32_t wsum[WG / 64];
   const uint32_t nbins = (uint32_t)s.nbins;
@@ -463,7 +441,7 @@ __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
 #pragma unroll
   for (int k = 0; k < SCAN_PER; ++k) {
     const uint32_t cnt = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
-    c += cnt;
+    c += padded(cnt);
     ch += (cnt + (1u << s.chunk_shift) - 1u) >> s.chunk_shift;
   }
   uint32_t tc, tch;
@@ -506,13 +484,13 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
   for (int k = 0; k < SCAN_PER; ++k) {
     c[k] = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
     ch[k] = (c[k] + (1u << shift) - 1u) >> shift;
-    csum += c[k];
+    csum += padded(c[k]);
     chsum += ch[k];
   }
   uint32_t tc, tch;
   const uint32_t ic = block_scan_incl<NT>(csum, wsum, &tc);
   const uint32_t ich = block_scan_incl<NT>(chsum, wsum, &tch);
-  uint32_t run = ic - csum, chrun = ich - chsum;  // tile-relative
+  uint32_t run = ic - csum, chrun = ich - chsum;  // tile-relative, in slots (multiples of SLOT_ALIGN)
   // Many-tile grids are sparse per bin (a chunk or two): each thread writes
   // its bins' chunk records.  The one-workgroup path (small, often dense
   // scenes, many chunks per bin) spreads the records over all threads.
@@ -522,7 +500,7 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
     const uint32_t b = b0 + k;
     if (spread) {
       cfirst[lb0 + k] = chrun;
-      pfirst[lb0 + k] = run;
+      pfirst[lb0 + k] = run | (c[k] & (uint32_t)(SLOT_ALIGN - 1));  // (run is aligned: the low bits carry the count)
     }
     if (b < nbins) {
       s.bin_count[b] = 0u;
@@ -538,7 +516,7 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
           s.chunks[lay][tile_base_ch + chrun + j] = make_uint4(tile_base_c + run + off, cnt, b, cnt);
         }
     }
-    run += c[k];
+    run += padded(c[k]);
     chrun += ch[k];
   }
   if (spread && threadIdx.x == 0) {
@@ -555,26 +533,51 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
       if (cfirst[mid] <= cc) lo = mid;
       else hi = mid - 1u;
     }
-    const uint32_t off = (cc - cfirst[lo]) << shift;
-    const uint32_t pcount = pfirst[lo + 1] - pfirst[lo], cnt = min(1u << shift, pcount - off);
-    s.chunks[lay][tile_base_ch + cc] = make_uint4(tile_base_c + pfirst[lo] + off, cnt, t * TILE + lo, cnt);
+    const uint32_t off = (cc - cfirst[lo]) << shift, amask = (uint32_t)(SLOT_ALIGN - 1);
+    const uint32_t pstart = pfirst[lo] & ~amask, span = (pfirst[lo + 1] & ~amask) - pstart, rem = pfirst[lo] & amask;
+    const uint32_t pcount = rem ? span - (uint32_t)SLOT_ALIGN + rem : span;  // the bin's particle count
+    const uint32_t cnt = min(1u << shift, pcount - off);
+    s.chunks[lay][tile_base_ch + cc] = make_uint4(tile_base_c + pstart + off, cnt, t * TILE + lo, cnt);
   }
   if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS + lay] = tile_base_ch + tch;
 }
 
-// Bucket scatter at creation: particle i of the creation order goes to the
-// next free slot of its bin (one atomic per distinct bin per wavefront; the
-// order within a bin is the order the atomics happen to run in).
+// Creation: move the initial state (buffer 0, creation order) into bin order
+// in buffer 1 (layout 1, whose chunk list the scan wrote): particle i goes to
+// the next free slot of its bin (one atomic per distinct bin per wavefront;
+// the order within a bin is the order the atomics happen to run in).  Writes
+// the keys of the new order and counts every particle as a stayer of its bin
+// (the chunk records already say so), for the first step's scan.
 __global__ __launch_bounds__(WG) void k_scatter_init(SimDev s) {
   const uint32_t i = blockIdx.x * WG + threadIdx.x;
   const bool valid = i < (uint32_t)s.N;
-  const uint32_t kc = valid ? s.key[i] : 0u;
-  const uint32_t key = kc & ((1u << KEY_CELL_SHIFT) - 1u);
-  const uint32_t slot = wave_aggregated_increment(s.bin_cursor, key, valid);
-  if (valid && slot < (uint32_t)s.N) {
-    s.perm[slot] = i;
-    s.cellp[slot] = (uint8_t)(kc >> KEY_CELL_SHIFT);
+  const PBuf a = s.buf[0], b = s.buf[1];
+  const size_t Np = (size_t)s.Np;
+  int base[3] = {0, 0, 0};
+  float xi[3] = {0.f, 0.f, 0.f};
+  uint32_t key = 0;
+  if (valid) {
+    for (int c = 0; c < 3; ++c) {
+      xi[c] = a.x[c * Np + i];
+      base[c] = base_node(xi[c] * s.fn);
+    }
+    key = bin_key(s, base[0], base[1], base[2]);
   }
+  const uint32_t slot = wave_aggregated_increment(s.bin_cursor, key, valid);
+  if (valid && slot < (uint32_t)s.Np) {
+    for (int c = 0; c < 3; ++c) {
+      b.x[c * Np + slot] = xi[c];
+      b.v[c * Np + slot] = a.v[c * Np + i];
+    }
+    for (int k = 0; k < 9; ++k) b.C[k * Np + slot] = a.C[k * Np + i];
+    const int fw = s.material == MPM_J_FLUID ? 1 : 9;
+    for (int k = 0; k < fw; ++k) b.F[k * Np + slot] = a.F[k * Np + i];
+    if (s.has_E) b.E[slot] = a.E[i];
+    b.id[slot] = a.id[i];
+    s.key[slot] = key | (cell_in_bin(base[0], base[1], base[2]) << KEY_CELL_SHIFT);
+  }
+  wave_aggregated_increment(s.bin_count, key, valid);
+  wave_aggregated_increment(s.stay_count, key, valid);
 }
 
 // Bucket scatter of a step that reads buffer (layout) src.  Persistent
@@ -643,7 +646,7 @@ __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
         const uint32_t mslot = wave_aggregated_increment(s.bin_cursor, key, valid && !stay);
         if (!stay) slot = mslot;
       }
-      if (valid && slot < (uint32_t)s.N) {
+      if (valid && slot < (uint32_t)s.Np) {
         s.perm[slot] = start + r;
         s.cellp[slot] = (uint8_t)(kc[j] >> KEY_CELL_SHIFT);
       }
@@ -688,7 +691,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
 
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
-  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
   // Workgroup b runs on XCD b % 8 and takes every (grid/8)-th chunk of that
   // XCD's contiguous (Morton-ordered, so spatially compact) share of the
   // chunk list.  Static assignment: no contended atomics on a work queue.
@@ -711,7 +714,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       pf_src[j] = 0xFFFFFFFFu;
       pf_cell[j] = 0u;
       if (qi < pcount) {
-        pf_src[j] = min(s.perm[pstart + qi], (uint32_t)s.N - 1u);
+        pf_src[j] = min(s.perm[pstart + qi], Np - 1u);
         pf_cell[j] = (uint32_t)s.cellp[pstart + qi] & (uint32_t)(CB3 - 1);
       }
     }
@@ -1129,7 +1132,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
   __shared__ float4 win[PW3];
   const PBuf out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
-  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
   const float fn = s.fn;
   const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
   const uint32_t nch = s.ctr[CTR_NCHUNKS + (src ^ 1)];
@@ -1275,45 +1278,54 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
 }
 
 // Readback: unpermute to creation order, apply the pending F (or J) update.
+// Single-wavefront workgroups walk the chunk list of layout cur (the slots
+// between bins are padding).
 template <int MAT>
-__global__ __launch_bounds__(WG) void k_read_particles(SimDev s, int cur, float *__restrict__ x, float *__restrict__ v,
+__global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float *__restrict__ x, float *__restrict__ v,
                                                        float *__restrict__ C, float *__restrict__ F) {
-  const uint32_t slot = blockIdx.x * WG + threadIdx.x;
-  if (slot >= (uint32_t)s.N) return;
   const PBuf b = s.buf[cur];
-  const uint32_t Np = (uint32_t)s.Np;  // 9 Np < 2^32: element offsets are exact in 32 bits
-  const size_t id = b.id[slot];
-  if (id >= (size_t)s.N) return;
+  const size_t Np = (size_t)s.Np;
   const bool pending = s.ctr[CTR_PENDING] != 0u;
-  float Cp[9];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) Cp[k] = b.C[k * Np + slot];
-  for (int a = 0; a < 3; ++a) {
-    if (x) x[3 * id + a] = b.x[a * Np + slot];
-    if (v) v[3 * id + a] = b.v[a * Np + slot];
-  }
-  if (C)
-    for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
-  if (!F) return;
   const float dt = s.dt;
-  if (MAT == MPM_J_FLUID) {
-    float J = b.F[slot];
-    if (pending) {
-      const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
-                          dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
-      J = J * det3(G);
-    }
-    F[id] = J;
-  } else {
-    float Fp[9];
-    for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
-    for (int r = 0; r < 3; ++r)
-      for (int c = 0; c < 3; ++c) {
-        float val = Fp[r * 3 + c];
-        if (pending)
-          val += dt * (Cp[r * 3 + 0] * Fp[0 * 3 + c] + Cp[r * 3 + 1] * Fp[1 * 3 + c] + Cp[r * 3 + 2] * Fp[2 * 3 + c]);
-        F[9 * id + r * 3 + c] = val;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + cur];
+  for (uint32_t c = blockIdx.x; c < nch; c += gridDim.x) {
+    const uint4 ch = s.chunks[cur][c];
+    for (uint32_t r = threadIdx.x; r < ch.y; r += 64) {
+      const size_t slot = (size_t)ch.x + r;
+      if (slot >= Np) break;
+      const size_t id = b.id[slot];
+      if (id >= (size_t)s.N) continue;
+      float Cp[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) Cp[k] = b.C[k * Np + slot];
+      for (int a = 0; a < 3; ++a) {
+        if (x) x[3 * id + a] = b.x[a * Np + slot];
+        if (v) v[3 * id + a] = b.v[a * Np + slot];
       }
+      if (C)
+        for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
+      if (!F) continue;
+      if (MAT == MPM_J_FLUID) {
+        float J = b.F[slot];
+        if (pending) {
+          const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
+                              dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
+          J = J * det3(G);
+        }
+        F[id] = J;
+      } else {
+        float Fp[9];
+        for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
+        for (int rr = 0; rr < 3; ++rr)
+          for (int cc = 0; cc < 3; ++cc) {
+            float val = Fp[rr * 3 + cc];
+            if (pending)
+              val += dt * (Cp[rr * 3 + 0] * Fp[0 * 3 + cc] + Cp[rr * 3 + 1] * Fp[1 * 3 + cc] +
+                           Cp[rr * 3 + 2] * Fp[2 * 3 + cc]);
+            F[9 * id + rr * 3 + cc] = val;
+          }
+      }
+    }
   }
 }
 
@@ -1347,6 +1359,14 @@ __global__ __launch_bounds__(WG) void k_read_grid(SimDev s, int q, float *__rest
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Slots per particle buffer: N plus the padding of every bin that can hold a
+// particle (at most SLOT_ALIGN - 1 each), in whole wavefronts.
+int64_t slot_capacity(int64_t N, int nbin) {
+  const int64_t bins = (int64_t)nbin * nbin * nbin;
+  return ((N + (int64_t)(SLOT_ALIGN - 1) * std::min(N, bins)) + 63) / 64 * 64;
+}
+constexpr int64_t MAX_SLOTS = int64_t(1) << 29;  // 8 Np < 2^32 (32-bit component offsets)
+
 bool valid_params(const mpm_params *p) {
   if (!p || p->struct_size < sizeof(mpm_params)) return false;
   // grid_n <= 1024: at most 256^3 bins, so a bin index fits below the cell
@@ -1366,10 +1386,10 @@ bool valid_params(const mpm_params *p) {
 
 // Workspace layout; with base == nullptr only the size is computed.
 size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d) {
-  const int64_t Np = ((N + 63) / 64) * 64;
   const int n = p->grid_n, nb = (n + NB - 1) / NB;
   const int64_t nblk = (int64_t)nb * nb * nb;
   const int nbin = (n + CB - 1) / CB;
+  const int64_t Np = slot_capacity(N, nbin);
   int nbin2 = 1;
   while (nbin2 < nbin) nbin2 <<= 1;
   const int64_t nbins = (int64_t)nbin2 * nbin2 * nbin2;
@@ -1561,6 +1581,7 @@ extern "C" {
 
 size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles) {
   if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 28)) return 0;
+  if (slot_capacity(n_particles, (params->grid_n + CB - 1) / CB) >= MAX_SLOTS) return 0;
   // The per-particle modulus array is always reserved so that one size fits
   // both the uniform and the per-particle case.
   return layout(params, n_particles, true, nullptr, nullptr);
@@ -1572,6 +1593,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
   if (!out) return MPM_ERR_INVALID_ARG;
   *out = nullptr;
   if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 28)) return MPM_ERR_INVALID_ARG;
+  if (slot_capacity(n_particles, (params->grid_n + CB - 1) / CB) >= MAX_SLOTS) return MPM_ERR_INVALID_ARG;
   if (n_particles > 0 && !x0) return MPM_ERR_INVALID_ARG;
   const size_t need = mpm_workspace_bytes(params, n_particles);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
@@ -1641,7 +1663,6 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
       launch_kernel(sim, 0, st, 0);
       launch_kernel(sim, 1, st, 0);
       k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
-      k_permute_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d);
       sim->cur = 1;
     }
     if (hipGetLastError() != hipSuccess) { rc = MPM_ERR_HIP; break; }
@@ -1706,9 +1727,9 @@ int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J
   if (!sim) return MPM_ERR_INVALID_ARG;
   if (sim->d.N == 0) return MPM_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int g = (sim->d.N + WG - 1) / WG;
-  if (sim->d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, WG, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
-  else k_read_particles<MPM_FIXED_COROTATED><<<g, WG, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
+  const int g = sim->grid_g2p;
+  if (sim->d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
+  else k_read_particles<MPM_FIXED_COROTATED><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 
