@@ -1138,50 +1138,61 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
   const uint32_t nch = s.ctr[CTR_NCHUNKS + (src ^ 1)];
   uint4 *chunks = s.chunks[src ^ 1];
   const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  // Window load in whole cubes (one 128-byte line each): lane = (cube, node
+  // in cube), 8 cubes per load instruction, 4 instructions.  This lane's
+  // window node of instruction t, packed wx | wy << 8 | wz << 16 (all ones
+  // when cube 8t + lane / 8 is past the 27th).
+  uint32_t wpack[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int cb = 8 * t + (lane >> 3), j = lane & 7;
+    const int wx = 2 * (cb % 3) + (j & 1), wy = 2 * ((cb / 3) % 3) + ((j >> 1) & 1), wz = 2 * (cb / 9) + (j >> 2);
+    wpack[t] = cb < 27 ? (uint32_t)(wx | (wy << 8) | (wz << 16)) : 0xFFFFFFFFu;
+  }
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = chunks[c];
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
-    // Window load in whole cubes (one 128-byte line each): lane = (cube,
-    // node in cube), 8 cubes per load instruction.  Nodes outside the grid
-    // read as zero.
-    {
-      // cube cb = 8t + lane / 8 at cube coordinates (cx, cy, cz), advanced
-      // by 8 = 2 rows + 2 cubes per step
-      const int j = lane & 7;
-      int cb = lane >> 3, cx = cb % 3, cy = cb / 3, cz = 0;
-#pragma unroll 1
-      for (; cb < 27; cb += 8) {
-        const int wx = 2 * cx + (j & 1), wy = 2 * cy + ((j >> 1) & 1), wz = 2 * cz + (j >> 2);
-        const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gx < s.n && gy < s.n && gz < s.n) g = grid_velocity(s, s.gridA[src][node_index(s, gx, gy, gz)], gx, gy, gz);
-        win[(wz * PW + wy) * PW + wx] = g;
-        cx += 2;
-        cy += 2;
-        if (cx >= 3) {
-          cx -= 3;
-          ++cy;
-        }
-        if (cy >= 3) {
-          cy -= 3;
-          ++cz;
-        }
-      }
+    // The window's accumulator values and the first round's positions are
+    // requested together, then the window is converted to velocities (the
+    // grid update) in LDS.  Nodes outside the grid read as zero.
+    float4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int gx = ox0 + (int)(wpack[t] & 0xFFu), gy = oy0 + (int)((wpack[t] >> 8) & 0xFFu),
+                gz = oz0 + (int)((wpack[t] >> 16) & 0xFFu);
+      if (wpack[t] != 0xFFFFFFFFu && gx < s.n && gy < s.n && gz < s.n) acc[t] = s.gridA[src][node_index(s, gx, gy, gz)];
+    }
+    float xnext[3] = {0.f, 0.f, 0.f};  // positions of the next round, written by this step's P2G in this order
+    if ((uint32_t)lane < count) {
+#pragma unroll
+      for (int a = 0; a < 3; ++a) xnext[a] = at_byte(out.x + a * Np, 4u * (start + (uint32_t)lane));
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (wpack[t] == 0xFFFFFFFFu) continue;
+      const int wx = (int)(wpack[t] & 0xFFu), wy = (int)((wpack[t] >> 8) & 0xFFu), wz = (int)((wpack[t] >> 16) & 0xFFu);
+      const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+      win[(wz * PW + wy) * PW + wx] =
+          (gx < s.n && gy < s.n && gz < s.n) ? grid_velocity(s, acc[t], gx, gy, gz) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     uint32_t nstay = 0;
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
       const uint32_t slot = start + r0 + (uint32_t)lane, so = 4u * slot;
       const bool valid = r0 + (uint32_t)lane < count;
+      float xp[3] = {xnext[0], xnext[1], xnext[2]};
+      if (r0 + 64u < count && r0 + 64u + (uint32_t)lane < count) {
+#pragma unroll
+        for (int a = 0; a < 3; ++a) xnext[a] = at_byte(out.x + a * Np, so + 256u);
+      }
       uint32_t key = 0;
       if (valid) {
-        float xp[3];
         int b[3];
         float w[3][3], d[3][3];
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
-          xp[a] = at_byte(out.x + a * Np, so);  // written by this step's P2G in this order
           const float xn = xp[a] * fn;
           b[a] = base_node(xn);
           const float f = xn - (float)b[a];
