@@ -704,7 +704,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
 
   // A chunk's sorted source indices and cells are loaded one chunk ahead,
   // during the previous chunk's pass B, so pass A starts with them in
-  // registers (lanes past the count get an invalid source and cell 0).
+  // registers (lanes past the count get an invalid source and cell 0).  The
+  // raw values are kept: clamping them here would wait for the loads.
   uint32_t pf_src[KMAX / 64], pf_cell[KMAX / 64];
   auto prefetch = [&](const uint4 &chrec) {
     const uint32_t pstart = chrec.x, pcount = min(chrec.y, (uint32_t)KMAX);
@@ -714,8 +715,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       pf_src[j] = 0xFFFFFFFFu;
       pf_cell[j] = 0u;
       if (qi < pcount) {
-        pf_src[j] = min(s.perm[pstart + qi], Np - 1u);
-        pf_cell[j] = (uint32_t)s.cellp[pstart + qi] & (uint32_t)(CB3 - 1);
+        pf_src[j] = s.perm[pstart + qi];
+        pf_cell[j] = s.cellp[pstart + qi];
       }
     }
   };
@@ -763,8 +764,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     uint32_t cells[KMAX / 64], srcs[KMAX / 64], srcmin[KMAX / 64];
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
-      cells[j] = pf_cell[j];
-      uint32_t src = pf_src[j];
+      cells[j] = pf_cell[j] & (uint32_t)(CB3 - 1);
+      uint32_t src = (uint32_t)(64 * j + lane) < count ? min(pf_src[j], Np - 1u) : 0xFFFFFFFFu;
       srcs[j] = src;
       srcmin[j] = 0xFFFFFFFFu;
       if ((uint32_t)j >= nsub) continue;
