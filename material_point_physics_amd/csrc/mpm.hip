@@ -134,6 +134,21 @@ __device__ __forceinline__ T &at_byte(T *base, uint32_t off) {
   return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
 }
 
+// Streaming accesses for particle fields that a step writes once and reads
+// only in the next step (F, E, id, v, C, G2P's advected x) or reads once
+// (P2G's C and F): the non-temporal hint keeps these lines from displacing
+// the ones reused within the step -- the positions P2G stores for G2P, the
+// keys G2P stores for the scatter, the grid lines of the windows.  Measured
+// on the 12M slab: scatter + P2G + G2P 1.154 -> 1.063 ms.
+template <typename T>
+__device__ __forceinline__ void stream_store(T v, T &dst) {
+  __builtin_nontemporal_store(v, &dst);
+}
+template <typename T>
+__device__ __forceinline__ T stream_load(const T &src) {
+  return __builtin_nontemporal_load(&src);
+}
+
 // Node-blocked grid index: blocks of 8^3 nodes (x fastest across blocks);
 // inside a block, 4^3 cubes of 2x2x2 nodes (x fastest), and inside a cube
 // the 8 nodes with x fastest.  A cube's 8 float4 records fill one 128-byte
@@ -874,17 +889,17 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         vp[a] = at_byte(in.v + a * Np, io);
       }
 #pragma unroll
-      for (int k = 0; k < 9; ++k) Cp[k] = at_byte(in.C + k * Np, io);
+      for (int k = 0; k < 9; ++k) Cp[k] = stream_load(at_byte(in.C + k * Np, io));
       if (valid) {
 #pragma unroll
         for (int a = 0; a < 3; ++a) at_byte(out.x + a * Np, od) = xp[a];
-        at_byte(out.id, od) = at_byte(in.id, io);
+        stream_store(at_byte(in.id, io), at_byte(out.id, od));
       }
 
       float tau_diag = 0.f;
       float tau[9];
       if (MAT == MPM_J_FLUID) {
-        float J = at_byte(in.F, io);
+        float J = stream_load(at_byte(in.F, io));
         if (pending) {
           const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
                               dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
@@ -892,15 +907,15 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         }
         const float K = HAS_E ? at_byte(in.E, io) : s.E;
         if (valid) {
-          at_byte(out.F, od) = J;
-          if (HAS_E) at_byte(out.E, od) = K;
+          stream_store(J, at_byte(out.F, od));
+          if (HAS_E) stream_store(K, at_byte(out.E, od));
           if (!(J > 0.f)) flag_status(s, MPM_STATUS_INVERTED, 2);
         }
         tau_diag = K * J * (J - 1.f);
       } else {
         float Fp[9];
 #pragma unroll
-        for (int k = 0; k < 9; ++k) Fp[k] = at_byte(in.F + k * Np, io);
+        for (int k = 0; k < 9; ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
         if (pending) {
           float Fn[9];
 #pragma unroll
@@ -915,8 +930,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         const float E = HAS_E ? at_byte(in.E, io) : s.E;
         if (valid) {
 #pragma unroll
-          for (int k = 0; k < 9; ++k) at_byte(out.F + k * Np, od) = Fp[k];
-          if (HAS_E) at_byte(out.E, od) = E;
+          for (int k = 0; k < 9; ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
+          if (HAS_E) stream_store(E, at_byte(out.E, od));
         }
         const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
         float R[9];
@@ -1257,15 +1272,15 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
           if (!isfinite(xa) || !isfinite(v[a])) nonfinite = true;
           if (xa < s.lo || xa > s.hi) clamped = true;
           xa = fminf(fmaxf(xa, s.lo), s.hi);
-          at_byte(out.x + a * Np, so) = xa;
-          at_byte(out.v + a * Np, so) = v[a];
+          stream_store(xa, at_byte(out.x + a * Np, so));
+          stream_store(v[a], at_byte(out.v + a * Np, so));
           b[a] = base_node(xa * fn);
         }
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
           const float ck = s.c_scale * B[k];
           if (!isfinite(ck)) nonfinite = true;
-          at_byte(out.C + k * Np, so) = ck;
+          stream_store(ck, at_byte(out.C + k * Np, so));
         }
         // the next bin: nearly always the chunk's own (Morton encoding only
         // when some lane of the wavefront left it)
