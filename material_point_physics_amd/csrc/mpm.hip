@@ -68,6 +68,7 @@ constexpr int NQ = 8;            // P2G work queues, one per XCD
 // padding slots (holes) are never read: every kernel walks the chunk list.
 constexpr int SLOT_ALIGN = 32;
 constexpr int NUM_KERNELS = 5;
+constexpr int STEP_BATCH = 8;    // steps per batched graph (even: a batch ends on its starting parity)
 
 enum Ctr : int {
   CTR_NCHUNKS = 0,  // + layout parity: chunks of each layout
@@ -494,10 +495,11 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
   block_scan_incl<NT>(pc, wsum, &tile_base_c);
   block_scan_incl<NT>(pch, wsum, &tile_base_ch);
   const uint32_t lb0 = threadIdx.x * SCAN_PER, b0 = t * TILE + lb0;
-  uint32_t c[SCAN_PER], ch[SCAN_PER], csum = 0, chsum = 0;
+  uint32_t c[SCAN_PER], st[SCAN_PER], ch[SCAN_PER], csum = 0, chsum = 0;
 #pragma unroll
   for (int k = 0; k < SCAN_PER; ++k) {
     c[k] = (b0 + k < nbins) ? s.bin_count[b0 + k] : 0u;
+    st[k] = (b0 + k < nbins) ? s.stay_count[b0 + k] : 0u;  // (loaded with the counts: no second round trip)
     ch[k] = (c[k] + (1u << shift) - 1u) >> shift;
     csum += padded(c[k]);
     chsum += ch[k];
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
     if (b < nbins) {
       s.bin_count[b] = 0u;
       if (c[k] > 0u) {  // (stay_count <= bin_count: both are zero otherwise)
-        const uint32_t stay = min(s.stay_count[b], c[k]);
+        const uint32_t stay = min(st[k], c[k]);
         s.stay_count[b] = 0u;
         s.bin_start[b] = tile_base_c + run;
         s.bin_cursor[b] = tile_base_c + run + stay;
@@ -738,10 +740,12 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   // Clear the previous step's accumulator (the other parity): the
   // node-blocks it marked, and their marks; its G2P has finished reading
   // them, and the next step accumulates there.  Workgroup b takes blocks
-  // b, b + grid, ...; the stores drain while it works on its chunks.
+  // G-1-b, 2G-1-b, ... (G workgroups; counted from the last one because in
+  // a small scene the first ones have chunks and the flag loads would delay
+  // them); the stores drain while it works on its chunks.
   {
     const int prev = src ^ 1;
-    for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+    for (uint32_t blk = gridDim.x - 1u - blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
       if (s.active_flag[prev][blk] == 0u) continue;
       float4 *g = s.gridA[prev] + ((size_t)blk << 9);
 #pragma unroll
@@ -1518,8 +1522,11 @@ struct mpm_sim {
   int cur = 0;  // buffer holding the current state
   int64_t steps = 0;
   hipStream_t cap = nullptr;
-  hipGraph_t graph[2] = {nullptr, nullptr};
-  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  // graph[q]: one step that reads buffer q; graph[2 + q]: STEP_BATCH steps
+  // starting from buffer q (the per-launch gap between graphs, ~8 us on
+  // this GPU, is paid once per batch)
+  hipGraph_t graph[4] = {nullptr, nullptr, nullptr, nullptr};
+  hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_scatter = 0;
   int grid_p2g = 0;
@@ -1574,24 +1581,26 @@ int enqueue_step(mpm_sim *sim, hipStream_t st, int src) {
 }
 
 int build_graphs(mpm_sim *sim) {
-  for (int src = 0; src < 2; ++src) {
+  for (int g = 0; g < 4; ++g) {
+    const int src = g & 1, nsteps = g < 2 ? 1 : STEP_BATCH;
     HIP_TRY(hipStreamBeginCapture(sim->cap, hipStreamCaptureModeThreadLocal));
-    const int rc = enqueue_step(sim, sim->cap, src);
-    hipGraph_t g = nullptr;
-    const hipError_t e = hipStreamEndCapture(sim->cap, &g);
+    int rc = MPM_OK;
+    for (int k = 0; k < nsteps && rc == MPM_OK; ++k) rc = enqueue_step(sim, sim->cap, src ^ (k & 1));
+    hipGraph_t gr = nullptr;
+    const hipError_t e = hipStreamEndCapture(sim->cap, &gr);
     if (rc || e != hipSuccess) {
-      if (g) (void)hipGraphDestroy(g);
+      if (gr) (void)hipGraphDestroy(gr);
       return MPM_ERR_HIP;
     }
-    sim->graph[src] = g;
-    HIP_TRY(hipGraphInstantiate(&sim->exec[src], g, nullptr, nullptr, 0));
+    sim->graph[g] = gr;
+    HIP_TRY(hipGraphInstantiate(&sim->exec[g], gr, nullptr, nullptr, 0));
   }
   return MPM_OK;
 }
 
 void release(mpm_sim *sim) {
   if (!sim) return;
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < 4; ++k) {
     if (sim->exec[k]) (void)hipGraphExecDestroy(sim->exec[k]);
     if (sim->graph[k]) (void)hipGraphDestroy(sim->graph[k]);
   }
@@ -1709,9 +1718,16 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
     sim->steps += n_steps;
     return MPM_OK;
   }
-  if (!sim->exec[0] || !sim->exec[1]) return MPM_ERR_STATE;
+  for (int g = 0; g < 4; ++g)
+    if (!sim->exec[g]) return MPM_ERR_STATE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  for (int32_t k = 0; k < n_steps; ++k) {
+  int32_t left = n_steps;
+  while (left >= STEP_BATCH) {  // batches end on their starting parity
+    if (hipGraphLaunch(sim->exec[2 + sim->cur], st) != hipSuccess) return MPM_ERR_HIP;
+    sim->steps += STEP_BATCH;
+    left -= STEP_BATCH;
+  }
+  for (; left > 0; --left) {
     if (hipGraphLaunch(sim->exec[sim->cur], st) != hipSuccess) return MPM_ERR_HIP;
     sim->cur ^= 1;
     sim->steps += 1;
