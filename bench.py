@@ -35,12 +35,20 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bool) -> dict:
+def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bool, sorted_steps=True) -> dict:
     """Algorithmic HBM bytes per launch of each kernel (what the method must
     move through that kernel; see the byte model in the design notes).
-    fp32 everywhere; F is 9 floats (elastic) or 1 (fluid J)."""
+    fp32 everywhere; F is 9 floats (elastic) or 1 (fluid J).  With
+    sorted_steps=False (free-zone steps without a sort) the scatter moves
+    nothing and P2G reads the key word (4 B) instead of perm and the cell
+    byte (5 B)."""
     f = 36 if material == 0 else 4
     e = 4 if has_E else 0
+    if not sorted_steps:
+        kb = kernel_bytes(N, active_nodes, nbins, material, has_E)
+        kb["k_scatter"] = 0
+        kb["k_p2g"] -= N
+        return kb
     return {
         # bin counts read twice, cursors written, counts zeroed
         "k_scan_tiles": 4 * nbins,
@@ -92,6 +100,11 @@ def main():
     ap.add_argument("--workload", default="slab_12m")
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps for the CPU baseline (0 = skip)")
+    ap.add_argument("--sort-interval", type=int, default=0,
+                    help="free-zone sort policy: sort at least every K steps (0 = sort every step, the default)")
+    ap.add_argument("--mover-budget", type=int, default=-1,
+                    help="free-zone sort policy: also sort when more particles than this left their bins "
+                         "(default: N/1000)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -108,6 +121,11 @@ def main():
     log(f"scene {sc.name}: N={sc.N} n={sc.n} generated in {time.time() - t0:.1f}s")
     sim = mpm.Simulation(sc)
     stream = sim.stream
+    free_zone = args.sort_interval > 1
+    budget = args.mover_budget if args.mover_budget >= 0 else sc.N // 1000
+    if free_zone:
+        sim.set_sort_policy(args.sort_interval, budget)
+        log(f"free-zone sort policy: at least every {args.sort_interval} steps, or more than {budget} movers")
     log("created; warmup")
     sim.step(args.warmup)
     torch.cuda.synchronize()
@@ -147,7 +165,8 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst
-    kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None)
+    kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None,
+                      sorted_steps=not free_zone)
     kernels = {k: {"avg_ms": round(kavg[k], 5), "alg_bytes": kb[k],
                    "GBps": round(kb[k] / (kavg[k] * 1e-3) / 1e9, 1)} for k in kavg}
     dom = max(kavg, key=kavg.get)
@@ -186,7 +205,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{sc.name}: {sc.description}", "particles": sc.N, "grid": f"{n}^3",
-                   "dt": sc.dt, "material": "fixed-corotated" if sc.material == 0 else "J-fluid"},
+                   "dt": sc.dt, "material": "fixed-corotated" if sc.material == 0 else "J-fluid",
+                   "sort": (f"free zone: at least every {args.sort_interval} steps or above {budget} movers "
+                            "(byte model assumes no sort in the timed steps)") if free_zone else "every step"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "step_hbm": {"alg_bytes_per_step": step_bytes,

@@ -128,9 +128,25 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
                size_t workspace_bytes, void *stream, mpm_sim **out);
 
 /* Advance n_steps >= 0 explicit steps, enqueued asynchronously on `stream`
- * (one graph launch per step: key/bucket sort, P2G, grid update, G2P).  No
- * host synchronisation, no allocation. */
+ * (captured graphs of 8 steps, then single steps: per step key/bucket sort,
+ * P2G, grid update, G2P).  No host synchronisation, no allocation. */
 int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream);
+
+/* Sort policy: the free zone of the page's non-essential-phase discussion
+ * (the particle-to-bin mapping is rebuilt only when needed).
+ *   max_interval : 0 or 1 = sort every step (the default); k > 1 = sort at
+ *                  least every k steps.
+ *   mover_budget : between those sorts, sort as soon as more than this many
+ *                  particles are outside the bin of their chunk (counted on
+ *                  the device by G2P; the decision is taken on the device at
+ *                  the start of each step, without a host synchronisation).
+ * Between sorts each chunk keeps its particles, and a particle that left its
+ * chunk's bin is deposited and gathered through the grid directly (global
+ * atomics and loads) instead of the chunk's LDS window.  The results equal
+ * those of sorting every step up to the order of float additions.  Enqueued
+ * on `stream`, it applies from the next step on.  Negative arguments return
+ * MPM_ERR_INVALID_ARG. */
+int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget, void *stream);
 
 /* Copy the particle state after the last step, in creation order, into
  * caller-owned device arrays: x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)

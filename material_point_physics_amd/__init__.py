@@ -37,7 +37,8 @@ MPM_STATUS_NO_CONVERGE = 0x10
 MPM_STATUS_WORDS = 8
 
 # Every symbol include/mpm.h declares.
-EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_read_particles", "mpm_read_grid",
+EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_set_sort_policy", "mpm_read_particles",
+           "mpm_read_grid",
            "mpm_status", "mpm_steps_taken", "mpm_num_kernels", "mpm_kernel_name", "mpm_step_profiled",
            "mpm_destroy", "mpm_error_string")
 
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.mpm_create.restype = ctypes.c_int
     L.mpm_step.argtypes = [vp, i32, vp]
     L.mpm_step.restype = ctypes.c_int
+    L.mpm_set_sort_policy.argtypes = [vp, i32, i64, vp]
+    L.mpm_set_sort_policy.restype = ctypes.c_int
     L.mpm_read_particles.argtypes = [vp, vp, vp, vp, vp, vp]
     L.mpm_read_particles.restype = ctypes.c_int
     L.mpm_read_grid.argtypes = [vp, vp, vp, vp]
@@ -151,6 +154,11 @@ def mpm_create(params: mpm_params, n_particles: int, x0, v0=None, C0=None, F0=No
 
 def mpm_step(sim: int, n_steps: int, stream=None) -> None:
     _check(lib().mpm_step(sim, int(n_steps), _stream(stream)), "mpm_step")
+
+
+def mpm_set_sort_policy(sim: int, max_interval: int, mover_budget: int, stream=None) -> None:
+    _check(lib().mpm_set_sort_policy(sim, int(max_interval), int(mover_budget), _stream(stream)),
+           "mpm_set_sort_policy")
 
 
 def mpm_read_particles(sim: int, x=None, v=None, C=None, F_or_J=None, stream=None) -> None:
@@ -238,6 +246,9 @@ class Simulation:
 
     def step(self, k: int = 1):
         mpm_step(self.handle, k, self.stream)
+
+    def set_sort_policy(self, max_interval: int, mover_budget: int):
+        mpm_set_sort_policy(self.handle, max_interval, mover_budget, self.stream)
 
     def read_particles(self):
         torch = self.torch

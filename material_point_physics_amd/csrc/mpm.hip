@@ -71,10 +71,16 @@ constexpr int NUM_KERNELS = 5;
 constexpr int STEP_BATCH = 8;    // steps per batched graph (even: a batch ends on its starting parity)
 
 enum Ctr : int {
-  CTR_NCHUNKS = 0,  // + layout parity: chunks of each layout
+  CTR_NCHUNKS = 0,       // + layout parity: chunks of each layout
   CTR_PENDING = 2,
+  CTR_MOVERS = 3,        // particles outside their chunk's bin after the last G2P
+  CTR_SINCE = 4,         // steps since the last sort
+  CTR_SORT = 5,          // + buffer parity: whether the step that reads that buffer sorts
+  CTR_MAX_INTERVAL = 7,  // sort policy: at least every this many steps (0 or 1: every step) ...
+  CTR_MOVER_BUDGET = 8,  // ... and whenever more particles than this are outside their bins
   CTR_WORDS = 16,
 };
+constexpr uint8_t MOVER_TAG = 0xFF;  // P2G order tag of a particle outside its chunk's bin
 
 struct PBuf {
   float *x;      // [3][Np]
@@ -405,6 +411,14 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
   wave_aggregated_increment(s.bin_count, key, valid);
 }
 
+// Sort policy words (see mpm_set_sort_policy).
+__global__ void k_set_sort_policy(SimDev s, uint32_t max_interval, uint32_t mover_budget) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    s.ctr[CTR_MAX_INTERVAL] = max_interval;
+    s.ctr[CTR_MOVER_BUDGET] = mover_budget;
+  }
+}
+
 // Zero a uint32 range (fill kernel; graphs avoid memset nodes).
 __global__ __launch_bounds__(WG) void k_zero_u32(uint32_t *p, size_t n) {
   for (size_t k = (size_t)blockIdx.x * WG + threadIdx.x; k < n; k += (size_t)gridDim.x * WG) p[k] = 0u;
@@ -448,9 +462,23 @@ __device__ __forceinline__ uint32_t padded(uint32_t count) {
   return (count + (uint32_t)SLOT_ALIGN - 1u) & ~(uint32_t)(SLOT_ALIGN - 1);
 }
 
+// Whether the current step sorts (the free-zone policy of [RT-MPM],
+// non-essential-phase discussion: particles stay in their bins' chunks
+// between sorts, and the few that left their bin are handled one by one).
+// Every step sorts unless a policy was set with mpm_set_sort_policy.
+__device__ __forceinline__ bool sort_this_step(const SimDev &s) {
+  const uint32_t maxint = s.ctr[CTR_MAX_INTERVAL];
+  return maxint <= 1u || s.ctr[CTR_SINCE] + 1u >= maxint || s.ctr[CTR_MOVERS] > s.ctr[CTR_MOVER_BUDGET];
+}
+
 // Scan, phase 1: per-tile totals of (padded) slot counts and chunk counts.
-__global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s) {
+// Also takes the step's sort decision (uniform: every thread reads the same
+// counters) and publishes it for the step's other kernels.
+__global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s, int src) {
   __shared__ uint32_t wsum[WG / 64];
+  const bool sort = sort_this_step(s);
+  if (blockIdx.x == 0 && threadIdx.x == 0) s.ctr[CTR_SORT + src] = sort ? 1u : 0u;
+  if (!sort) return;
   const uint32_t nbins = (uint32_t)s.nbins;
   const uint32_t b0 = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_PER;
   uint32_t c = 0, ch = 0;
@@ -486,6 +514,37 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
   const uint32_t nbins = (uint32_t)s.nbins;
   const uint32_t t = blockIdx.x;
   const uint32_t shift = (uint32_t)s.chunk_shift;
+  const int src = lay ^ 1;
+  // The sort decision: taken here by the one-workgroup scan (no k_scan_tiles
+  // before it), else read from k_scan_tiles.  The mover count is reset for
+  // G2P to fill again (every thread has read it before the barrier).
+  bool sort;
+  if (NT == SCAN_SMALL_NT) {
+    sort = sort_this_step(s);
+    __syncthreads();
+    if (threadIdx.x == 0) s.ctr[CTR_SORT + src] = sort ? 1u : 0u;
+  } else {
+    sort = s.ctr[CTR_SORT + src] != 0u;
+  }
+  if (t == 0 && threadIdx.x == 0) s.ctr[CTR_MOVERS] = 0u;
+  if (!sort) {
+    // No sort: layout lay repeats layout src (its chunk list is copied),
+    // and the bin counts are cleared for this step's G2P.
+    const uint32_t nch_old = s.ctr[CTR_NCHUNKS + src];
+    for (uint32_t c = t * NT + threadIdx.x; c < nch_old; c += gridDim.x * NT) s.chunks[lay][c] = s.chunks[src][c];
+    const uint32_t b0 = t * TILE + threadIdx.x * SCAN_PER;
+#pragma unroll
+    for (int k = 0; k < SCAN_PER; ++k)
+      if (b0 + k < nbins) {
+        s.bin_count[b0 + k] = 0u;
+        s.stay_count[b0 + k] = 0u;
+      }
+    if (t == 0 && threadIdx.x == 0) {
+      s.ctr[CTR_NCHUNKS + lay] = nch_old;
+      s.ctr[CTR_SINCE] = s.ctr[CTR_SINCE] + 1u;
+    }
+    return;
+  }
   uint32_t pc = 0, pch = 0;
   for (uint32_t k = threadIdx.x; k < t; k += NT) {
     pc += s.tile_sum[2 * k];
@@ -557,6 +616,7 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
     s.chunks[lay][tile_base_ch + cc] = make_uint4(tile_base_c + pstart + off, cnt, t * TILE + lo, cnt);
   }
   if (t == gridDim.x - 1 && threadIdx.x == 0) s.ctr[CTR_NCHUNKS + lay] = tile_base_ch + tch;
+  if (t == 0 && threadIdx.x == 0) s.ctr[CTR_SINCE] = 0u;
 }
 
 // Creation: move the initial state (buffer 0, creation order) into bin order
@@ -606,6 +666,7 @@ __global__ __launch_bounds__(WG) void k_scatter_init(SimDev s) {
 // consecutive addresses.  A particle that changes bin takes the bin's atomic
 // cursor, which starts after the bin's stayers.
 __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
+  if (s.ctr[CTR_SORT + src] == 0u) return;  // a step without a sort
   const int lane = threadIdx.x;
   const uint64_t below = (1ull << lane) - 1ull;
   const uint32_t nch = s.ctr[CTR_NCHUNKS + src];
@@ -697,15 +758,16 @@ struct P2GRankTables {                   // lives in the window space while a ch
 };
 static_assert(sizeof(P2GRankTables) <= sizeof(float4) * NWIN * PW3, "rank tables must fit the windows");
 
-template <int MAT, bool HAS_E>
-__global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
-  __shared__ union P2GShared {
-    float4 win[NWIN * PW3];
-    P2GRankTables rk;
-  } sm;
-  __shared__ uint32_t order[KMAX];      // source index of each processing position
-  __shared__ uint8_t ordtag[KMAX];      // super-rank * NWIN + window of each position
+union P2GShared {
+  float4 win[NWIN * PW3];
+  P2GRankTables rk;
+};
 
+// The P2G of one step.  FREE: a step without a sort (free-zone policy), with
+// the paths for particles outside their chunk's bin; the per-step-sort
+// instance has none of that code.
+template <int MAT, bool HAS_E, bool FREE>
+__device__ __forceinline__ void p2g_step(const SimDev &s, int src, P2GShared &sm, uint32_t *order, uint8_t *ordtag) {
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
   const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
@@ -717,6 +779,11 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   const uint4 *chunks = s.chunks[src ^ 1];  // the layout this step builds
   const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
   const bool pending = s.ctr[CTR_PENDING] != 0u;
+  // Without a sort this step (free-zone policy), the layout is the previous
+  // one: each slot is its own source, its cell comes from the key G2P wrote,
+  // and a particle whose key names another bin is outside the chunk's window
+  // (a mover: deposited with direct global atomics).
+  constexpr bool sorted = !FREE;
   const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
 
   // A chunk's sorted source indices and cells are loaded one chunk ahead,
@@ -732,8 +799,13 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       pf_src[j] = 0xFFFFFFFFu;
       pf_cell[j] = 0u;
       if (qi < pcount) {
-        pf_src[j] = s.perm[pstart + qi];
-        pf_cell[j] = s.cellp[pstart + qi];
+        if (sorted) {
+          pf_src[j] = s.perm[pstart + qi];
+          pf_cell[j] = s.cellp[pstart + qi];
+        } else {
+          pf_src[j] = pstart + qi;
+          pf_cell[j] = s.key[pstart + qi];  // the whole key: bin and cell
+        }
       }
     }
   };
@@ -780,10 +852,15 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     // cell that G2P computed with the key, so no position gather is needed)
     // (sub-rounds past the chunk's count are skipped with uniform branches)
     const uint32_t nsub = (count + 63u) / 64u;
+    // cells[j]: the cell (bits 0-5) and, bit 6, a mover (never in a sorted step)
     uint32_t cells[KMAX / 64], srcs[KMAX / 64], srcmin[KMAX / 64];
+    uint32_t nmov = 0;
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
-      cells[j] = pf_cell[j] & (uint32_t)(CB3 - 1);
+      const uint32_t kc = pf_cell[j];
+      const bool mv = !sorted && (uint32_t)(64 * j + lane) < count && (kc & ((1u << KEY_CELL_SHIFT) - 1u)) != bin;
+      cells[j] = ((sorted ? kc : (kc >> KEY_CELL_SHIFT)) & (uint32_t)(CB3 - 1)) | (mv ? (uint32_t)CB3 : 0u);
+      if (FREE) nmov += (uint32_t)__popcll(__ballot(mv));
       uint32_t src = (uint32_t)(64 * j + lane) < count ? min(pf_src[j], Np - 1u) : 0xFFFFFFFFu;
       srcs[j] = src;
       srcmin[j] = 0xFFFFFFFFu;
@@ -798,8 +875,8 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
     for (int j = 0; j < KMAX / 64; ++j) {
       rin[j] = 0u;
       if ((uint32_t)j >= nsub) continue;
-      const bool v = (uint32_t)(64 * j + lane) < count;
-      const uint32_t cell = cells[j];
+      const bool v = (uint32_t)(64 * j + lane) < count && (!FREE || cells[j] < (uint32_t)CB3);
+      const uint32_t cell = cells[j] & (uint32_t)(CB3 - 1);
       uint64_t peers = __ballot(v);
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
@@ -820,7 +897,7 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       for (int k = 0; k < KMAX / 64; ++k) {
         if ((uint32_t)k >= nsub) continue;
         const bool earlier = srcmin[k] < srcmin[j] || (srcmin[k] == srcmin[j] && k < j);
-        if (k != j && earlier) before += rk.subcnt[k][cells[j]];
+        if (k != j && earlier) before += rk.subcnt[k][cells[j] & (uint32_t)(CB3 - 1)];
       }
       rank[j] = before + rin[j];
     }
@@ -853,17 +930,26 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       }
     }
     __syncthreads();
+    uint32_t mbefore = count - nmov;  // movers go after the ranked particles
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) {
       const uint32_t qi = (uint32_t)(64 * j + lane);
+      const uint64_t mmask = FREE ? __ballot(cells[j] >= (uint32_t)CB3) : 0ull;
       if ((uint32_t)j < nsub && qi < count) {
-        const uint32_t cell = cells[j], sr = rank[j] / NWIN, w = rank[j] % NWIN;
-        uint32_t pos = rk.rstart[sr] + (uint32_t)__popcll(rk.rmask[NWIN * sr + w] & ((1ull << cell) - 1ull));
-        for (uint32_t w2 = 0; w2 < w; ++w2) pos += (uint32_t)__popcll(rk.rmask[NWIN * sr + w2]);
-        pos = min(pos, (uint32_t)KMAX - 1u);
-        order[pos] = srcs[j];
-        ordtag[pos] = (uint8_t)(sr * NWIN + w);
+        if (FREE && cells[j] >= (uint32_t)CB3) {
+          const uint32_t pos = min(mbefore + (uint32_t)__popcll(mmask & below), (uint32_t)KMAX - 1u);
+          order[pos] = srcs[j];
+          ordtag[pos] = MOVER_TAG;
+        } else {
+          const uint32_t cell = cells[j], sr = rank[j] / NWIN, w = rank[j] % NWIN;
+          uint32_t pos = rk.rstart[sr] + (uint32_t)__popcll(rk.rmask[NWIN * sr + w] & ((1ull << cell) - 1ull));
+          for (uint32_t w2 = 0; w2 < w; ++w2) pos += (uint32_t)__popcll(rk.rmask[NWIN * sr + w2]);
+          pos = min(pos, (uint32_t)KMAX - 1u);
+          order[pos] = srcs[j];
+          ordtag[pos] = (uint8_t)(sr * NWIN + w);
+        }
       }
+      mbefore += (uint32_t)__popcll(mmask);
     }
     __syncthreads();
     // the tables are dead: clear the windows
@@ -986,10 +1072,13 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
       // round with the same (window, cell) (ballot-matched, 7 bits), which
       // gives the fewest conflict-free passes; lanes of one super-rank never
       // share (window, cell), so this is at most one pass per super-rank.
+      // (a mover's stencil is outside the window: it takes no pass)
+      const bool mov = FREE && tag == MOVER_TAG;
+      const bool inwin = valid && !mov;
       uint32_t pass_id;
       {
         const uint32_t wc = (tag % NWIN) * (uint32_t)CB3 + (uint32_t)((lz * CB + ly) * CB + lx);
-        uint64_t peers = __ballot(valid);
+        uint64_t peers = __ballot(inwin);
 #pragma unroll
         for (int k = 0; k < 7; ++k) {
           const uint64_t bk = __ballot((wc >> k) & 1u);
@@ -997,7 +1086,35 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
         }
         pass_id = (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
       }
-      bool todo = valid;
+      // A mover (only in a step without a sort; rare) deposits its 27 nodes
+      // with direct global atomics and marks the node-blocks its stencil
+      // touches, for the next step's clear and the grid readback.
+      if (FREE && valid && mov) {
+#pragma unroll 1
+        for (int oz = 0; oz < 3; ++oz)
+#pragma unroll 1
+          for (int oy = 0; oy < 3; ++oy)
+#pragma unroll 1
+            for (int ox = 0; ox < 3; ++ox) {
+              const int gx = b[0] + ox, gy = b[1] + oy, gz = b[2] + oz;
+              if (gx < 0 || gy < 0 || gz < 0 || gx >= s.n || gy >= s.n || gz >= s.n) continue;
+              const float wt = w[0][ox] * w[1][oy] * w[2][oz];
+              float *g = reinterpret_cast<float *>(s.gridA[src] + node_index(s, gx, gy, gz));
+              unsafeAtomicAdd(g + 0, wt * mass);
+              unsafeAtomicAdd(g + 1, wt * (q0[0] + Ad[0] * ox + Ad[1] * oy + Ad[2] * oz));
+              unsafeAtomicAdd(g + 2, wt * (q0[1] + Ad[3] * ox + Ad[4] * oy + Ad[5] * oz));
+              unsafeAtomicAdd(g + 3, wt * (q0[2] + Ad[6] * ox + Ad[7] * oy + Ad[8] * oz));
+            }
+#pragma unroll 1
+        for (int k = 0; k < 8; ++k) {
+          const int gx = min(b[0] + 2 * (k & 1), s.n - 1), gy = min(b[1] + ((k >> 1) & 1) * 2, s.n - 1),
+                    gz = min(b[2] + (k >> 2) * 2, s.n - 1);
+          if (gx < 0 || gy < 0 || gz < 0) continue;
+          s.active_flag[src][((uint32_t)(gz >> 3) * (uint32_t)s.nb + (uint32_t)(gy >> 3)) * (uint32_t)s.nb +
+                             (uint32_t)(gx >> 3)] = 1u;
+        }
+      }
+      bool todo = inwin;
       for (uint32_t pnow = 0;; ++pnow) {
         // (occurrence indices of a key are 0, 1, ..., so no lane waits for a
         // pass after an empty one)
@@ -1122,7 +1239,16 @@ __global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
   }
 }
 
-// The grid update (a4) -- v = p/m + dt g where m > 0, sticky walls -- is
+template <int MAT, bool HAS_E>
+__global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
+  __shared__ P2GShared sm;
+  __shared__ uint32_t order[KMAX];  // source index of each processing position
+  __shared__ uint8_t ordtag[KMAX];  // super-rank * NWIN + window of each position (or MOVER_TAG)
+  if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false>(s, src, sm, order, ordtag);
+  else p2g_step<MAT, HAS_E, true>(s, src, sm, order, ordtag);
+}
+
+// The grid update -- v = p/m + dt g where m > 0, sticky walls -- is
 // evaluated by G2P on its window nodes as it loads them (grid_velocity), and
 // the accumulator is cleared by the next step's P2G, so the step needs no
 // separate pass over the grid.
@@ -1221,6 +1347,11 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
           d[a][1] = 1.f - f;
           d[a][2] = 2.f - f;
         }
+        // A particle that left its chunk's bin since the last sort (only
+        // without a sort this step; rare) has its stencil outside the window:
+        // it gathers its 27 nodes from the grid, with the grid update.
+        const bool outside = b[0] - ox0 < 0 || b[0] - ox0 >= CB || b[1] - oy0 < 0 || b[1] - oy0 >= CB ||
+                             b[2] - oz0 < 0 || b[2] - oz0 >= CB;
         const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
                   lz = min(max(b[2] - oz0, 0), CB - 1);
         const int li0 = (lz * PW + ly) * PW + lx;
@@ -1232,6 +1363,35 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
         // column.
         const float w2x = 2.f * w[0][2];
         float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (outside) {
+          // node rows of three, their loads issued together
+#pragma unroll 1
+          for (int r = 0; r < 9; ++r) {
+            const int oy = r % 3, oz = r / 3;
+            const int gy = b[1] + oy, gz = b[2] + oz;
+            float4 acc[3];
+#pragma unroll
+            for (int ox = 0; ox < 3; ++ox) {
+              const int gx = b[0] + ox;
+              acc[ox] = make_float4(0.f, 0.f, 0.f, 0.f);
+              if (gx >= 0 && gy >= 0 && gz >= 0 && gx < s.n && gy < s.n && gz < s.n)
+                acc[ox] = s.gridA[src][node_index(s, gx, gy, gz)];
+            }
+#pragma unroll
+            for (int ox = 0; ox < 3; ++ox) {
+              const float4 g = grid_velocity(s, acc[ox], b[0] + ox, gy, gz);
+              const float wt = w[0][ox] * w[1][oy] * w[2][oz];
+              const float vel[3] = {g.x, g.y, g.z};
+#pragma unroll
+              for (int a = 0; a < 3; ++a) {
+                v[a] = fmaf(wt, vel[a], v[a]);
+                B[a * 3 + 0] = fmaf(wt * (float)ox, vel[a], B[a * 3 + 0]);
+                B[a * 3 + 1] = fmaf(wt * (float)oy, vel[a], B[a * 3 + 1]);
+                B[a * 3 + 2] = fmaf(wt * (float)oz, vel[a], B[a * 3 + 2]);
+              }
+            }
+          }
+        } else {
 #pragma unroll
         for (int oz = 0; oz < 3; ++oz)
 #pragma unroll
@@ -1265,6 +1425,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
               if (oz > 0) B[a * 3 + 2] = fmaf(oz == 1 ? wyz : wyz2, S[a], B[a * 3 + 2]);
             }
           }
+        }
 #pragma unroll
         for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -1302,6 +1463,7 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
     if (lane == 0) {
       chunks[c].w = nstay;
       if (nstay) atomicAdd(s.stay_count + bin, nstay);
+      if (nstay < count) atomicAdd(s.ctr + CTR_MOVERS, count - nstay);  // for the next sort decision
     }
     __syncthreads();  // the window is reloaded for the next chunk
   }
@@ -1546,7 +1708,7 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
   switch (k) {
     case 0:
       // (a small grid's bins are scanned by one workgroup, without tile totals)
-      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d);
+      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d, src);
       break;
     case 1:
       if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_bins<WG><<<d.ntiles, WG, 0, st>>>(d, src ^ 1);
@@ -1733,6 +1895,13 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
     sim->steps += 1;
   }
   return MPM_OK;
+}
+
+int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget, void *stream) {
+  if (!sim || max_interval < 0 || mover_budget < 0) return MPM_ERR_INVALID_ARG;
+  const uint32_t budget = mover_budget > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)mover_budget;
+  k_set_sort_policy<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(sim->d, (uint32_t)max_interval, budget);
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 
 int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms) {

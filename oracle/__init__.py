@@ -162,17 +162,18 @@ class OracleSim:
         self.params = make_params(**p)
         self.n = p["n"]
         N = scene.N if x is None else len(x)
-        self.x = np.ascontiguousarray(np.asarray(scene.x if x is None else x, dt).reshape(N, 3))
-        self.v = np.ascontiguousarray(np.asarray(scene.v if v is None else v, dt).reshape(N, 3))
+        # Own copies: the state is advanced in place, and the inputs (the
+        # scene's arrays) must stay as they were.
+        own = lambda a, shape: np.array(np.reshape(a, shape), dtype=dt, order="C", copy=True)
+        self.x = own(scene.x if x is None else x, (N, 3))
+        self.v = own(scene.v if v is None else v, (N, 3))
         C0 = C if C is not None else scene.C
-        self.C = (np.zeros((N, 3, 3), dt) if C0 is None
-                  else np.ascontiguousarray(np.asarray(C0, dt).reshape(N, 3, 3)))
+        self.C = np.zeros((N, 3, 3), dt) if C0 is None else own(C0, (N, 3, 3))
         F0 = F if F is not None else scene.F
-        self.F = (np.tile(np.eye(3, dtype=dt), (N, 1, 1)) if F0 is None
-                  else np.ascontiguousarray(np.asarray(F0, dt).reshape(N, 3, 3)))
+        self.F = np.tile(np.eye(3, dtype=dt), (N, 1, 1)) if F0 is None else own(F0, (N, 3, 3))
         J0 = J if J is not None else scene.J
-        self.J = np.ones(N, dt) if J0 is None else np.ascontiguousarray(np.asarray(J0, dt).reshape(N))
-        self.E_p = None if scene.E_p is None else np.ascontiguousarray(np.asarray(scene.E_p, dt))
+        self.J = np.ones(N, dt) if J0 is None else own(J0, (N,))
+        self.E_p = None if scene.E_p is None else own(scene.E_p, (N,))
         nn = self.n ** 3
         self.gm = np.zeros(nn, dt)
         self.gp = np.zeros((nn, 3), dt)

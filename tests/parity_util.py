@@ -19,11 +19,14 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def gpu_run(scene, steps: int, read=("particles", "grid")):
-    """Create, step and read back through the C ABI (torch only for memory)."""
+def gpu_run(scene, steps: int, read=("particles", "grid"), sort_policy=None):
+    """Create, step and read back through the C ABI (torch only for memory).
+    sort_policy = (max_interval, mover_budget) for mpm_set_sort_policy."""
     import material_point_physics_amd as mpm
     sim = mpm.Simulation(scene)
     try:
+        if sort_policy is not None:
+            sim.set_sort_policy(*sort_policy)
         sim.step(steps)
         out = {}
         if "particles" in read:

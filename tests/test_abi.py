@@ -95,6 +95,7 @@ def test_create_rejects_bad_arguments_before_any_launch():
 def test_null_handle_calls_are_rejected():
     L = mpm.lib()
     assert L.mpm_step(None, 1, None) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_set_sort_policy(None, 8, 1000, None) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_read_particles(None, None, None, None, None, None) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_read_grid(None, None, None, None) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_status(None, None, None) == mpm.MPM_ERR_INVALID_ARG
