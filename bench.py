@@ -165,6 +165,26 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst
+    # The practical HBM ceiling on this device: a plain 1 GiB device copy
+    # (read 1 GiB, write 1 GiB), median of 5, outside the timed region.
+    cp_src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    cp_ms = []
+    for _ in range(6):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cp_dst.copy_(cp_src)
+        e1.record()
+        torch.cuda.synchronize()
+        cp_ms.append(e0.elapsed_time(e1))
+    copy_gbps = 2 * cp_src.numel() * 4 / (float(np.median(cp_ms[1:])) * 1e-3) / 1e9
+    del cp_src, cp_dst
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "memory_GB": round(props.total_memory / 1e9, 1)}
+    log(f"device {device}; plain 1 GiB copy {copy_gbps:.0f} GB/s")
     kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None,
                       sorted_steps=not free_zone)
     kernels = {k: {"avg_ms": round(kavg[k], 5), "alg_bytes": kb[k],
@@ -185,10 +205,15 @@ def main():
         t1 = time.perf_counter()
         orc.step(args.cpu_steps)
         t_cpu = time.perf_counter() - t1
+        cpu_model = ""
+        try:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+        except (OSError, StopIteration):
+            pass
         cpu = {"value": round(sc.N * args.cpu_steps / t_cpu, 1), "unit": "particle-steps/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{args.cpu_steps} full step(s) of {sc.name} ({sc.N} particles, {n}^3 grid), "
-                         f"serial fp64 oracle, {t_cpu:.1f} s"}
+                         f"serial fp64 oracle, {t_cpu:.1f} s; host {cpu_model}, {os.cpu_count()} logical CPUs"}
         log(f"oracle: {t_cpu:.1f} s")
 
     out = {
@@ -212,7 +237,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "step_hbm": {"alg_bytes_per_step": step_bytes,
                      "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-                     "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+                     "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "copy_GBps": round(copy_gbps, 1),
+                     "frac_of_copy": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4)},
+        "device": device,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
