@@ -111,6 +111,7 @@ struct SimDev {
   uint32_t *bin_count;         // particles per bin in the next layout (G2P counts)
   uint32_t *stay_count;        // of those, particles already in that bin (G2P counts)
   uint32_t *bin_start, *bin_cursor;  // first slot of each bin; next slot for particles entering it
+  uint32_t *bin_stay;          // particles that stay in each bin at this sort (set by the scan)
   uint32_t *tile_sum;          // [ntiles][2] scan tile totals (particles, chunks)
   int32_t ntiles;
   // Chunk lists, one per layout (particle buffer) q: chunks[q][c] = (first
@@ -584,6 +585,7 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
         const uint32_t stay = min(st[k], c[k]);
         s.stay_count[b] = 0u;
         s.bin_start[b] = tile_base_c + run;
+        s.bin_stay[b] = stay;
         s.bin_cursor[b] = tile_base_c + run + stay;
       }
       if (!spread)
@@ -665,9 +667,28 @@ __global__ __launch_bounds__(WG) void k_scatter_init(SimDev s) {
 // the storage order, repeats from step to step and its gathers read
 // consecutive addresses.  A particle that changes bin takes the bin's atomic
 // cursor, which starts after the bin's stayers.
+// Position of the bin's stayer number j (in their previous order) in the
+// bin's new slot range.  A dense bin's stayers fill several chunks of K =
+// 2^kshift; each chunk was stored in P2G's (super-rank, window, cell) order,
+// so its rounds of 64 hold about one particle per cell, while its cells as a
+// whole may be far from balanced (particles created cell by cell stay
+// together).  For Cp = 2 or 4 full chunks (the most with blocks of at least
+// one round), the blocks are transposed -- new chunk q takes block q of every
+// old chunk -- so each new chunk draws evenly from all of them and needs
+// fewer read-modify-write passes.  Other stayers keep their order.
+__device__ __forceinline__ uint32_t stayer_slot(uint32_t j, uint32_t stay, uint32_t kshift) {
+  const uint32_t full = stay >> kshift, cap = 1u << (kshift - KMIN_SHIFT);  // blocks >= 64 particles
+  const uint32_t cp = min(full, cap) >= 4u ? 4u : (min(full, cap) >= 2u ? 2u : 1u);
+  if (cp == 1u || j >= (cp << kshift)) return j;
+  const uint32_t K = 1u << kshift, B = K / cp;
+  const uint32_t m = j >> kshift, r = j & (K - 1u), q = r / B, i = r % B;
+  return (q << kshift) + m * B + i;
+}
+
 __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
   if (s.ctr[CTR_SORT + src] == 0u) return;  // a step without a sort
   const int lane = threadIdx.x;
+  const uint32_t kshift = (uint32_t)s.chunk_shift;
   const uint64_t below = (1ull << lane) - 1ull;
   const uint32_t nch = s.ctr[CTR_NCHUNKS + src];
   const uint4 *chunks = s.chunks[src];
@@ -694,7 +715,8 @@ __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
       const uint32_t r = (uint32_t)(64 * j + lane);
       kc[j] = r < count ? s.key[start + r] : 0u;
     }
-    uint32_t base = s.bin_start[bin];
+    const uint32_t bstart = s.bin_start[bin], bstay = s.bin_stay[bin];
+    uint32_t base = 0;  // stayers before this chunk's, in the bin
     // stayers of the bin's earlier chunks (a bin's chunks are consecutive;
     // nearly always none, or a few records)
     for (uint32_t c0 = c; prev_bin == bin && c0 > 0;) {
@@ -718,7 +740,7 @@ __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
       const uint32_t key = kc[j] & ((1u << KEY_CELL_SHIFT) - 1u);
       const bool stay = valid && key == bin;
       const uint64_t sm = __ballot(stay);
-      uint32_t slot = base + (uint32_t)__popcll(sm & below);
+      uint32_t slot = bstart + stayer_slot(base + (uint32_t)__popcll(sm & below), bstay, kshift);
       base += (uint32_t)__popcll(sm);
       if (__ballot(valid && !stay) != 0ull) {
         const uint32_t mslot = wave_aggregated_increment(s.bin_cursor, key, valid && !stay);
@@ -1612,6 +1634,7 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   uint32_t *cnt = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *stay = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *bstart = (uint32_t *)take(sizeof(uint32_t) * nbins);
+  uint32_t *bstay = (uint32_t *)take(sizeof(uint32_t) * nbins);
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
   uint32_t *tiles = (uint32_t *)take(sizeof(uint32_t) * 2 * ntiles);
@@ -1658,6 +1681,7 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->bin_count = cnt;
     d->stay_count = stay;
     d->bin_start = bstart;
+    d->bin_stay = bstay;
     d->bin_cursor = cur;
     d->tile_sum = tiles;
     d->ntiles = (int32_t)ntiles;

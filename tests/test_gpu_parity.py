@@ -202,6 +202,30 @@ def test_profiled_steps_match_graph_steps():
         b.close()
 
 
+def test_batched_graphs_match_single_steps():
+    """mpm_step(17) (two 8-step graphs and one single step) against 17 calls of
+    mpm_step(1): the same steps, and the same step count."""
+    sc = scenes.random_scene(20000, 32, 66, cscale=10.0, fstretch=0.2, vscale=1.0)
+    pu.log("batched vs single-step graphs")
+    a = mpm.Simulation(sc)
+    b = mpm.Simulation(sc)
+    try:
+        a.step(17)
+        for _ in range(17):
+            b.step(1)
+        assert mpm.mpm_steps_taken(a.handle) == mpm.mpm_steps_taken(b.handle) == 17
+        ra, rb = a.read_particles(), b.read_particles()
+        for u, w in zip(ra, rb):
+            assert float((u - w).abs().max() / w.abs().max()) < 1e-5
+        ma, pa = a.read_grid()
+        mb, pb = b.read_grid()
+        assert float((ma - mb).abs().max() / mb.abs().max()) < 1e-5
+        assert float((pa - pb).abs().max() / pb.abs().max()) < 1e-5
+    finally:
+        a.close()
+        b.close()
+
+
 def test_resume_from_read_state():
     """10 steps equal 5 steps, read back, re-create from the read state, 5 steps."""
     sc = scenes.random_scene(20000, 32, 65, cscale=10.0, fstretch=0.2, vscale=1.0, per_particle_E=True)
