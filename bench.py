@@ -158,15 +158,9 @@ def main():
     active_blocks = int(pad.reshape(nb, 8, nb, 8, nb, 8).any(axis=(1, 3, 5)).sum())
     status = sim.status()
     sim.close()
-    # Calibration for the HBM-byte counters: one plain device copy of known
-    # size (read 256 MiB, write 256 MiB), outside the timed region.
-    cal_src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-    cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
-    del cal_src, cal_dst
     # The practical HBM ceiling on this device: a plain 1 GiB device copy
-    # (read 1 GiB, write 1 GiB), median of 5, outside the timed region.
+    # (read 1 GiB, write 1 GiB), median of 5, outside the timed region.  The
+    # same copy calibrates the HBM-byte counters of a rocprofv3 run.
     cp_src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
     cp_dst = torch.empty_like(cp_src)
     cp_ms = []

@@ -98,13 +98,14 @@ def main():
 
 # ------------------------------------------------------------ HBM traffic
 
-COPY_KIB = 262144  # the benchmark's calibration copy: 256 MiB read, 256 MiB written
+COPY_KIB = 1048576  # the benchmark's plain device copy: 1 GiB read, 1 GiB written
 
 
 def copy_calibration(db: str, counter: str, known_kib: float = COPY_KIB) -> float:
     """Scale factor for `counter` (FETCH_SIZE or WRITE_SIZE, KiB per dispatch):
-    known bytes of the benchmark's plain 256 MiB device copy divided by what
-    the counter reads for that copy (the copy dispatch with the largest value)."""
+    known bytes of the benchmark's plain 1 GiB device copy divided by what
+    the counter reads for that copy (the copy dispatch with the largest value:
+    no other copy in the benchmark moves as much)."""
     cur = sqlite3.connect(db).cursor()
     rows = cur.execute("select dispatch_id, kernel_name, value from counters_collection where counter_name = ?",
                        (counter,)).fetchall()
