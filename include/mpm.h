@@ -148,6 +148,21 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream);
  * MPM_ERR_INVALID_ARG. */
 int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget, void *stream);
 
+/* Fused steps: the page's fused G2P2G kernel (the G2P of one step and the
+ * P2G of the next in one pass over the particles).  enable = 1: from the
+ * next mpm_step on, a step whose successor does not sort (see
+ * mpm_set_sort_policy) runs its G2P fused with the successor's P2G, so that
+ * between sorts the state carried from step to step is x, F (or J) and the
+ * modulus only.  The successor's sort decision is then taken one step
+ * earlier, on the movers counted by the step before.  enable = 0 (the
+ * default): separate P2G and G2P kernels.  Under the default policy (sort
+ * every step) both settings run the same work.  The results equal those of
+ * separate kernels up to the order of float additions; mpm_read_particles
+ * and mpm_read_grid read the same state.  The first mpm_step after enabling
+ * captures the fused graphs (host work, no device allocation).  A host-side
+ * setting: no stream.  enable outside {0, 1} returns MPM_ERR_INVALID_ARG. */
+int mpm_set_fused_steps(mpm_sim *sim, int32_t enable);
+
 /* Copy the particle state after the last step, in creation order, into
  * caller-owned device arrays: x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)
  * for the elastic material or (N) for the fluid.  Any output may be NULL.

@@ -37,7 +37,8 @@ MPM_STATUS_NO_CONVERGE = 0x10
 MPM_STATUS_WORDS = 8
 
 # Every symbol include/mpm.h declares.
-EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_set_sort_policy", "mpm_read_particles",
+EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_set_sort_policy", "mpm_set_fused_steps",
+           "mpm_read_particles",
            "mpm_read_grid",
            "mpm_status", "mpm_steps_taken", "mpm_num_kernels", "mpm_kernel_name", "mpm_step_profiled",
            "mpm_destroy", "mpm_error_string")
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.mpm_step.restype = ctypes.c_int
     L.mpm_set_sort_policy.argtypes = [vp, i32, i64, vp]
     L.mpm_set_sort_policy.restype = ctypes.c_int
+    L.mpm_set_fused_steps.argtypes = [vp, i32]
+    L.mpm_set_fused_steps.restype = ctypes.c_int
     L.mpm_read_particles.argtypes = [vp, vp, vp, vp, vp, vp]
     L.mpm_read_particles.restype = ctypes.c_int
     L.mpm_read_grid.argtypes = [vp, vp, vp, vp]
@@ -159,6 +162,10 @@ def mpm_step(sim: int, n_steps: int, stream=None) -> None:
 def mpm_set_sort_policy(sim: int, max_interval: int, mover_budget: int, stream=None) -> None:
     _check(lib().mpm_set_sort_policy(sim, int(max_interval), int(mover_budget), _stream(stream)),
            "mpm_set_sort_policy")
+
+
+def mpm_set_fused_steps(sim: int, enable: int) -> None:
+    _check(lib().mpm_set_fused_steps(sim, int(enable)), "mpm_set_fused_steps")
 
 
 def mpm_read_particles(sim: int, x=None, v=None, C=None, F_or_J=None, stream=None) -> None:
@@ -249,6 +256,9 @@ class Simulation:
 
     def set_sort_policy(self, max_interval: int, mover_budget: int):
         mpm_set_sort_policy(self.handle, max_interval, mover_budget, self.stream)
+
+    def set_fused_steps(self, enable: bool):
+        mpm_set_fused_steps(self.handle, 1 if enable else 0)
 
     def read_particles(self):
         torch = self.torch

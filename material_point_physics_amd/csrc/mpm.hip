@@ -68,7 +68,14 @@ constexpr int NQ = 8;            // P2G work queues, one per XCD
 // padding slots (holes) are never read: every kernel walks the chunk list.
 constexpr int SLOT_ALIGN = 32;
 constexpr int NUM_KERNELS = 5;
-constexpr int STEP_BATCH = 8;    // steps per batched graph (even: a batch ends on its starting parity)
+constexpr int STEP_BATCH = 8;    // steps per batched graph (a multiple of NACC: a batch ends on its starting phase)
+// P2G accumulators.  Step n accumulates into gridA[n mod NACC] and its G2P
+// reads it.  With the fused G2P2G kernel, the P2G of step n + 1 runs while
+// other wavefronts still read step n's accumulator, so the buffer a P2G
+// clears for later use is the one of step n - 2 (both its P2G and its G2P
+// ended at least one kernel earlier): four buffers, step n clears n + 2.
+constexpr int NACC = 4;
+static_assert(STEP_BATCH % NACC == 0, "a batch must end on its starting phase");
 
 enum Ctr : int {
   CTR_NCHUNKS = 0,       // + layout parity: chunks of each layout
@@ -78,6 +85,13 @@ enum Ctr : int {
   CTR_SORT = 5,          // + buffer parity: whether the step that reads that buffer sorts
   CTR_MAX_INTERVAL = 7,  // sort policy: at least every this many steps (0 or 1: every step) ...
   CTR_MOVER_BUDGET = 8,  // ... and whenever more particles than this are outside their bins
+  // Control words for the fused G2P2G kernel, per buffer parity (the step
+  // that reads that buffer).  The step before writes them and the step
+  // itself reads them, so no kernel writes a word that its own workgroups
+  // read.
+  CTR_LOOK = 9,          // + parity: that step's P2G was done by the fused kernel before it
+  CTR_PRESET = 11,       // + parity: that step's sort decision (CTR_SORT) was taken before it
+  CTR_MOVSNAP = 13,      // movers counted by the previous step's G2P, kept for the fused kernel
   CTR_WORDS = 16,
 };
 constexpr uint8_t MOVER_TAG = 0xFF;  // P2G order tag of a particle outside its chunk's bin
@@ -119,12 +133,12 @@ struct SimDev {
   // ctr[CTR_NCHUNKS + q] chunks.  The step that reads buffer q builds
   // layout q ^ 1; its scatter walks layout q.
   uint4 *chunks[2];
-  // Grid, double-buffered by step parity (the particle buffer the step reads):
-  // the step with parity q accumulates into gridA[q] and marks the node-blocks
-  // it touched in active_flag[q]; its G2P reads gridA[q]; the next step's
-  // P2G clears them (and their flags) while it accumulates into the other.
-  uint32_t *active_flag[2];  // per node-block: 1 = touched by that step's P2G
-  float4 *gridA[2];          // P2G accumulator per node: (m, p_x, p_y, p_z)
+  // Grid accumulators, rotating by step number: step n accumulates into
+  // gridA[n mod NACC] and marks the node-blocks it touched in the same
+  // active_flag; its G2P reads them; the P2G of step n + 2 clears them (and
+  // their flags) while it accumulates into its own.
+  uint32_t *active_flag[NACC];  // per node-block: 1 = touched by that step's P2G
+  float4 *gridA[NACC];          // P2G accumulator per node: (m, p_x, p_y, p_z)
   uint32_t *ctr;
   uint32_t *status;
 };
@@ -472,13 +486,28 @@ __device__ __forceinline__ bool sort_this_step(const SimDev &s) {
   return maxint <= 1u || s.ctr[CTR_SINCE] + 1u >= maxint || s.ctr[CTR_MOVERS] > s.ctr[CTR_MOVER_BUDGET];
 }
 
+// The decision for the next step, taken by the fused kernel before that step
+// begins (it must know whether to run the next step's P2G): the same rule,
+// on the movers the previous step counted, since the current step's G2P is
+// still running.
+__device__ __forceinline__ bool sort_next_step(const SimDev &s) {
+  const uint32_t maxint = s.ctr[CTR_MAX_INTERVAL];
+  return maxint <= 1u || s.ctr[CTR_SINCE] + 1u >= maxint || s.ctr[CTR_MOVSNAP] > s.ctr[CTR_MOVER_BUDGET];
+}
+
+// The current step's decision: taken before it by the fused kernel, or now.
+__device__ __forceinline__ bool decide_sort(const SimDev &s, int src) {
+  return s.ctr[CTR_PRESET + src] != 0u ? s.ctr[CTR_SORT + src] != 0u : sort_this_step(s);
+}
+
 // Scan, phase 1: per-tile totals of (padded) slot counts and chunk counts.
 // Also takes the step's sort decision (uniform: every thread reads the same
 // counters) and publishes it for the step's other kernels.
 __global__ __launch_bounds__(WG) void k_scan_tiles(SimDev s, int src) {
   __shared__ uint32_t wsum[WG / 64];
-  const bool sort = sort_this_step(s);
-  if (blockIdx.x == 0 && threadIdx.x == 0) s.ctr[CTR_SORT + src] = sort ? 1u : 0u;
+  const bool sort = decide_sort(s, src);
+  // (a preset decision is already in the word, which other workgroups read)
+  if (blockIdx.x == 0 && threadIdx.x == 0 && s.ctr[CTR_PRESET + src] == 0u) s.ctr[CTR_SORT + src] = sort ? 1u : 0u;
   if (!sort) return;
   const uint32_t nbins = (uint32_t)s.nbins;
   const uint32_t b0 = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_PER;
@@ -517,17 +546,21 @@ __global__ __launch_bounds__(NT) void k_scan_bins(SimDev s, int lay) {
   const uint32_t shift = (uint32_t)s.chunk_shift;
   const int src = lay ^ 1;
   // The sort decision: taken here by the one-workgroup scan (no k_scan_tiles
-  // before it), else read from k_scan_tiles.  The mover count is reset for
-  // G2P to fill again (every thread has read it before the barrier).
+  // before it), else read from k_scan_tiles.  The mover count is kept for
+  // the fused kernel's decision and reset for this step's G2P to fill again
+  // (every thread has read it before the barrier).
   bool sort;
   if (NT == SCAN_SMALL_NT) {
-    sort = sort_this_step(s);
+    sort = decide_sort(s, src);
     __syncthreads();
     if (threadIdx.x == 0) s.ctr[CTR_SORT + src] = sort ? 1u : 0u;
   } else {
     sort = s.ctr[CTR_SORT + src] != 0u;
   }
-  if (t == 0 && threadIdx.x == 0) s.ctr[CTR_MOVERS] = 0u;
+  if (t == 0 && threadIdx.x == 0) {
+    s.ctr[CTR_MOVSNAP] = s.ctr[CTR_MOVERS];
+    s.ctr[CTR_MOVERS] = 0u;
+  }
   if (!sort) {
     // No sort: layout lay repeats layout src (its chunk list is copied),
     // and the bin counts are cleared for this step's G2P.
@@ -785,11 +818,260 @@ union P2GShared {
   P2GRankTables rk;
 };
 
+// Deferred deformation-gradient update with the C of the G2P before it:
+// F <- (I + dt C) F, or for the fluid J <- J det(I + dt C).
+template <int MAT>
+__device__ __forceinline__ void update_F(float *Fp, const float Cp[9], float dt) {
+  if (MAT == MPM_J_FLUID) {
+    const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
+                        dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
+    Fp[0] = Fp[0] * det3(G);
+  } else {
+    float Fn[9];
+#pragma unroll
+    for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+      for (int c2 = 0; c2 < 3; ++c2)
+        Fn[r2 * 3 + c2] = Fp[r2 * 3 + c2] + dt * (Cp[r2 * 3 + 0] * Fp[0 * 3 + c2] + Cp[r2 * 3 + 1] * Fp[1 * 3 + c2] +
+                                                  Cp[r2 * 3 + 2] * Fp[2 * 3 + c2]);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
+  }
+}
+
+// Kirchhoff stress of the fixed-corotated model, tau = 2 mu (F - R) F^T +
+// lam (J - 1) J I with R the rotation closest to F (fluid: tau = K J (J - 1) I,
+// K = E), and the APIC affine momentum matrix A = m C - dt V0 (4/dx^2) tau.
+// Returns status bits (inverted or unconverged F; fluid: J <= 0).
+template <int MAT>
+__device__ __forceinline__ uint32_t affine_momentum(const SimDev &s, const float *Fp, float E, const float Cp[9],
+                                                    float A[9]) {
+  const float mass = s.mass;
+  if (MAT == MPM_J_FLUID) {
+    const float J = Fp[0];
+    const float tau_diag = E * J * (J - 1.f);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) A[k] = mass * Cp[k] - s.stress_k * ((k % 4 == 0) ? tau_diag : 0.f);
+    return (J > 0.f) ? 0u : (uint32_t)MPM_STATUS_INVERTED;
+  }
+  const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
+  float R[9];
+  const uint32_t st = rotation_of(Fp, R);
+  const float J = det3(Fp);
+  float D[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) D[k] = 2.f * mu * (Fp[k] - R[k]);
+  const float vl = lam * (J - 1.f) * J;
+#pragma unroll
+  for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) {
+      const float tau = D[r2 * 3 + 0] * Fp[c2 * 3 + 0] + D[r2 * 3 + 1] * Fp[c2 * 3 + 1] + D[r2 * 3 + 2] * Fp[c2 * 3 + 2] +
+                        (r2 == c2 ? vl : 0.f);
+      A[r2 * 3 + c2] = mass * Cp[r2 * 3 + c2] - s.stress_k * tau;
+    }
+  return st;
+}
+
+// Base node b = floor(x/dx - 1/2), fractional offset f and quadratic
+// B-spline weights w[axis][o] of a position.
+__device__ __forceinline__ void particle_weights(const float xp[3], float fn, int b[3], float f[3], float w[3][3]) {
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float xn = xp[a] * fn;
+    b[a] = base_node(xn);
+    f[a] = xn - (float)b[a];
+    bspline_weights(f[a], w[a]);
+  }
+}
+
+// APIC momentum at stencil node o: m v + A (o - f) dx = q0 + Ad o.
+__device__ __forceinline__ void momentum_terms(float mass, float dx, const float vp[3], const float A[9],
+                                               const float f[3], float q0[3], float Ad[9]) {
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    q0[a] = mass * vp[a] - dx * (A[a * 3 + 0] * f[0] + A[a * 3 + 1] * f[1] + A[a * 3 + 2] * f[2]);
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) Ad[a * 3 + c2] = dx * A[a * 3 + c2];
+  }
+}
+
+// One particle's 27 node contributions (w m, w (q0 + Ad o)) added to an LDS
+// window, li0 = the window index of stencil offset 0: plain read-modify-
+// writes, which the caller makes conflict-free across the wavefront's lanes.
+__device__ __forceinline__ void deposit_window(float4 *win, int li0, float w[3][3], float q0[3], float Ad[9],
+                                               float mass) {
+  // Form the 27 node contributions here rather than keeping all 108 of them
+  // live across the caller's pass loop (register pressure limits occupancy).
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    __asm__ __volatile__("" : "+v"(q0[k]), "+v"(w[0][k]), "+v"(w[1][k]), "+v"(w[2][k]));
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) __asm__ __volatile__("" : "+v"(Ad[k]));
+  // Momentum at node o is q0 + Ad (ox, oy, oz): running sums along z, y and
+  // x (one add per component per step; no multiplications by the constant
+  // offsets, which IEEE rules keep the compiler from folding).
+  float qz[3] = {q0[0], q0[1], q0[2]};
+#pragma unroll
+  for (int oz = 0; oz < 3; ++oz) {
+    if (oz > 0) {
+      qz[0] += Ad[2];
+      qz[1] += Ad[5];
+      qz[2] += Ad[8];
+    }
+    float qy[3] = {qz[0], qz[1], qz[2]};
+#pragma unroll
+    for (int oy = 0; oy < 3; ++oy) {
+      if (oy > 0) {
+        qy[0] += Ad[1];
+        qy[1] += Ad[4];
+        qy[2] += Ad[7];
+      }
+      const float wyz = w[1][oy] * w[2][oz];
+      float qx[3] = {qy[0], qy[1], qy[2]};
+#pragma unroll
+      for (int ox = 0; ox < 3; ++ox) {
+        if (ox > 0) {
+          qx[0] += Ad[0];
+          qx[1] += Ad[3];
+          qx[2] += Ad[6];
+        }
+        const float wt = w[0][ox] * wyz;
+        const int li = li0 + (oz * PW + oy) * PW + ox;
+        float4 g = win[li];
+        g.x = fmaf(wt, mass, g.x);
+        g.y = fmaf(wt, qx[0], g.y);
+        g.z = fmaf(wt, qx[1], g.z);
+        g.w = fmaf(wt, qx[2], g.w);
+        win[li] = g;
+        // keep this read-modify-write ahead of the next one in issue order
+        __asm__ __volatile__("" ::: "memory");
+      }
+    }
+  }
+}
+
+// Clear accumulator a (that of the step two before the one accumulating
+// now: its P2G and its G2P have ended): the node-blocks it marked, and their
+// marks.  Workgroup b takes blocks G-1-b, 2G-1-b, ... (G workgroups; counted
+// from the last one because in a small scene the first ones have chunks and
+// the flag loads would delay them); the stores drain while it works on its
+// chunks.  One wavefront per workgroup.
+__device__ __forceinline__ void clear_accumulator(const SimDev &s, int a) {
+  const int lane = threadIdx.x;
+  for (uint32_t blk = gridDim.x - 1u - blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+    if (s.active_flag[a][blk] == 0u) continue;
+    float4 *g = s.gridA[a] + ((size_t)blk << 9);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[k * 64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane == 0) s.active_flag[a][blk] = 0u;
+  }
+}
+
+// Flush: the sum of the NWIN windows (window origin = first base node of
+// the bin, ox0, oy0, oz0), one native global float atomic per nonzero value
+// (adding zero changes nothing) into accumulator a, in whole cubes: lane =
+// (cube of the pair, node in cube, channel), so each atomic instruction
+// covers two cubes = two full 128-byte lines (the memory-side atomic units
+// work per line).  A window cube's node index is separable per axis; with
+// the window origin a multiple of 4, the axis terms of cube coordinate 0..2
+// are uniform (relative to the origin's node-block: at most one block step
+// per axis), so a lane's address is a uniform block pointer plus the cube
+// offset of its half of the wavefront plus its node and channel.  Then the
+// (at most 2x2x2) node-blocks the window overlaps are marked: the P2G two
+// steps later clears exactly these (and mpm_read_grid reads them).  A marked
+// block whose nodes got no mass is cleared for nothing, which is harmless.
+// Plain stores: every writer stores the same value.
+__device__ __forceinline__ void flush_windows(const SimDev &s, const float4 *win, int ox0, int oy0, int oz0, int a) {
+  const int lane = threadIdx.x;
+  {
+    const int h = lane >> 5, j = (lane >> 2) & 7, chn = lane & 3;
+    const int jx = j & 1, jy = (j >> 1) & 1, jz = j >> 2;
+    const uint32_t nbs = (uint32_t)s.nb;
+    uint32_t XC[3], YC[3], ZC[3];  // node offsets of cube coordinate 0..2 per axis
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t ux = (uint32_t)(ox0 >> 1) + (uint32_t)k, uy = (uint32_t)(oy0 >> 1) + (uint32_t)k,
+                     uz = (uint32_t)(oz0 >> 1) + (uint32_t)k;
+      XC[k] = (((ux >> 2) - (uint32_t)(ox0 >> 3)) << 9) + ((ux & 3u) << 3);
+      YC[k] = (((uy >> 2) - (uint32_t)(oy0 >> 3)) * nbs << 9) + ((uy & 3u) << 5);
+      ZC[k] = (((uz >> 2) - (uint32_t)(oz0 >> 3)) * nbs * nbs << 9) + ((uz & 3u) << 7);
+    }
+    float4 *gblk = s.gridA[a] +
+                   (((size_t)(oz0 >> 3) * nbs + (size_t)(oy0 >> 3)) * nbs + (size_t)(ox0 >> 3)) * 512u;
+    const uint32_t lane_b = (uint32_t)(16 * j + 4 * chn);
+    const float *winl = reinterpret_cast<const float *>(win) + 4 * ((jz * PW + jy) * PW + jx) + chn;
+    // the window reaches past the grid only at the grid's upper faces
+    const bool interior = ox0 + PW <= s.n && oy0 + PW <= s.n && oz0 + PW <= s.n;
+#pragma unroll
+    for (int t = 0; t < 14; ++t) {
+      const int c0 = 2 * t, c1 = 2 * t + 1;  // the two cubes of this step
+      const int x0 = c0 % 3, y0 = (c0 / 3) % 3, z0 = c0 / 9;
+      const int x1 = c1 % 3, y1 = (c1 / 3) % 3, z1 = (c1 < 27) ? c1 / 9 : 0;
+      const uint32_t o0 = XC[x0] + YC[y0] + ZC[z0], o1 = XC[x1] + YC[y1] + ZC[z1];
+      const int kw0 = ((2 * z0) * PW + 2 * y0) * PW + 2 * x0, kw1 = ((2 * z1) * PW + 2 * y1) * PW + 2 * x1;
+      if (c1 >= 27 && h) continue;
+      const int kw = h ? kw1 : kw0;
+      float val = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWIN; ++w) val += winl[4 * (kw + w * PW3)];
+      bool inb = val != 0.f;
+      if (!interior) {
+        const int cx = h ? x1 : x0, cy = h ? y1 : y0, cz = h ? z1 : z0;
+        inb = inb && ox0 + 2 * cx + jx < s.n && oy0 + 2 * cy + jy < s.n && oz0 + 2 * cz + jz < s.n;
+      }
+      if (inb) unsafeAtomicAdd(&at_byte(reinterpret_cast<float *>(gblk), 16u * (h ? o1 : o0) + lane_b), val);
+    }
+  }
+  if (lane < 8) {
+    const int bx = (ox0 >> 3) + (lane & 1), by = (oy0 >> 3) + ((lane >> 1) & 1), bz = (oz0 >> 3) + (lane >> 2);
+    const int ex = min(ox0 + PW - 1, s.n - 1) >> 3, ey = min(oy0 + PW - 1, s.n - 1) >> 3,
+              ez = min(oz0 + PW - 1, s.n - 1) >> 3;
+    if (bx <= ex && by <= ey && bz <= ez)
+      s.active_flag[a][((uint32_t)bz * (uint32_t)s.nb + (uint32_t)by) * (uint32_t)s.nb + (uint32_t)bx] = 1u;
+  }
+}
+
+// A particle whose stencil is outside its chunk's window (only in steps
+// without a sort; rare) deposits its 27 nodes into accumulator a with direct
+// global atomics and marks the node-blocks its stencil touches, for the
+// clear two steps later and the grid readback.  Momentum at node o is
+// q0 + Ad o.
+__device__ __forceinline__ void deposit_global(const SimDev &s, int a, const int b[3], const float w[3][3],
+                                               const float q0[3], const float Ad[9]) {
+  const float mass = s.mass;
+#pragma unroll 1
+  for (int oz = 0; oz < 3; ++oz)
+#pragma unroll 1
+    for (int oy = 0; oy < 3; ++oy)
+#pragma unroll 1
+      for (int ox = 0; ox < 3; ++ox) {
+        const int gx = b[0] + ox, gy = b[1] + oy, gz = b[2] + oz;
+        if (gx < 0 || gy < 0 || gz < 0 || gx >= s.n || gy >= s.n || gz >= s.n) continue;
+        const float wt = w[0][ox] * w[1][oy] * w[2][oz];
+        float *g = reinterpret_cast<float *>(s.gridA[a] + node_index(s, gx, gy, gz));
+        unsafeAtomicAdd(g + 0, wt * mass);
+        unsafeAtomicAdd(g + 1, wt * (q0[0] + Ad[0] * ox + Ad[1] * oy + Ad[2] * oz));
+        unsafeAtomicAdd(g + 2, wt * (q0[1] + Ad[3] * ox + Ad[4] * oy + Ad[5] * oz));
+        unsafeAtomicAdd(g + 3, wt * (q0[2] + Ad[6] * ox + Ad[7] * oy + Ad[8] * oz));
+      }
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k) {
+    const int gx = min(b[0] + 2 * (k & 1), s.n - 1), gy = min(b[1] + ((k >> 1) & 1) * 2, s.n - 1),
+              gz = min(b[2] + (k >> 2) * 2, s.n - 1);
+    if (gx < 0 || gy < 0 || gz < 0) continue;
+    s.active_flag[a][((uint32_t)(gz >> 3) * (uint32_t)s.nb + (uint32_t)(gy >> 3)) * (uint32_t)s.nb +
+                     (uint32_t)(gx >> 3)] = 1u;
+  }
+}
+
 // The P2G of one step.  FREE: a step without a sort (free-zone policy), with
 // the paths for particles outside their chunk's bin; the per-step-sort
 // instance has none of that code.
 template <int MAT, bool HAS_E, bool FREE>
-__device__ __forceinline__ void p2g_step(const SimDev &s, int src, P2GShared &sm, uint32_t *order, uint8_t *ordtag) {
+__device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GShared &sm, uint32_t *order,
+                                         uint8_t *ordtag) {
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
   const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
@@ -831,22 +1113,7 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, P2GShared &sm
       }
     }
   };
-  // Clear the previous step's accumulator (the other parity): the
-  // node-blocks it marked, and their marks; its G2P has finished reading
-  // them, and the next step accumulates there.  Workgroup b takes blocks
-  // G-1-b, 2G-1-b, ... (G workgroups; counted from the last one because in
-  // a small scene the first ones have chunks and the flag loads would delay
-  // them); the stores drain while it works on its chunks.
-  {
-    const int prev = src ^ 1;
-    for (uint32_t blk = gridDim.x - 1u - blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
-      if (s.active_flag[prev][blk] == 0u) continue;
-      float4 *g = s.gridA[prev] + ((size_t)blk << 9);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) g[k * 64 + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (lane == 0) s.active_flag[prev][blk] = 0u;
-    }
-  }
+  clear_accumulator(s, (acc + 2) & (NACC - 1));
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
   if (qbeg + wq < qend) {
     ch_next = chunks[qbeg + wq];
@@ -1008,83 +1275,24 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, P2GShared &sm
         stream_store(at_byte(in.id, io), at_byte(out.id, od));
       }
 
-      float tau_diag = 0.f;
-      float tau[9];
-      if (MAT == MPM_J_FLUID) {
-        float J = stream_load(at_byte(in.F, io));
-        if (pending) {
-          const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
-                              dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
-          J = J * det3(G);
-        }
-        const float K = HAS_E ? at_byte(in.E, io) : s.E;
-        if (valid) {
-          stream_store(J, at_byte(out.F, od));
-          if (HAS_E) stream_store(K, at_byte(out.E, od));
-          if (!(J > 0.f)) flag_status(s, MPM_STATUS_INVERTED, 2);
-        }
-        tau_diag = K * J * (J - 1.f);
-      } else {
-        float Fp[9];
+      // Deferred deformation-gradient update, stress, APIC momentum.
+      float Fp[MAT == MPM_J_FLUID ? 1 : 9];
 #pragma unroll
-        for (int k = 0; k < 9; ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
-        if (pending) {
-          float Fn[9];
+      for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
+      if (pending) update_F<MAT>(Fp, Cp, dt);
+      const float E = HAS_E ? at_byte(in.E, io) : s.E;
+      if (valid) {
 #pragma unroll
-          for (int r2 = 0; r2 < 3; ++r2)
-#pragma unroll
-            for (int c2 = 0; c2 < 3; ++c2)
-              Fn[r2 * 3 + c2] = Fp[r2 * 3 + c2] + dt * (Cp[r2 * 3 + 0] * Fp[0 * 3 + c2] + Cp[r2 * 3 + 1] * Fp[1 * 3 + c2] +
-                                                        Cp[r2 * 3 + 2] * Fp[2 * 3 + c2]);
-#pragma unroll
-          for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
-        }
-        const float E = HAS_E ? at_byte(in.E, io) : s.E;
-        if (valid) {
-#pragma unroll
-          for (int k = 0; k < 9; ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
-          if (HAS_E) stream_store(E, at_byte(out.E, od));
-        }
-        const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
-        float R[9];
-        const uint32_t st = rotation_of(Fp, R);
-        if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
-        const float J = det3(Fp);
-        float D[9];
-#pragma unroll
-        for (int k = 0; k < 9; ++k) D[k] = 2.f * mu * (Fp[k] - R[k]);
-        const float vl = lam * (J - 1.f) * J;
-#pragma unroll
-        for (int r2 = 0; r2 < 3; ++r2)
-#pragma unroll
-          for (int c2 = 0; c2 < 3; ++c2)
-            tau[r2 * 3 + c2] = D[r2 * 3 + 0] * Fp[c2 * 3 + 0] + D[r2 * 3 + 1] * Fp[c2 * 3 + 1] +
-                               D[r2 * 3 + 2] * Fp[c2 * 3 + 2] + (r2 == c2 ? vl : 0.f);
+        for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
+        if (HAS_E) stream_store(E, at_byte(out.E, od));
       }
-      // APIC affine momentum matrix A = m C - dt V0 (4/dx^2) tau.
       float A[9];
-#pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        const float t = (MAT == MPM_J_FLUID) ? ((k % 4 == 0) ? tau_diag : 0.f) : tau[k];
-        A[k] = mass * Cp[k] - s.stress_k * t;
-      }
+      const uint32_t st = affine_momentum<MAT>(s, Fp, E, Cp, A);
+      if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
       int b[3];
-      float f[3], w[3][3];
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        const float xn = xp[a] * fn;
-        b[a] = base_node(xn);
-        f[a] = xn - (float)b[a];
-        bspline_weights(f[a], w[a]);
-      }
-      // momentum at node o: m v + A (o - f) dx
-      float q0[3], Ad[9];
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        q0[a] = mass * vp[a] - dx * (A[a * 3 + 0] * f[0] + A[a * 3 + 1] * f[1] + A[a * 3 + 2] * f[2]);
-#pragma unroll
-        for (int c2 = 0; c2 < 3; ++c2) Ad[a * 3 + c2] = dx * A[a * 3 + c2];
-      }
+      float f[3], w[3][3], q0[3], Ad[9];
+      particle_weights(xp, fn, b, f, w);
+      momentum_terms(mass, dx, vp, A, f, q0, Ad);
       const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
                 lz = min(max(b[2] - oz0, 0), CB - 1);
       const int li0 = (int)(tag % NWIN) * PW3 + (lz * PW + ly) * PW + lx;
@@ -1108,166 +1316,33 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, P2GShared &sm
         }
         pass_id = (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
       }
-      // A mover (only in a step without a sort; rare) deposits its 27 nodes
-      // with direct global atomics and marks the node-blocks its stencil
-      // touches, for the next step's clear and the grid readback.
-      if (FREE && valid && mov) {
-#pragma unroll 1
-        for (int oz = 0; oz < 3; ++oz)
-#pragma unroll 1
-          for (int oy = 0; oy < 3; ++oy)
-#pragma unroll 1
-            for (int ox = 0; ox < 3; ++ox) {
-              const int gx = b[0] + ox, gy = b[1] + oy, gz = b[2] + oz;
-              if (gx < 0 || gy < 0 || gz < 0 || gx >= s.n || gy >= s.n || gz >= s.n) continue;
-              const float wt = w[0][ox] * w[1][oy] * w[2][oz];
-              float *g = reinterpret_cast<float *>(s.gridA[src] + node_index(s, gx, gy, gz));
-              unsafeAtomicAdd(g + 0, wt * mass);
-              unsafeAtomicAdd(g + 1, wt * (q0[0] + Ad[0] * ox + Ad[1] * oy + Ad[2] * oz));
-              unsafeAtomicAdd(g + 2, wt * (q0[1] + Ad[3] * ox + Ad[4] * oy + Ad[5] * oz));
-              unsafeAtomicAdd(g + 3, wt * (q0[2] + Ad[6] * ox + Ad[7] * oy + Ad[8] * oz));
-            }
-#pragma unroll 1
-        for (int k = 0; k < 8; ++k) {
-          const int gx = min(b[0] + 2 * (k & 1), s.n - 1), gy = min(b[1] + ((k >> 1) & 1) * 2, s.n - 1),
-                    gz = min(b[2] + (k >> 2) * 2, s.n - 1);
-          if (gx < 0 || gy < 0 || gz < 0) continue;
-          s.active_flag[src][((uint32_t)(gz >> 3) * (uint32_t)s.nb + (uint32_t)(gy >> 3)) * (uint32_t)s.nb +
-                             (uint32_t)(gx >> 3)] = 1u;
-        }
-      }
+      // A mover (only in a step without a sort; rare) deposits directly.
+      if (FREE && valid && mov) deposit_global(s, acc, b, w, q0, Ad);
       bool todo = inwin;
       for (uint32_t pnow = 0;; ++pnow) {
         // (occurrence indices of a key are 0, 1, ..., so no lane waits for a
         // pass after an empty one)
         if (__ballot(todo && pass_id == pnow) == 0ull) break;
         if (todo && pass_id == pnow) {
-          // Form the 27 node contributions here rather than keeping all 108 of
-          // them live across the pass loop (register pressure limits occupancy).
-#pragma unroll
-          for (int k = 0; k < 3; ++k) {
-            __asm__ __volatile__("" : "+v"(q0[k]), "+v"(w[0][k]), "+v"(w[1][k]), "+v"(w[2][k]));
-          }
-#pragma unroll
-          for (int k = 0; k < 9; ++k) __asm__ __volatile__("" : "+v"(Ad[k]));
-          // Momentum at node o is q0 + Ad (ox, oy, oz): running sums along z,
-          // y and x (one add per component per step; no multiplications by
-          // the constant offsets, which IEEE rules keep the compiler from
-          // folding).
-          float qz[3] = {q0[0], q0[1], q0[2]};
-#pragma unroll
-          for (int oz = 0; oz < 3; ++oz) {
-            if (oz > 0) {
-              qz[0] += Ad[2];
-              qz[1] += Ad[5];
-              qz[2] += Ad[8];
-            }
-            float qy[3] = {qz[0], qz[1], qz[2]};
-#pragma unroll
-            for (int oy = 0; oy < 3; ++oy) {
-              if (oy > 0) {
-                qy[0] += Ad[1];
-                qy[1] += Ad[4];
-                qy[2] += Ad[7];
-              }
-              const float wyz = w[1][oy] * w[2][oz];
-              float qx[3] = {qy[0], qy[1], qy[2]};
-#pragma unroll
-              for (int ox = 0; ox < 3; ++ox) {
-                if (ox > 0) {
-                  qx[0] += Ad[0];
-                  qx[1] += Ad[3];
-                  qx[2] += Ad[6];
-                }
-                const float wt = w[0][ox] * wyz;
-                const int li = li0 + (oz * PW + oy) * PW + ox;
-                float4 g = sm.win[li];
-                g.x = fmaf(wt, mass, g.x);
-                g.y = fmaf(wt, qx[0], g.y);
-                g.z = fmaf(wt, qx[1], g.z);
-                g.w = fmaf(wt, qx[2], g.w);
-                sm.win[li] = g;
-                // keep this read-modify-write ahead of the next one in issue order
-                __asm__ __volatile__("" ::: "memory");
-              }
-            }
-          }
+          deposit_window(sm.win, li0, w, q0, Ad, mass);
           todo = false;
         }
       }
     }
     __syncthreads();
-
-    // Flush: the windows' sum, one native global float atomic per nonzero
-    // value (adding zero changes nothing), in whole cubes: lane = (cube of
-    // the pair, node in cube, channel), so each atomic instruction covers two
-    // cubes = two full 128-byte lines (the memory-side atomic units work per
-    // line).  A window cube's node index is separable per axis; with the
-    // window origin a multiple of 4, the axis terms of cube coordinate 0..2
-    // are uniform (relative to the origin's node-block: at most one block
-    // step per axis), so a lane's address is a uniform block pointer plus the
-    // cube offset of its half of the wavefront plus its node and channel.
-    {
-      const int h = lane >> 5, j = (lane >> 2) & 7, chn = lane & 3;
-      const int jx = j & 1, jy = (j >> 1) & 1, jz = j >> 2;
-      const uint32_t nbs = (uint32_t)s.nb;
-      uint32_t XC[3], YC[3], ZC[3];  // node offsets of cube coordinate 0..2 per axis
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const uint32_t ux = (uint32_t)(ox0 >> 1) + (uint32_t)k, uy = (uint32_t)(oy0 >> 1) + (uint32_t)k,
-                       uz = (uint32_t)(oz0 >> 1) + (uint32_t)k;
-        XC[k] = (((ux >> 2) - (uint32_t)(ox0 >> 3)) << 9) + ((ux & 3u) << 3);
-        YC[k] = (((uy >> 2) - (uint32_t)(oy0 >> 3)) * nbs << 9) + ((uy & 3u) << 5);
-        ZC[k] = (((uz >> 2) - (uint32_t)(oz0 >> 3)) * nbs * nbs << 9) + ((uz & 3u) << 7);
-      }
-      float4 *gblk = s.gridA[src] +
-                     (((size_t)(oz0 >> 3) * nbs + (size_t)(oy0 >> 3)) * nbs + (size_t)(ox0 >> 3)) * 512u;
-      const uint32_t lane_b = (uint32_t)(16 * j + 4 * chn);
-      const float *winl = reinterpret_cast<const float *>(sm.win) + 4 * ((jz * PW + jy) * PW + jx) + chn;
-      // the window reaches past the grid only at the grid's upper faces
-      const bool interior = ox0 + PW <= s.n && oy0 + PW <= s.n && oz0 + PW <= s.n;
-#pragma unroll
-      for (int t = 0; t < 14; ++t) {
-        const int c0 = 2 * t, c1 = 2 * t + 1;  // the two cubes of this step
-        const int x0 = c0 % 3, y0 = (c0 / 3) % 3, z0 = c0 / 9;
-        const int x1 = c1 % 3, y1 = (c1 / 3) % 3, z1 = (c1 < 27) ? c1 / 9 : 0;
-        const uint32_t o0 = XC[x0] + YC[y0] + ZC[z0], o1 = XC[x1] + YC[y1] + ZC[z1];
-        const int kw0 = ((2 * z0) * PW + 2 * y0) * PW + 2 * x0, kw1 = ((2 * z1) * PW + 2 * y1) * PW + 2 * x1;
-        if (c1 >= 27 && h) continue;
-        const int kw = h ? kw1 : kw0;
-        float val = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWIN; ++w) val += winl[4 * (kw + w * PW3)];
-        bool inb = val != 0.f;
-        if (!interior) {
-          const int cx = h ? x1 : x0, cy = h ? y1 : y0, cz = h ? z1 : z0;
-          inb = inb && ox0 + 2 * cx + jx < s.n && oy0 + 2 * cy + jy < s.n && oz0 + 2 * cz + jz < s.n;
-        }
-        if (inb) unsafeAtomicAdd(&at_byte(reinterpret_cast<float *>(gblk), 16u * (h ? o1 : o0) + lane_b), val);
-      }
-    }
-    // Mark the (at most 2x2x2) node-blocks the window overlaps: the next
-    // step's P2G clears exactly these (and mpm_read_grid reads them).  A
-    // marked block whose nodes got no mass is cleared for nothing, which is
-    // harmless.  Plain stores: every writer stores the same value.
-    if (lane < 8) {
-      const int bx = (ox0 >> 3) + (lane & 1), by = (oy0 >> 3) + ((lane >> 1) & 1), bz = (oz0 >> 3) + (lane >> 2);
-      const int ex = min(ox0 + PW - 1, s.n - 1) >> 3, ey = min(oy0 + PW - 1, s.n - 1) >> 3,
-                ez = min(oz0 + PW - 1, s.n - 1) >> 3;
-      if (bx <= ex && by <= ey && bz <= ez)
-        s.active_flag[src][((uint32_t)bz * (uint32_t)s.nb + (uint32_t)by) * (uint32_t)s.nb + (uint32_t)bx] = 1u;
-    }
+    flush_windows(s, sm.win, ox0, oy0, oz0, acc);
     __syncthreads();
   }
 }
 
 template <int MAT, bool HAS_E>
-__global__ __launch_bounds__(64) void k_p2g(SimDev s, int src) {
+__global__ __launch_bounds__(64) void k_p2g(SimDev s, int src, int acc) {
   __shared__ P2GShared sm;
   __shared__ uint32_t order[KMAX];  // source index of each processing position
   __shared__ uint8_t ordtag[KMAX];  // super-rank * NWIN + window of each position (or MOVER_TAG)
-  if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false>(s, src, sm, order, ordtag);
-  else p2g_step<MAT, HAS_E, true>(s, src, sm, order, ordtag);
+  if (s.ctr[CTR_LOOK + src] != 0u) return;  // done by the fused kernel of the step before
+  if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false>(s, src, acc, sm, order, ordtag);
+  else p2g_step<MAT, HAS_E, true>(s, src, acc, sm, order, ordtag);
 }
 
 // The grid update -- v = p/m + dt g where m > 0, sticky walls -- is
@@ -1294,57 +1369,198 @@ __device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int
 // occupy the consecutive slots [start, start + count) (P2G stored them
 // there), and all of their stencils lie in the bin's 6^3-node window, which
 // is loaded once into LDS; each particle then gathers its 27 nodes from LDS.
-// Writes x, v, C in place and the next step's bin key and count.
-template <int MAT>
-__global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
-  __shared__ float4 win[PW3];
-  const PBuf out = s.buf[src ^ 1];
+
+// Window load in whole cubes (one 128-byte line each): lane = (cube, node in
+// cube), 8 cubes per load instruction, 4 instructions.  This lane's window
+// node of instruction t, packed wx | wy << 8 | wz << 16 (all ones when cube
+// 8t + lane / 8 is past the 27th).
+__device__ __forceinline__ void window_lanes(uint32_t wpack[4]) {
   const int lane = threadIdx.x;
-  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
-  const float fn = s.fn;
-  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
-  const uint32_t nch = s.ctr[CTR_NCHUNKS + (src ^ 1)];
-  uint4 *chunks = s.chunks[src ^ 1];
-  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
-  // Window load in whole cubes (one 128-byte line each): lane = (cube, node
-  // in cube), 8 cubes per load instruction, 4 instructions.  This lane's
-  // window node of instruction t, packed wx | wy << 8 | wz << 16 (all ones
-  // when cube 8t + lane / 8 is past the 27th).
-  uint32_t wpack[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int cb = 8 * t + (lane >> 3), j = lane & 7;
     const int wx = 2 * (cb % 3) + (j & 1), wy = 2 * ((cb / 3) % 3) + ((j >> 1) & 1), wz = 2 * (cb / 9) + (j >> 2);
     wpack[t] = cb < 27 ? (uint32_t)(wx | (wy << 8) | (wz << 16)) : 0xFFFFFFFFu;
   }
+}
+
+// Requests the accumulator values (m, p) of the window at (ox0, oy0, oz0)
+// from accumulator a; nodes outside the grid read as zero.
+__device__ __forceinline__ void fetch_window(const SimDev &s, int a, int ox0, int oy0, int oz0, const uint32_t wpack[4],
+                                             float4 acc[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int gx = ox0 + (int)(wpack[t] & 0xFFu), gy = oy0 + (int)((wpack[t] >> 8) & 0xFFu),
+              gz = oz0 + (int)((wpack[t] >> 16) & 0xFFu);
+    if (wpack[t] != 0xFFFFFFFFu && gx < s.n && gy < s.n && gz < s.n) acc[t] = s.gridA[a][node_index(s, gx, gy, gz)];
+  }
+}
+
+// Converts fetched window values to grid velocities (the grid update) in LDS.
+__device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4], const uint32_t wpack[4], int ox0,
+                                             int oy0, int oz0, float4 *win) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (wpack[t] == 0xFFFFFFFFu) continue;
+    const int wx = (int)(wpack[t] & 0xFFu), wy = (int)((wpack[t] >> 8) & 0xFFu), wz = (int)((wpack[t] >> 16) & 0xFFu);
+    const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+    win[(wz * PW + wy) * PW + wx] =
+        (gx < s.n && gy < s.n && gz < s.n) ? grid_velocity(s, acc[t], gx, gy, gz) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Gather of one particle at xp: v = sum w v_i and B = sum w v_i (o - f)^T
+// (C = 4/dx^2 B dx, applied by the caller), from the velocity window of the
+// bin at (ox0, oy0, oz0), or from accumulator a with the grid update for a
+// particle whose stencil is outside the window (it left the chunk's bin
+// since the last sort: only in steps without a sort; rare).
+__device__ __forceinline__ void gather_particle(const SimDev &s, const float4 *win, int a, const float xp[3], int ox0,
+                                                int oy0, int oz0, float v[3], float B[9]) {
+  int b[3];
+  float w[3][3], d[3][3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const float xn = xp[k] * s.fn;
+    b[k] = base_node(xn);
+    const float f = xn - (float)b[k];
+    bspline_weights(f, w[k]);
+    d[k][0] = -f;
+    d[k][1] = 1.f - f;
+    d[k][2] = 2.f - f;
+  }
+  const bool outside = b[0] - ox0 < 0 || b[0] - ox0 >= CB || b[1] - oy0 < 0 || b[1] - oy0 >= CB || b[2] - oz0 < 0 ||
+                       b[2] - oz0 >= CB;
+  const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
+            lz = min(max(b[2] - oz0, 0), CB - 1);
+  const int li0 = (lz * PW + ly) * PW + lx;
+  // The quadratic B-spline's first moment sum_o w_o (o - f) = 0 gives the
+  // columns of B as B_a = sum w o_a v_i - f_a v.  Reduced along x first for
+  // each (y, z) row: S = sum_x w_x v_i and U = sum_x w_x ox v_i; offsets
+  // equal to zero add nothing, so rows with oy = 0 (oz = 0) skip the y (z)
+  // column.
+  const float w2x = 2.f * w[0][2];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) v[k] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) B[k] = 0.f;
+  if (outside) {
+    // node rows of three, their loads issued together
+#pragma unroll 1
+    for (int r = 0; r < 9; ++r) {
+      const int oy = r % 3, oz = r / 3;
+      const int gy = b[1] + oy, gz = b[2] + oz;
+      float4 acc[3];
+#pragma unroll
+      for (int ox = 0; ox < 3; ++ox) {
+        const int gx = b[0] + ox;
+        acc[ox] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gx >= 0 && gy >= 0 && gz >= 0 && gx < s.n && gy < s.n && gz < s.n)
+          acc[ox] = s.gridA[a][node_index(s, gx, gy, gz)];
+      }
+#pragma unroll
+      for (int ox = 0; ox < 3; ++ox) {
+        const float4 g = grid_velocity(s, acc[ox], b[0] + ox, gy, gz);
+        const float wt = w[0][ox] * w[1][oy] * w[2][oz];
+        const float vel[3] = {g.x, g.y, g.z};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          v[k] = fmaf(wt, vel[k], v[k]);
+          B[k * 3 + 0] = fmaf(wt * (float)ox, vel[k], B[k * 3 + 0]);
+          B[k * 3 + 1] = fmaf(wt * (float)oy, vel[k], B[k * 3 + 1]);
+          B[k * 3 + 2] = fmaf(wt * (float)oz, vel[k], B[k * 3 + 2]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int oz = 0; oz < 3; ++oz)
+#pragma unroll
+      for (int oy = 0; oy < 3; ++oy) {
+        float S[3], U[3];
+        const float4 g0 = win[li0 + (oz * PW + oy) * PW + 0];
+        const float4 g1 = win[li0 + (oz * PW + oy) * PW + 1];
+        const float4 g2 = win[li0 + (oz * PW + oy) * PW + 2];
+        S[0] = w[0][0] * g0.x;
+        S[1] = w[0][0] * g0.y;
+        S[2] = w[0][0] * g0.z;
+        U[0] = w[0][1] * g1.x;
+        U[1] = w[0][1] * g1.y;
+        U[2] = w[0][1] * g1.z;
+        S[0] = fmaf(w[0][1], g1.x, S[0]);
+        S[1] = fmaf(w[0][1], g1.y, S[1]);
+        S[2] = fmaf(w[0][1], g1.z, S[2]);
+        S[0] = fmaf(w[0][2], g2.x, S[0]);
+        S[1] = fmaf(w[0][2], g2.y, S[1]);
+        S[2] = fmaf(w[0][2], g2.z, S[2]);
+        U[0] = fmaf(w2x, g2.x, U[0]);
+        U[1] = fmaf(w2x, g2.y, U[1]);
+        U[2] = fmaf(w2x, g2.z, U[2]);
+        const float wyz = w[1][oy] * w[2][oz];
+        const float wyz2 = wyz + wyz;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          v[k] = fmaf(wyz, S[k], v[k]);
+          B[k * 3 + 0] = fmaf(wyz, U[k], B[k * 3 + 0]);
+          if (oy > 0) B[k * 3 + 1] = fmaf(oy == 1 ? wyz : wyz2, S[k], B[k * 3 + 1]);
+          if (oz > 0) B[k * 3 + 2] = fmaf(oz == 1 ? wyz : wyz2, S[k], B[k * 3 + 2]);
+        }
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) B[k * 3 + c2] = fmaf(d[c2][0], v[k], B[k * 3 + c2]);  // d[c2][0] = -f_c2
+}
+
+// Advection x + dt v, clamped to the box; status bits for a clamp or a
+// non-finite value (of x, v or C = c_scale B, which the caller stores).
+__device__ __forceinline__ void advect(const SimDev &s, const float xp[3], const float v[3], const float B[9],
+                                       float xn[3], float C[9], bool &clamped, bool &nonfinite) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float xa = xp[k] + s.dt * v[k];
+    if (!isfinite(xa) || !isfinite(v[k])) nonfinite = true;
+    if (xa < s.lo || xa > s.hi) clamped = true;
+    xn[k] = fminf(fmaxf(xa, s.lo), s.hi);
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    C[k] = s.c_scale * B[k];
+    if (!isfinite(C[k])) nonfinite = true;
+  }
+}
+
+// The G2P of the step that accumulated into a: particles of layout lay (the
+// one P2G built), x, v, C written in place, and the next step's bin keys and
+// counts.
+template <int MAT>
+__device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4 *win) {
+  const PBuf out = s.buf[lay];
+  const int lane = threadIdx.x;
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
+  const float fn = s.fn;
+  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + lay];
+  uint4 *chunks = s.chunks[lay];
+  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  uint32_t wpack[4];
+  window_lanes(wpack);
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = chunks[c];
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
     // The window's accumulator values and the first round's positions are
     // requested together, then the window is converted to velocities (the
-    // grid update) in LDS.  Nodes outside the grid read as zero.
+    // grid update) in LDS.
     float4 acc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-      const int gx = ox0 + (int)(wpack[t] & 0xFFu), gy = oy0 + (int)((wpack[t] >> 8) & 0xFFu),
-                gz = oz0 + (int)((wpack[t] >> 16) & 0xFFu);
-      if (wpack[t] != 0xFFFFFFFFu && gx < s.n && gy < s.n && gz < s.n) acc[t] = s.gridA[src][node_index(s, gx, gy, gz)];
-    }
+    fetch_window(s, a, ox0, oy0, oz0, wpack, acc);
     float xnext[3] = {0.f, 0.f, 0.f};  // positions of the next round, written by this step's P2G in this order
     if ((uint32_t)lane < count) {
 #pragma unroll
-      for (int a = 0; a < 3; ++a) xnext[a] = at_byte(out.x + a * Np, 4u * (start + (uint32_t)lane));
+      for (int k = 0; k < 3; ++k) xnext[k] = at_byte(out.x + k * Np, 4u * (start + (uint32_t)lane));
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (wpack[t] == 0xFFFFFFFFu) continue;
-      const int wx = (int)(wpack[t] & 0xFFu), wy = (int)((wpack[t] >> 8) & 0xFFu), wz = (int)((wpack[t] >> 16) & 0xFFu);
-      const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-      win[(wz * PW + wy) * PW + wx] =
-          (gx < s.n && gy < s.n && gz < s.n) ? grid_velocity(s, acc[t], gx, gy, gz) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    store_window(s, acc, wpack, ox0, oy0, oz0, win);
     __syncthreads();
     uint32_t nstay = 0;
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
@@ -1353,122 +1569,23 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
       float xp[3] = {xnext[0], xnext[1], xnext[2]};
       if (r0 + 64u < count && r0 + 64u + (uint32_t)lane < count) {
 #pragma unroll
-        for (int a = 0; a < 3; ++a) xnext[a] = at_byte(out.x + a * Np, so + 256u);
+        for (int k = 0; k < 3; ++k) xnext[k] = at_byte(out.x + k * Np, so + 256u);
       }
       uint32_t key = 0;
       if (valid) {
-        int b[3];
-        float w[3][3], d[3][3];
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-          const float xn = xp[a] * fn;
-          b[a] = base_node(xn);
-          const float f = xn - (float)b[a];
-          bspline_weights(f, w[a]);
-          d[a][0] = -f;
-          d[a][1] = 1.f - f;
-          d[a][2] = 2.f - f;
-        }
-        // A particle that left its chunk's bin since the last sort (only
-        // without a sort this step; rare) has its stencil outside the window:
-        // it gathers its 27 nodes from the grid, with the grid update.
-        const bool outside = b[0] - ox0 < 0 || b[0] - ox0 >= CB || b[1] - oy0 < 0 || b[1] - oy0 >= CB ||
-                             b[2] - oz0 < 0 || b[2] - oz0 >= CB;
-        const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
-                  lz = min(max(b[2] - oz0, 0), CB - 1);
-        const int li0 = (lz * PW + ly) * PW + lx;
-        // v = sum w v_i and B = sum w v_i (o - f)^T.  The quadratic B-spline's
-        // first moment sum_o w_o (o - f) = 0 gives the columns as
-        // B_a = sum w o_a v_i - f_a v.  Reduced along x first for each (y, z)
-        // row: S = sum_x w_x v_i and U = sum_x w_x ox v_i; offsets equal to
-        // zero add nothing, so rows with oy = 0 (oz = 0) skip the y (z)
-        // column.
-        const float w2x = 2.f * w[0][2];
-        float v[3] = {0.f, 0.f, 0.f}, B[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (outside) {
-          // node rows of three, their loads issued together
-#pragma unroll 1
-          for (int r = 0; r < 9; ++r) {
-            const int oy = r % 3, oz = r / 3;
-            const int gy = b[1] + oy, gz = b[2] + oz;
-            float4 acc[3];
-#pragma unroll
-            for (int ox = 0; ox < 3; ++ox) {
-              const int gx = b[0] + ox;
-              acc[ox] = make_float4(0.f, 0.f, 0.f, 0.f);
-              if (gx >= 0 && gy >= 0 && gz >= 0 && gx < s.n && gy < s.n && gz < s.n)
-                acc[ox] = s.gridA[src][node_index(s, gx, gy, gz)];
-            }
-#pragma unroll
-            for (int ox = 0; ox < 3; ++ox) {
-              const float4 g = grid_velocity(s, acc[ox], b[0] + ox, gy, gz);
-              const float wt = w[0][ox] * w[1][oy] * w[2][oz];
-              const float vel[3] = {g.x, g.y, g.z};
-#pragma unroll
-              for (int a = 0; a < 3; ++a) {
-                v[a] = fmaf(wt, vel[a], v[a]);
-                B[a * 3 + 0] = fmaf(wt * (float)ox, vel[a], B[a * 3 + 0]);
-                B[a * 3 + 1] = fmaf(wt * (float)oy, vel[a], B[a * 3 + 1]);
-                B[a * 3 + 2] = fmaf(wt * (float)oz, vel[a], B[a * 3 + 2]);
-              }
-            }
-          }
-        } else {
-#pragma unroll
-        for (int oz = 0; oz < 3; ++oz)
-#pragma unroll
-          for (int oy = 0; oy < 3; ++oy) {
-            float S[3], U[3];
-            const float4 g0 = win[li0 + (oz * PW + oy) * PW + 0];
-            const float4 g1 = win[li0 + (oz * PW + oy) * PW + 1];
-            const float4 g2 = win[li0 + (oz * PW + oy) * PW + 2];
-            S[0] = w[0][0] * g0.x;
-            S[1] = w[0][0] * g0.y;
-            S[2] = w[0][0] * g0.z;
-            U[0] = w[0][1] * g1.x;
-            U[1] = w[0][1] * g1.y;
-            U[2] = w[0][1] * g1.z;
-            S[0] = fmaf(w[0][1], g1.x, S[0]);
-            S[1] = fmaf(w[0][1], g1.y, S[1]);
-            S[2] = fmaf(w[0][1], g1.z, S[2]);
-            S[0] = fmaf(w[0][2], g2.x, S[0]);
-            S[1] = fmaf(w[0][2], g2.y, S[1]);
-            S[2] = fmaf(w[0][2], g2.z, S[2]);
-            U[0] = fmaf(w2x, g2.x, U[0]);
-            U[1] = fmaf(w2x, g2.y, U[1]);
-            U[2] = fmaf(w2x, g2.z, U[2]);
-            const float wyz = w[1][oy] * w[2][oz];
-            const float wyz2 = wyz + wyz;
-#pragma unroll
-            for (int a = 0; a < 3; ++a) {
-              v[a] = fmaf(wyz, S[a], v[a]);
-              B[a * 3 + 0] = fmaf(wyz, U[a], B[a * 3 + 0]);
-              if (oy > 0) B[a * 3 + 1] = fmaf(oy == 1 ? wyz : wyz2, S[a], B[a * 3 + 1]);
-              if (oz > 0) B[a * 3 + 2] = fmaf(oz == 1 ? wyz : wyz2, S[a], B[a * 3 + 2]);
-            }
-          }
-        }
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-          for (int k = 0; k < 3; ++k) B[a * 3 + k] = fmaf(d[k][0], v[a], B[a * 3 + k]);  // d[k][0] = -f_k
+        float v[3], B[9], xn[3], Cn[9];
+        gather_particle(s, win, a, xp, ox0, oy0, oz0, v, B);
         bool clamped = false, nonfinite = false;
+        advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
+        int b[3];
 #pragma unroll
-        for (int a = 0; a < 3; ++a) {
-          float xa = xp[a] + s.dt * v[a];
-          if (!isfinite(xa) || !isfinite(v[a])) nonfinite = true;
-          if (xa < s.lo || xa > s.hi) clamped = true;
-          xa = fminf(fmaxf(xa, s.lo), s.hi);
-          stream_store(xa, at_byte(out.x + a * Np, so));
-          stream_store(v[a], at_byte(out.v + a * Np, so));
-          b[a] = base_node(xa * fn);
+        for (int k = 0; k < 3; ++k) {
+          stream_store(xn[k], at_byte(out.x + k * Np, so));
+          stream_store(v[k], at_byte(out.v + k * Np, so));
+          b[k] = base_node(xn[k] * fn);
         }
 #pragma unroll
-        for (int k = 0; k < 9; ++k) {
-          const float ck = s.c_scale * B[k];
-          if (!isfinite(ck)) nonfinite = true;
-          stream_store(ck, at_byte(out.C + k * Np, so));
-        }
+        for (int k = 0; k < 9; ++k) stream_store(Cn[k], at_byte(out.C + k * Np, so));
         // the next bin: nearly always the chunk's own (Morton encoding only
         // when some lane of the wavefront left it)
         const bool same_bin = (b[0] >> 2) == (ox0 >> 2) && (b[1] >> 2) == (oy0 >> 2) && (b[2] >> 2) == (oz0 >> 2);
@@ -1489,18 +1606,192 @@ __global__ __launch_bounds__(64) void k_g2p(SimDev s, int src) {
     }
     __syncthreads();  // the window is reloaded for the next chunk
   }
-  if (blockIdx.x == 0 && lane == 0) s.ctr[CTR_PENDING] = 1u;
+}
+
+// The control words a G2P leaves for the next step (that reads buffer lay):
+// F is one update behind, and that step's P2G and sort decision are its own.
+__device__ __forceinline__ void g2p_handoff(const SimDev &s, int lay) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    s.ctr[CTR_PENDING] = 1u;
+    s.ctr[CTR_LOOK + lay] = 0u;
+    s.ctr[CTR_PRESET + lay] = 0u;
+  }
+}
+
+// G2P of a step that reads buffer src (accumulator a): writes x, v, C in
+// place in layout src ^ 1 and the next step's bin keys and counts.
+template <int MAT>
+__global__ __launch_bounds__(64) void k_g2p(SimDev s, int src, int a) {
+  __shared__ float4 win[PW3];
+  g2p_step<MAT>(s, src ^ 1, a, win);
+  g2p_handoff(s, src ^ 1);
+}
+
+// Fused G2P2G ([RT-MPM], the fused-kernel variant of the step: the G2P of
+// one step and the P2G of the next in one pass over the particles).  In a
+// step without a sort the next P2G needs no new order, so each chunk's
+// particles go from the G2P straight into the next step's deposit, and the
+// state carried from step to step is only x, F (or J), E and the ids:
+// velocity and C stay in registers (they are stored for readback only when
+// the launch asks for it).  Runs only when the next step does not sort (the
+// decision is taken here, on the movers the previous step counted); before
+// a sort it runs the plain G2P, which writes the keys the sort needs.
+struct FusedShared {
+  float4 vel[PW3];          // the step's grid velocities around the bin
+  float4 win[NWIN * PW3];   // the next step's accumulation windows
+};
+
+// Step n reads buffer src, accumulated into a, and its G2P works on layout
+// lay = src ^ 1.  The P2G of step n + 1 reads the particles there and writes
+// them to the same slots of buffer src (the layout of step n + 1 repeats
+// layout lay), accumulating into a + 1.  Particles are processed in their
+// storage order, which the last sort's P2G chose ((super-rank, window,
+// cell) within each chunk) and which changes little between sorts: a lane's
+// window and pass follow from its occurrence index among the lanes of its
+// round in the same cell.
+template <int MAT, bool HAS_E>
+__device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool write_vc, FusedShared &sm) {
+  const int lay = src ^ 1;
+  const PBuf in = s.buf[lay], out = s.buf[src];
+  const int a1 = (a + 1) & (NACC - 1);
+  const int lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
+  const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
+  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + lay];
+  const uint4 *chunks = s.chunks[lay];
+  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  constexpr int FW = MAT == MPM_J_FLUID ? 1 : 9;
+  clear_accumulator(s, (a1 + 2) & (NACC - 1));
+  uint32_t wpack[4];
+  window_lanes(wpack);
+  for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
+    const uint4 ch = chunks[c];
+    const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
+    const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
+    float4 acc[4];
+    fetch_window(s, a, ox0, oy0, oz0, wpack, acc);
+    for (int k = lane; k < NWIN * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    store_window(s, acc, wpack, ox0, oy0, oz0, sm.vel);
+    __syncthreads();
+    uint32_t nmov = 0;
+    for (uint32_t r0 = 0; r0 < count; r0 += 64) {
+      const bool valid = r0 + (uint32_t)lane < count;
+      // lanes past the count read the chunk's first particle and store nothing
+      const uint32_t so = 4u * (start + (valid ? r0 + (uint32_t)lane : 0u));
+      float xp[3], Fp[FW];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) xp[k] = at_byte(in.x + k * Np, so);
+      const float E = HAS_E ? stream_load(at_byte(in.E, so)) : s.E;
+      {
+        // the id moves with the particle (its load completes with x's)
+        const uint32_t id = stream_load(at_byte(in.id, so));
+        if (valid) stream_store(id, at_byte(out.id, so));
+      }
+      // G2P of step n
+      float v[3], B[9], xn[3], Cn[9];
+      gather_particle(s, sm.vel, a, xp, ox0, oy0, oz0, v, B);
+#pragma unroll
+      for (int k = 0; k < FW; ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, so));
+      bool clamped = false, nonfinite = false;
+      advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
+      // P2G of step n + 1: F update with the new C, stress, deposit at xn
+      update_F<MAT>(Fp, Cn, dt);
+      if (valid) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) at_byte(out.x + k * Np, so) = xn[k];
+#pragma unroll
+        for (int k = 0; k < FW; ++k) stream_store(Fp[k], at_byte(out.F + k * Np, so));
+        if (HAS_E) stream_store(E, at_byte(out.E, so));
+        if (write_vc) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) stream_store(v[k], at_byte(out.v + k * Np, so));
+#pragma unroll
+          for (int k = 0; k < 9; ++k) stream_store(Cn[k], at_byte(out.C + k * Np, so));
+        }
+        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
+        if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
+      }
+      float A[9];
+      const uint32_t st = affine_momentum<MAT>(s, Fp, E, Cn, A);
+      if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
+      int b[3];
+      float f[3], w[3][3], q0[3], Ad[9];
+      particle_weights(xn, fn, b, f, w);
+      momentum_terms(mass, dx, v, A, f, q0, Ad);
+      // A particle whose new base node left the chunk's bin deposits directly
+      // (and counts toward the sort decision).
+      const bool mov = valid && (b[0] - ox0 < 0 || b[0] - ox0 >= CB || b[1] - oy0 < 0 || b[1] - oy0 >= CB ||
+                                 b[2] - oz0 < 0 || b[2] - oz0 >= CB);
+      nmov += (uint32_t)__popcll(__ballot(mov));
+      if (mov) deposit_global(s, a1, b, w, q0, Ad);
+      const bool inwin = valid && !mov;
+      const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
+                lz = min(max(b[2] - oz0, 0), CB - 1);
+      // occurrence index among the earlier lanes of the round in the same
+      // cell (ballot-matched, 6 bits): window = occ % NWIN, pass = occ / NWIN,
+      // so lanes of one pass never share (window, cell)
+      uint32_t occ;
+      {
+        const uint32_t cell = (uint32_t)((lz * CB + ly) * CB + lx);
+        uint64_t peers = __ballot(inwin);
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          const uint64_t bk = __ballot((cell >> k) & 1u);
+          peers &= ((cell >> k) & 1u) ? bk : ~bk;
+        }
+        occ = (uint32_t)__popcll(peers & below);
+      }
+      const uint32_t pass_id = occ / NWIN;
+      const int li0 = (int)(occ % NWIN) * PW3 + (lz * PW + ly) * PW + lx;
+      bool todo = inwin;
+      for (uint32_t pnow = 0;; ++pnow) {
+        if (__ballot(todo && pass_id == pnow) == 0ull) break;
+        if (todo && pass_id == pnow) {
+          deposit_window(sm.win, li0, w, q0, Ad, mass);
+          todo = false;
+        }
+      }
+    }
+    __syncthreads();
+    flush_windows(s, sm.win, ox0, oy0, oz0, a1);
+    if (lane == 0 && nmov) atomicAdd(s.ctr + CTR_MOVERS, nmov);  // for the sort decision two steps on
+    __syncthreads();  // the windows are cleared for the next chunk
+  }
+}
+
+// Step n reads buffer src and accumulated into a; write_vc: store v and C
+// (the last step of a launch, so that the state can be read back).  Leaves
+// the next step's sort decision and whether its P2G is done.
+template <int MAT, bool HAS_E>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_g2p2g(SimDev s, int src, int a,
+                                                                                     int write_vc) {
+  __shared__ FusedShared sm;
+  const bool next_sort = sort_next_step(s);  // uniform: the words it reads do not change in this kernel
+  if (next_sort) g2p_step<MAT>(s, src ^ 1, a, sm.vel);
+  else fused_step<MAT, HAS_E>(s, src, a, write_vc != 0, sm);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    // F in layout src ^ 1 is one update behind after the plain G2P; after the
+    // fused pass the state of the next step's P2G is in buffer src, current.
+    s.ctr[CTR_PENDING] = 1u;
+    s.ctr[CTR_LOOK + (src ^ 1)] = next_sort ? 0u : 1u;
+    s.ctr[CTR_PRESET + (src ^ 1)] = 1u;
+    s.ctr[CTR_SORT + (src ^ 1)] = next_sort ? 1u : 0u;
+  }
 }
 
 // Readback: unpermute to creation order, apply the pending F (or J) update.
 // Single-wavefront workgroups walk the chunk list of layout cur (the slots
-// between bins are padding).
+// between bins are padding).  After a fused G2P2G pass the state is in the
+// same slots of the other buffer, with F current.
 template <int MAT>
 __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float *__restrict__ x, float *__restrict__ v,
                                                        float *__restrict__ C, float *__restrict__ F) {
-  const PBuf b = s.buf[cur];
+  const bool fused = s.ctr[CTR_LOOK + cur] != 0u;
+  const PBuf b = s.buf[fused ? cur ^ 1 : cur];
   const size_t Np = (size_t)s.Np;
-  const bool pending = s.ctr[CTR_PENDING] != 0u;
+  const bool pending = !fused && s.ctr[CTR_PENDING] != 0u;
   const float dt = s.dt;
   const uint32_t nch = s.ctr[CTR_NCHUNKS + cur];
   for (uint32_t c = blockIdx.x; c < nch; c += gridDim.x) {
@@ -1618,8 +1909,8 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   };
   // The grid first: its placement then does not depend on N or on the other
   // arrays (shifting it by tens of MB measurably changed the grid update).
-  float4 *gA0 = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
-  float4 *gA1 = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
+  float4 *gA[NACC];
+  for (int k = 0; k < NACC; ++k) gA[k] = (float4 *)take(sizeof(float4) * (size_t)nblk * 512);
   PBuf bufs[2];
   for (int k = 0; k < 2; ++k) {
     bufs[k].x = (float *)take(sizeof(float) * 3 * Np);
@@ -1638,8 +1929,8 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
   uint32_t *cur = (uint32_t *)take(sizeof(uint32_t) * nbins);
   const int64_t ntiles = (nbins + SCAN_TILE - 1) / SCAN_TILE;
   uint32_t *tiles = (uint32_t *)take(sizeof(uint32_t) * 2 * ntiles);
-  uint32_t *aflag0 = (uint32_t *)take(sizeof(uint32_t) * nblk);
-  uint32_t *aflag1 = (uint32_t *)take(sizeof(uint32_t) * nblk);
+  uint32_t *aflag[NACC];
+  for (int k = 0; k < NACC; ++k) aflag[k] = (uint32_t *)take(sizeof(uint32_t) * nblk);
   uint4 *chunks0 = (uint4 *)take(sizeof(uint4) * max_chunks);
   uint4 *chunks1 = (uint4 *)take(sizeof(uint4) * max_chunks);
   uint32_t *ctr = (uint32_t *)take(sizeof(uint32_t) * CTR_WORDS);
@@ -1685,14 +1976,12 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     d->bin_cursor = cur;
     d->tile_sum = tiles;
     d->ntiles = (int32_t)ntiles;
-    d->active_flag[0] = aflag0;
-    d->active_flag[1] = aflag1;
+    for (int k = 0; k < NACC; ++k) d->active_flag[k] = aflag[k];
     d->chunks[0] = chunks0;
     d->chunks[1] = chunks1;
     d->ctr = ctr;
     d->status = status;
-    d->gridA[0] = gA0;
-    d->gridA[1] = gA1;
+    for (int k = 0; k < NACC; ++k) d->gridA[k] = gA[k];
   }
   return off;
 }
@@ -1702,21 +1991,27 @@ const char *const KERNEL_NAMES[NUM_KERNELS] = {"k_scan_tiles", "k_scan_bins", "k
 
 }  // namespace
 
+constexpr int NGRAPH = 2 * NACC;
+
 struct mpm_sim {
   SimDev d;
   int device = 0;
-  int cur = 0;  // buffer holding the current state
+  int cur = 0;  // buffer holding the current state (step n reads buffer (n + 1) mod 2)
   int64_t steps = 0;
+  bool fused = false;  // steps without a sort run the fused G2P2G kernel (mpm_set_fused_steps)
   hipStream_t cap = nullptr;
-  // graph[q]: one step that reads buffer q; graph[2 + q]: STEP_BATCH steps
-  // starting from buffer q (the per-launch gap between graphs, ~8 us on
-  // this GPU, is paid once per batch)
-  hipGraph_t graph[4] = {nullptr, nullptr, nullptr, nullptr};
-  hipGraphExec_t exec[4] = {nullptr, nullptr, nullptr, nullptr};
+  // Per mode (plain, fused): graph[p] = one step of phase p = n mod NACC
+  // (buffer and accumulator parities of step n); graph[NACC + p] =
+  // STEP_BATCH steps from phase p (the per-launch gap between graphs, ~8 us
+  // on this GPU, is paid once per batch).  The fused set is built on first
+  // use.
+  hipGraph_t graph[2][NGRAPH] = {};
+  hipGraphExec_t exec[2][NGRAPH] = {};
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_scatter = 0;
   int grid_p2g = 0;
   int grid_g2p = 0;
+  int grid_g2p2g = 0;
   int grid_blocks = 0;   // node-block loops (grid readback)
 };
 
@@ -1727,7 +2022,11 @@ namespace {
     if ((expr) != hipSuccess) return MPM_ERR_HIP; \
   } while (0)
 
-int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
+// Kernel k of the step of phase p (reads buffer src = (p + 1) mod 2,
+// accumulates into p); fused: the plain G2P is replaced by the G2P2G kernel,
+// which stores v and C when write_vc is set.
+int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool write_vc) {
+  const int src = (p + 1) & 1;
   const SimDev &d = sim->d;
   switch (k) {
     case 0:
@@ -1743,53 +2042,68 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int src) {
       break;
     case 3:
       if (d.material == MPM_J_FLUID) {
-        if (d.has_E) k_p2g<MPM_J_FLUID, true><<<sim->grid_p2g, 64, 0, st>>>(d, src);
-        else k_p2g<MPM_J_FLUID, false><<<sim->grid_p2g, 64, 0, st>>>(d, src);
+        if (d.has_E) k_p2g<MPM_J_FLUID, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
+        else k_p2g<MPM_J_FLUID, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
       } else {
-        if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true><<<sim->grid_p2g, 64, 0, st>>>(d, src);
-        else k_p2g<MPM_FIXED_COROTATED, false><<<sim->grid_p2g, 64, 0, st>>>(d, src);
+        if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
+        else k_p2g<MPM_FIXED_COROTATED, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
       }
       break;
     case 4:
-      if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src);
-      else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_g2p, 64, 0, st>>>(d, src);
+      if (fused) {
+        const int wv = write_vc ? 1 : 0;
+        const int g = sim->grid_g2p2g;
+        if (d.material == MPM_J_FLUID) {
+          if (d.has_E) k_g2p2g<MPM_J_FLUID, true><<<g, 64, 0, st>>>(d, src, p, wv);
+          else k_g2p2g<MPM_J_FLUID, false><<<g, 64, 0, st>>>(d, src, p, wv);
+        } else {
+          if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv);
+          else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv);
+        }
+      } else {
+        if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
+        else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
+      }
       break;
   }
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 
-int enqueue_step(mpm_sim *sim, hipStream_t st, int src) {
+int enqueue_step(mpm_sim *sim, hipStream_t st, int p, bool fused, bool write_vc) {
   for (int k = 0; k < NUM_KERNELS; ++k) {
-    const int rc = launch_kernel(sim, k, st, src);
+    const int rc = launch_kernel(sim, k, st, p, fused, write_vc);
     if (rc) return rc;
   }
   return MPM_OK;
 }
 
-int build_graphs(mpm_sim *sim) {
-  for (int g = 0; g < 4; ++g) {
-    const int src = g & 1, nsteps = g < 2 ? 1 : STEP_BATCH;
+// The graphs of one mode (0 plain, 1 fused), captured on the private stream.
+int build_graphs(mpm_sim *sim, int mode) {
+  for (int g = 0; g < NGRAPH; ++g) {
+    const int p0 = g % NACC, nsteps = g < NACC ? 1 : STEP_BATCH;
     HIP_TRY(hipStreamBeginCapture(sim->cap, hipStreamCaptureModeThreadLocal));
     int rc = MPM_OK;
-    for (int k = 0; k < nsteps && rc == MPM_OK; ++k) rc = enqueue_step(sim, sim->cap, src ^ (k & 1));
+    for (int k = 0; k < nsteps && rc == MPM_OK; ++k)
+      rc = enqueue_step(sim, sim->cap, (p0 + k) % NACC, mode == 1, k == nsteps - 1);
     hipGraph_t gr = nullptr;
     const hipError_t e = hipStreamEndCapture(sim->cap, &gr);
     if (rc || e != hipSuccess) {
       if (gr) (void)hipGraphDestroy(gr);
       return MPM_ERR_HIP;
     }
-    sim->graph[g] = gr;
-    HIP_TRY(hipGraphInstantiate(&sim->exec[g], gr, nullptr, nullptr, 0));
+    sim->graph[mode][g] = gr;
+    HIP_TRY(hipGraphInstantiate(&sim->exec[mode][g], gr, nullptr, nullptr, 0));
   }
   return MPM_OK;
 }
 
 void release(mpm_sim *sim) {
   if (!sim) return;
-  for (int k = 0; k < 4; ++k) {
-    if (sim->exec[k]) (void)hipGraphExecDestroy(sim->exec[k]);
-    if (sim->graph[k]) (void)hipGraphDestroy(sim->graph[k]);
-  }
+  for (int m = 0; m < 2; ++m)
+    for (int k = 0; k < NGRAPH; ++k) {
+      if (sim->exec[m][k]) (void)hipGraphExecDestroy(sim->exec[m][k]);
+      if (sim->graph[m][k]) (void)hipGraphDestroy(sim->graph[m][k]);
+    }
   if (sim->cap) {
     (void)hipStreamSynchronize(sim->cap);
     (void)hipStreamDestroy(sim->cap);
@@ -1859,6 +2173,15 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     // 24 per CU, which 74 VGPRs would allow, was slower.
     occ_g = occ_g < 20 ? occ_g : 20;
     sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
+    // The fused kernel holds the G2P velocity window and the P2G windows
+    // (10 KB of LDS): at most 15 workgroups per CU; P2G's cap of 16 applies.
+    int occ_f = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, k_g2p2g<MPM_FIXED_COROTATED, false>, 64, 0) !=
+            hipSuccess ||
+        occ_f <= 0)
+      occ_f = 8;
+    occ_f = occ_f < 16 ? occ_f : 16;
+    sim->grid_g2p2g = ((cus * occ_f + NQ - 1) / NQ) * NQ;
     sim->grid_blocks = cus * 8;
     // single-wavefront workgroups, 8 per SIMD: the scatter is a chain of
     // short dependent loads per chunk, so it wants many chunks in flight
@@ -1871,24 +2194,25 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     const int zb = (int)std::min<int64_t>(((int64_t)d.nbins + WG - 1) / WG, 4096);
     k_zero_u32<<<zb, WG, 0, st>>>(d.bin_count, (size_t)d.nbins);
     k_zero_u32<<<zb, WG, 0, st>>>(d.stay_count, (size_t)d.nbins);
-    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[0], (size_t)d.nblk);
-    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[1], (size_t)d.nblk);
     const int gb = (int)std::min<int64_t>(((int64_t)d.nblk * 512 * 4 + WG - 1) / WG, 16384);
-    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[0]), (size_t)d.nblk * 512 * 4);
-    // G2P may read a stencil node whose weight is exactly zero and that no
-    // particle marked active; it must hold a finite value, so start at zero.
-    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[1]), (size_t)d.nblk * 512 * 4);
+    for (int k = 0; k < NACC; ++k) {
+      k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[k], (size_t)d.nblk);
+      // G2P may read a stencil node whose weight is exactly zero and that no
+      // particle marked active; it must hold a finite value, so start at zero.
+      k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[k]), (size_t)d.nblk * 512 * 4);
+    }
     if (d.N > 0) {
       k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
       // one bucket pass to bring the initial state into bin order (buffer 1,
-      // whose chunk list the scan writes)
-      launch_kernel(sim, 0, st, 0);
-      launch_kernel(sim, 1, st, 0);
+      // whose chunk list the scan writes): the scans of a step that reads
+      // buffer 0 (phase 1)
+      launch_kernel(sim, 0, st, 1, false, false);
+      launch_kernel(sim, 1, st, 1, false, false);
       k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
       sim->cur = 1;
     }
     if (hipGetLastError() != hipSuccess) { rc = MPM_ERR_HIP; break; }
-    if (d.N > 0) rc = build_graphs(sim);
+    if (d.N > 0) rc = build_graphs(sim, 0);
   } while (0);
   if (rc != MPM_OK) {
     release(sim);
@@ -1904,20 +2228,31 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
     sim->steps += n_steps;
     return MPM_OK;
   }
-  for (int g = 0; g < 4; ++g)
-    if (!sim->exec[g]) return MPM_ERR_STATE;
+  const int mode = sim->fused ? 1 : 0;
+  if (mode == 1 && !sim->exec[1][0]) {
+    const int rc = build_graphs(sim, 1);
+    if (rc) return rc;
+  }
+  for (int g = 0; g < NGRAPH; ++g)
+    if (!sim->exec[mode][g]) return MPM_ERR_STATE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t left = n_steps;
-  while (left >= STEP_BATCH) {  // batches end on their starting parity
-    if (hipGraphLaunch(sim->exec[2 + sim->cur], st) != hipSuccess) return MPM_ERR_HIP;
+  while (left >= STEP_BATCH) {  // batches end on their starting phase
+    if (hipGraphLaunch(sim->exec[mode][NACC + (int)(sim->steps % NACC)], st) != hipSuccess) return MPM_ERR_HIP;
     sim->steps += STEP_BATCH;
     left -= STEP_BATCH;
   }
   for (; left > 0; --left) {
-    if (hipGraphLaunch(sim->exec[sim->cur], st) != hipSuccess) return MPM_ERR_HIP;
+    if (hipGraphLaunch(sim->exec[mode][sim->steps % NACC], st) != hipSuccess) return MPM_ERR_HIP;
     sim->cur ^= 1;
     sim->steps += 1;
   }
+  return MPM_OK;
+}
+
+int mpm_set_fused_steps(mpm_sim *sim, int32_t enable) {
+  if (!sim || enable < 0 || enable > 1) return MPM_ERR_INVALID_ARG;
+  sim->fused = enable == 1;
   return MPM_OK;
 }
 
@@ -1942,7 +2277,7 @@ int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel
   for (int32_t s = 0; s < n_steps && rc == MPM_OK; ++s) {
     if (hipEventRecord(ev[0], st) != hipSuccess) { rc = MPM_ERR_HIP; break; }
     for (int k = 0; k < NUM_KERNELS && rc == MPM_OK; ++k) {
-      rc = launch_kernel(sim, k, st, sim->cur);
+      rc = launch_kernel(sim, k, st, (int)(sim->steps % NACC), sim->fused, true);
       if (rc == MPM_OK && hipEventRecord(ev[k + 1], st) != hipSuccess) rc = MPM_ERR_HIP;
     }
     if (rc != MPM_OK) break;
@@ -1976,8 +2311,9 @@ int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream) {
   const int zb = (int)std::min<size_t>((nn * 3 + WG - 1) / WG, 16384);
   if (mass) k_zero_f32<<<zb, WG, 0, st>>>(mass, nn);
   if (momentum) k_zero_f32<<<zb, WG, 0, st>>>(momentum, 3 * nn);
-  // the last step read buffer cur ^ 1 and used grid parity cur ^ 1
-  if (sim->d.N > 0 && sim->steps > 0) k_read_grid<<<sim->grid_blocks, WG, 0, st>>>(sim->d, sim->cur ^ 1, mass, momentum);
+  // the last step accumulated into its phase's accumulator
+  if (sim->d.N > 0 && sim->steps > 0)
+    k_read_grid<<<sim->grid_blocks, WG, 0, st>>>(sim->d, (int)((sim->steps - 1) % NACC), mass, momentum);
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 

@@ -19,14 +19,17 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def gpu_run(scene, steps: int, read=("particles", "grid"), sort_policy=None):
+def gpu_run(scene, steps: int, read=("particles", "grid"), sort_policy=None, fused=False):
     """Create, step and read back through the C ABI (torch only for memory).
-    sort_policy = (max_interval, mover_budget) for mpm_set_sort_policy."""
+    sort_policy = (max_interval, mover_budget) for mpm_set_sort_policy;
+    fused: mpm_set_fused_steps(1)."""
     import material_point_physics_amd as mpm
     sim = mpm.Simulation(scene)
     try:
         if sort_policy is not None:
             sim.set_sort_policy(*sort_policy)
+        if fused:
+            sim.set_fused_steps(True)
         sim.step(steps)
         out = {}
         if "particles" in read:

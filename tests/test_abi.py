@@ -96,6 +96,7 @@ def test_null_handle_calls_are_rejected():
     L = mpm.lib()
     assert L.mpm_step(None, 1, None) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_set_sort_policy(None, 8, 1000, None) == mpm.MPM_ERR_INVALID_ARG
+    assert L.mpm_set_fused_steps(None, 1) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_read_particles(None, None, None, None, None, None) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_read_grid(None, None, None, None) == mpm.MPM_ERR_INVALID_ARG
     assert L.mpm_status(None, None, None) == mpm.MPM_ERR_INVALID_ARG
