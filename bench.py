@@ -35,15 +35,26 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bool, sorted_steps=True) -> dict:
+def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bool, sorted_steps=True,
+                 fused=False) -> dict:
     """Algorithmic HBM bytes per launch of each kernel (what the method must
     move through that kernel; see the byte model in the design notes).
     fp32 everywhere; F is 9 floats (elastic) or 1 (fluid J).  With
     sorted_steps=False (free-zone steps without a sort) the scatter moves
     nothing and P2G reads the key word (4 B) instead of perm and the cell
-    byte (5 B)."""
+    byte (5 B).  With fused=True (fused steps without a sort) the separate
+    P2G moves nothing and the G2P2G kernel reads x, F, E, id and writes them
+    back, plus v and C (stored on the last step of each launch, and on every
+    profiled step), and per active node reads the window once, writes the
+    next accumulator and clears the one of two steps before."""
     f = 36 if material == 0 else 4
     e = 4 if has_E else 0
+    if fused:
+        kb = kernel_bytes(N, active_nodes, nbins, material, has_E, sorted_steps=False)
+        kb["k_p2g"] = 0
+        kb["k_g2p2g"] = N * 2 * (12 + f + e + 4) + N * (12 + 36) + 48 * active_nodes
+        del kb["k_g2p"]
+        return kb
     if not sorted_steps:
         kb = kernel_bytes(N, active_nodes, nbins, material, has_E)
         kb["k_scatter"] = 0
@@ -102,6 +113,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps for the CPU baseline (0 = skip)")
     ap.add_argument("--sort-interval", type=int, default=0,
                     help="free-zone sort policy: sort at least every K steps (0 = sort every step, the default)")
+    ap.add_argument("--fused", action="store_true",
+                    help="fused G2P2G steps between sorts (mpm_set_fused_steps; use with --sort-interval)")
     ap.add_argument("--mover-budget", type=int, default=-1,
                     help="free-zone sort policy: also sort when more particles than this left their bins "
                          "(default: N/1000)")
@@ -126,6 +139,9 @@ def main():
     if free_zone:
         sim.set_sort_policy(args.sort_interval, budget)
         log(f"free-zone sort policy: at least every {args.sort_interval} steps, or more than {budget} movers")
+    if args.fused:
+        sim.set_fused_steps(True)
+        log("fused G2P2G steps between sorts")
     log("created; warmup")
     sim.step(args.warmup)
     torch.cuda.synchronize()
@@ -147,7 +163,7 @@ def main():
 
     # ---- per-kernel launch times (HIP events around each kernel, same stream)
     kms = mpm.mpm_step_profiled(sim.handle, args.profile_steps, stream)
-    kavg = {k: v / args.profile_steps for k, v in kms.items()}
+    kavg = {("k_g2p2g" if (args.fused and k == "k_g2p") else k): v / args.profile_steps for k, v in kms.items()}
     m, _ = sim.read_grid()
     mass = m.cpu().numpy()
     active_nodes = int((mass > 0).sum())
@@ -180,13 +196,15 @@ def main():
               "memory_GB": round(props.total_memory / 1e9, 1)}
     log(f"device {device}; plain 1 GiB copy {copy_gbps:.0f} GB/s")
     kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None,
-                      sorted_steps=not free_zone)
+                      sorted_steps=not free_zone, fused=args.fused)
     kernels = {k: {"avg_ms": round(kavg[k], 5), "alg_bytes": kb[k],
                    "GBps": round(kb[k] / (kavg[k] * 1e-3) / 1e9, 1)} for k in kavg}
     dom = max(kavg, key=kavg.get)
     achieved = kb[dom] / (kavg[dom] * 1e-3) / 1e9
     traffic = committed_traffic(sc.name, dom)
     step_bytes = sum(kb.values())
+    if args.fused:
+        step_bytes -= sc.N * (12 + 36) * 7 // 8  # graph-replayed steps store v and C once per 8-step launch
     log(f"kernels: {kernels}")
     log(f"active nodes {active_nodes}, active blocks {active_blocks}, status {status[:4]}")
 
@@ -226,7 +244,8 @@ def main():
         "config": {"workload": f"{sc.name}: {sc.description}", "particles": sc.N, "grid": f"{n}^3",
                    "dt": sc.dt, "material": "fixed-corotated" if sc.material == 0 else "J-fluid",
                    "sort": (f"free zone: at least every {args.sort_interval} steps or above {budget} movers "
-                            "(byte model assumes no sort in the timed steps)") if free_zone else "every step"},
+                            "(byte model assumes no sort in the timed steps)") if free_zone else "every step",
+                   "fused_g2p2g": bool(args.fused)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "step_hbm": {"alg_bytes_per_step": step_bytes,

@@ -1666,12 +1666,28 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
   clear_accumulator(s, (a1 + 2) & (NACC - 1));
   uint32_t wpack[4];
   window_lanes(wpack);
+  uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);  // chunk records are loaded one chunk ahead
+  if (qbeg + wq < qend) ch_next = chunks[qbeg + wq];
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
-    const uint4 ch = chunks[c];
+    const uint4 ch = ch_next;
+    if (c + nwq < qend) ch_next = chunks[c + nwq];
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
+    // the window and the first round's x, F, E and ids are requested
+    // together; later rounds are loaded one round ahead
     float4 acc[4];
     fetch_window(s, a, ox0, oy0, oz0, wpack, acc);
+    float xq[3], Fq[FW], Eq = s.E;
+    uint32_t idq;
+    {
+      const uint32_t sn = 4u * (start + ((uint32_t)lane < count ? (uint32_t)lane : 0u));
+#pragma unroll
+      for (int k = 0; k < 3; ++k) xq[k] = at_byte(in.x + k * Np, sn);
+#pragma unroll
+      for (int k = 0; k < FW; ++k) Fq[k] = stream_load(at_byte(in.F + k * Np, sn));
+      if (HAS_E) Eq = stream_load(at_byte(in.E, sn));
+      idq = stream_load(at_byte(in.id, sn));
+    }
     for (int k = lane; k < NWIN * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     store_window(s, acc, wpack, ox0, oy0, oz0, sm.vel);
     __syncthreads();
@@ -1680,20 +1696,23 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       const bool valid = r0 + (uint32_t)lane < count;
       // lanes past the count read the chunk's first particle and store nothing
       const uint32_t so = 4u * (start + (valid ? r0 + (uint32_t)lane : 0u));
-      float xp[3], Fp[FW];
+      float xp[3] = {xq[0], xq[1], xq[2]}, Fp[FW];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) xp[k] = at_byte(in.x + k * Np, so);
-      const float E = HAS_E ? stream_load(at_byte(in.E, so)) : s.E;
-      {
-        // the id moves with the particle (its load completes with x's)
-        const uint32_t id = stream_load(at_byte(in.id, so));
-        if (valid) stream_store(id, at_byte(out.id, so));
+      for (int k = 0; k < FW; ++k) Fp[k] = Fq[k];
+      const float E = Eq;
+      if (valid) stream_store(idq, at_byte(out.id, so));
+      if (r0 + 64u < count) {
+        const bool vn = r0 + 64u + (uint32_t)lane < count;
+        const uint32_t sn = 4u * (start + (vn ? r0 + 64u + (uint32_t)lane : 0u));
+#pragma unroll
+        for (int k = 0; k < 3; ++k) xq[k] = at_byte(in.x + k * Np, sn);
+#pragma unroll
+        for (int k = 0; k < FW; ++k) Fq[k] = stream_load(at_byte(in.F + k * Np, sn));
+        if (HAS_E) Eq = stream_load(at_byte(in.E, sn));
+        idq = stream_load(at_byte(in.id, sn));
       }
-      // G2P of step n
       float v[3], B[9], xn[3], Cn[9];
       gather_particle(s, sm.vel, a, xp, ox0, oy0, oz0, v, B);
-#pragma unroll
-      for (int k = 0; k < FW; ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, so));
       bool clamped = false, nonfinite = false;
       advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
       // P2G of step n + 1: F update with the new C, stress, deposit at xn
@@ -1765,7 +1784,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
 // (the last step of a launch, so that the state can be read back).  Leaves
 // the next step's sort decision and whether its P2G is done.
 template <int MAT, bool HAS_E>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_g2p2g(SimDev s, int src, int a,
+__global__ __launch_bounds__(64) void k_g2p2g(SimDev s, int src, int a,
                                                                                      int write_vc) {
   __shared__ FusedShared sm;
   const bool next_sort = sort_next_step(s);  // uniform: the words it reads do not change in this kernel
@@ -2174,12 +2193,14 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     occ_g = occ_g < 20 ? occ_g : 20;
     sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
     // The fused kernel holds the G2P velocity window and the P2G windows
-    // (10 KB of LDS): at most 15 workgroups per CU; P2G's cap of 16 applies.
+    // (10 KB of LDS, at most 15 workgroups per CU) and, with its loads one
+    // round ahead, 130-150 VGPRs (3 waves per SIMD); P2G's cap of 16 applies.
     int occ_f = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, k_g2p2g<MPM_FIXED_COROTATED, false>, 64, 0) !=
-            hipSuccess ||
-        occ_f <= 0)
-      occ_f = 8;
+    const void *fk = d.material == MPM_J_FLUID
+                         ? (d.has_E ? (const void *)k_g2p2g<MPM_J_FLUID, true> : (const void *)k_g2p2g<MPM_J_FLUID, false>)
+                         : (d.has_E ? (const void *)k_g2p2g<MPM_FIXED_COROTATED, true>
+                                    : (const void *)k_g2p2g<MPM_FIXED_COROTATED, false>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, fk, 64, 0) != hipSuccess || occ_f <= 0) occ_f = 8;
     occ_f = occ_f < 16 ? occ_f : 16;
     sim->grid_g2p2g = ((cus * occ_f + NQ - 1) / NQ) * NQ;
     sim->grid_blocks = cus * 8;
