@@ -82,12 +82,13 @@ def source_sha1() -> str:
         return hashlib.sha1(f.read()).hexdigest()
 
 
-def committed_traffic(workload: str, kernel: str):
+def committed_traffic(workload: str, kernel: str, mode: str = ""):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
-    profiles/<workload>_all_kernels_traffic.txt (FETCH_SIZE and WRITE_SIZE runs, each
-    scaled by the calibration copy), or None when that summary is missing or
-    was taken from a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_all_kernels_traffic.txt")
+    profiles/<workload><mode>_all_kernels_traffic.txt (FETCH_SIZE and WRITE_SIZE runs,
+    each scaled by the calibration copy; mode "_fused" for the fused steps),
+    or None when that summary is missing or was taken from a different
+    kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{workload}{mode}_all_kernels_traffic.txt")
     if not os.path.exists(path):
         return None
     sha, val = None, None
@@ -201,7 +202,7 @@ def main():
                    "GBps": round(kb[k] / (kavg[k] * 1e-3) / 1e9, 1)} for k in kavg}
     dom = max(kavg, key=kavg.get)
     achieved = kb[dom] / (kavg[dom] * 1e-3) / 1e9
-    traffic = committed_traffic(sc.name, dom)
+    traffic = committed_traffic(sc.name, dom, "_fused" if args.fused else "")
     step_bytes = sum(kb.values())
     if args.fused:
         step_bytes -= sc.N * (12 + 36) * 7 // 8  # graph-replayed steps store v and C once per 8-step launch
