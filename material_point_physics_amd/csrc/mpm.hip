@@ -1666,11 +1666,15 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
   clear_accumulator(s, (a1 + 2) & (NACC - 1));
   uint32_t wpack[4];
   window_lanes(wpack);
+  // The next step's layout repeats this one: its chunk list is this list
+  // (copied here, for a next step that runs no scan).
+  if (blockIdx.x == 0 && lane == 0) s.ctr[CTR_NCHUNKS + src] = nch;
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);  // chunk records are loaded one chunk ahead
   if (qbeg + wq < qend) ch_next = chunks[qbeg + wq];
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = ch_next;
     if (c + nwq < qend) ch_next = chunks[c + nwq];
+    if (lane == 0) s.chunks[src][c] = ch;
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
     // the window and the first round's x, F, E and ids are requested
@@ -1781,13 +1785,15 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
 }
 
 // Step n reads buffer src and accumulated into a; write_vc: store v and C
-// (the last step of a launch, so that the state can be read back).  Leaves
-// the next step's sort decision and whether its P2G is done.
+// (the last step of a launch, so that the state can be read back); sched:
+// whether the next step sorts, 0 or 1 when the host schedules the sorts
+// (a fixed interval), -1 to decide here by the policy.  Leaves the next
+// step's sort decision and whether its P2G is done.
 template <int MAT, bool HAS_E>
-__global__ __launch_bounds__(64) void k_g2p2g(SimDev s, int src, int a,
-                                                                                     int write_vc) {
+__global__ __launch_bounds__(64) void k_g2p2g(SimDev s, int src, int a, int write_vc, int sched) {
   __shared__ FusedShared sm;
-  const bool next_sort = sort_next_step(s);  // uniform: the words it reads do not change in this kernel
+  // uniform: the words sort_next_step reads do not change in this kernel
+  const bool next_sort = sched < 0 ? sort_next_step(s) : sched != 0;
   if (next_sort) g2p_step<MAT>(s, src ^ 1, a, sm.vel);
   else fused_step<MAT, HAS_E>(s, src, a, write_vc != 0, sm);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -2010,22 +2016,27 @@ const char *const KERNEL_NAMES[NUM_KERNELS] = {"k_scan_tiles", "k_scan_bins", "k
 
 }  // namespace
 
-constexpr int NGRAPH = 2 * NACC;
+// Graph sets, one per mode: 0 = separate kernels; 1 = fused G2P2G steps,
+// sorts decided on the device; 2 = fused steps with sorts at a fixed
+// interval K (no mover budget), scheduled by the host, where a step without
+// a sort launches the fused kernel alone.  A set holds, for each phase p of
+// its period (the step number modulo NACC, or modulo max(K, 8) in mode 2),
+// one step (graph p) and STEP_BATCH steps (graph period + p).
+constexpr int MAX_PERIOD = 32;  // mode 2: K a power of two, at most this
 
 struct mpm_sim {
   SimDev d;
   int device = 0;
   int cur = 0;  // buffer holding the current state (step n reads buffer (n + 1) mod 2)
   int64_t steps = 0;
-  bool fused = false;  // steps without a sort run the fused G2P2G kernel (mpm_set_fused_steps)
+  bool fused = false;             // mpm_set_fused_steps
+  int32_t sort_interval = 0;      // the policy as last set (host copy)
+  int64_t mover_budget = 0;
+  int sched_K = 0;                // K of the built mode-2 graphs
+  bool sched_ready = false;       // the last step left the state the mode-2 schedule expects
   hipStream_t cap = nullptr;
-  // Per mode (plain, fused): graph[p] = one step of phase p = n mod NACC
-  // (buffer and accumulator parities of step n); graph[NACC + p] =
-  // STEP_BATCH steps from phase p (the per-launch gap between graphs, ~8 us
-  // on this GPU, is paid once per batch).  The fused set is built on first
-  // use.
-  hipGraph_t graph[2][NGRAPH] = {};
-  hipGraphExec_t exec[2][NGRAPH] = {};
+  hipGraph_t graph[3][2 * MAX_PERIOD] = {};
+  hipGraphExec_t exec[3][2 * MAX_PERIOD] = {};
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_scatter = 0;
   int grid_p2g = 0;
@@ -2041,10 +2052,24 @@ namespace {
     if ((expr) != hipSuccess) return MPM_ERR_HIP; \
   } while (0)
 
+int step_mode(const mpm_sim *sim) {
+  if (!sim->fused) return 0;
+  const int K = sim->sort_interval;
+  // a budget of at least N never triggers a sort
+  const bool no_budget = sim->mover_budget >= (int64_t)sim->d.N;
+  if (no_budget && K >= 2 && K <= MAX_PERIOD && (K & (K - 1)) == 0) return 2;
+  return 1;
+}
+
+int mode_period(const mpm_sim *sim, int mode) {
+  return mode == 2 ? std::max(sim->sort_interval, STEP_BATCH) : NACC;
+}
+
 // Kernel k of the step of phase p (reads buffer src = (p + 1) mod 2,
 // accumulates into p); fused: the plain G2P is replaced by the G2P2G kernel,
-// which stores v and C when write_vc is set.
-int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool write_vc) {
+// which stores v and C when write_vc is set and takes the next step's sort
+// decision from sched (-1: by the policy, on the device).
+int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool write_vc, int sched) {
   const int src = (p + 1) & 1;
   const SimDev &d = sim->d;
   switch (k) {
@@ -2073,11 +2098,11 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
         const int wv = write_vc ? 1 : 0;
         const int g = sim->grid_g2p2g;
         if (d.material == MPM_J_FLUID) {
-          if (d.has_E) k_g2p2g<MPM_J_FLUID, true><<<g, 64, 0, st>>>(d, src, p, wv);
-          else k_g2p2g<MPM_J_FLUID, false><<<g, 64, 0, st>>>(d, src, p, wv);
+          if (d.has_E) k_g2p2g<MPM_J_FLUID, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          else k_g2p2g<MPM_J_FLUID, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
         } else {
-          if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv);
-          else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv);
+          if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
         }
       } else {
         if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
@@ -2088,22 +2113,51 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 
-int enqueue_step(mpm_sim *sim, hipStream_t st, int p, bool fused, bool write_vc) {
+// Which kernels step n runs in a mode: all five, or (mode 2, a step after a
+// fused pass) the fused kernel alone; and the fused kernel's sched argument.
+// lean_ok = false forces all five (the first step under a new schedule,
+// whose P2G may not have run).
+void step_plan(const mpm_sim *sim, int64_t n, int mode, bool lean_ok, bool run[NUM_KERNELS], int &sched) {
+  for (int k = 0; k < NUM_KERNELS; ++k) run[k] = true;
+  sched = -1;
+  if (mode == 2) {
+    const int K = sim->sort_interval, c = (int)(n % K);
+    sched = (c == K - 1) ? 1 : 0;
+    if (c != 0 && lean_ok)
+      for (int k = 0; k < NUM_KERNELS - 1; ++k) run[k] = false;
+  }
+}
+
+int enqueue_step(mpm_sim *sim, hipStream_t st, int64_t n, int mode, bool lean_ok, bool write_vc) {
+  bool run[NUM_KERNELS];
+  int sched;
+  step_plan(sim, n, mode, lean_ok, run, sched);
   for (int k = 0; k < NUM_KERNELS; ++k) {
-    const int rc = launch_kernel(sim, k, st, p, fused, write_vc);
+    if (!run[k]) continue;
+    const int rc = launch_kernel(sim, k, st, (int)(n % NACC), mode != 0, write_vc, sched);
     if (rc) return rc;
   }
   return MPM_OK;
 }
 
-// The graphs of one mode (0 plain, 1 fused), captured on the private stream.
+void destroy_graphs(mpm_sim *sim, int mode) {
+  for (int k = 0; k < 2 * MAX_PERIOD; ++k) {
+    if (sim->exec[mode][k]) (void)hipGraphExecDestroy(sim->exec[mode][k]);
+    if (sim->graph[mode][k]) (void)hipGraphDestroy(sim->graph[mode][k]);
+    sim->exec[mode][k] = nullptr;
+    sim->graph[mode][k] = nullptr;
+  }
+}
+
+// The graphs of one mode, captured on the private stream.
 int build_graphs(mpm_sim *sim, int mode) {
-  for (int g = 0; g < NGRAPH; ++g) {
-    const int p0 = g % NACC, nsteps = g < NACC ? 1 : STEP_BATCH;
+  const int P = mode_period(sim, mode);
+  for (int g = 0; g < 2 * P; ++g) {
+    const int p0 = g % P, nsteps = g < P ? 1 : STEP_BATCH;
     HIP_TRY(hipStreamBeginCapture(sim->cap, hipStreamCaptureModeThreadLocal));
     int rc = MPM_OK;
     for (int k = 0; k < nsteps && rc == MPM_OK; ++k)
-      rc = enqueue_step(sim, sim->cap, (p0 + k) % NACC, mode == 1, k == nsteps - 1);
+      rc = enqueue_step(sim, sim->cap, p0 + k, mode, true, k == nsteps - 1);
     hipGraph_t gr = nullptr;
     const hipError_t e = hipStreamEndCapture(sim->cap, &gr);
     if (rc || e != hipSuccess) {
@@ -2118,11 +2172,7 @@ int build_graphs(mpm_sim *sim, int mode) {
 
 void release(mpm_sim *sim) {
   if (!sim) return;
-  for (int m = 0; m < 2; ++m)
-    for (int k = 0; k < NGRAPH; ++k) {
-      if (sim->exec[m][k]) (void)hipGraphExecDestroy(sim->exec[m][k]);
-      if (sim->graph[m][k]) (void)hipGraphDestroy(sim->graph[m][k]);
-    }
+  for (int m = 0; m < 3; ++m) destroy_graphs(sim, m);
   if (sim->cap) {
     (void)hipStreamSynchronize(sim->cap);
     (void)hipStreamDestroy(sim->cap);
@@ -2227,8 +2277,8 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
       // one bucket pass to bring the initial state into bin order (buffer 1,
       // whose chunk list the scan writes): the scans of a step that reads
       // buffer 0 (phase 1)
-      launch_kernel(sim, 0, st, 1, false, false);
-      launch_kernel(sim, 1, st, 1, false, false);
+      launch_kernel(sim, 0, st, 1, false, false, -1);
+      launch_kernel(sim, 1, st, 1, false, false, -1);
       k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
       sim->cur = 1;
     }
@@ -2249,22 +2299,38 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
     sim->steps += n_steps;
     return MPM_OK;
   }
-  const int mode = sim->fused ? 1 : 0;
-  if (mode == 1 && !sim->exec[1][0]) {
-    const int rc = build_graphs(sim, 1);
-    if (rc) return rc;
+  const int mode = step_mode(sim);
+  if (mode == 2 && sim->sched_K != sim->sort_interval) {
+    destroy_graphs(sim, 2);
+    sim->sched_K = 0;
   }
-  for (int g = 0; g < NGRAPH; ++g)
+  if (mode != 0 && !sim->exec[mode][0]) {
+    const int rc = build_graphs(sim, mode);
+    if (rc) return rc;
+    if (mode == 2) sim->sched_K = sim->sort_interval;
+  }
+  const int P = mode_period(sim, mode);
+  for (int g = 0; g < 2 * P; ++g)
     if (!sim->exec[mode][g]) return MPM_ERR_STATE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t left = n_steps;
-  while (left >= STEP_BATCH) {  // batches end on their starting phase
-    if (hipGraphLaunch(sim->exec[mode][NACC + (int)(sim->steps % NACC)], st) != hipSuccess) return MPM_ERR_HIP;
-    sim->steps += STEP_BATCH;
+  if (mode == 2 && !sim->sched_ready && left > 0) {
+    // the first step under the schedule runs all its kernels (its P2G may
+    // not have run yet)
+    const int rc = enqueue_step(sim, st, sim->steps, 2, false, left == 1);
+    if (rc) return rc;
+    sim->cur ^= 1;
+    sim->steps += 1;
+    left -= 1;
+    sim->sched_ready = true;
+  }
+  while (left >= STEP_BATCH) {
+    if (hipGraphLaunch(sim->exec[mode][P + (int)(sim->steps % P)], st) != hipSuccess) return MPM_ERR_HIP;
+    sim->steps += STEP_BATCH;  // even: the buffer parity is unchanged
     left -= STEP_BATCH;
   }
   for (; left > 0; --left) {
-    if (hipGraphLaunch(sim->exec[mode][sim->steps % NACC], st) != hipSuccess) return MPM_ERR_HIP;
+    if (hipGraphLaunch(sim->exec[mode][sim->steps % P], st) != hipSuccess) return MPM_ERR_HIP;
     sim->cur ^= 1;
     sim->steps += 1;
   }
@@ -2274,6 +2340,7 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
 int mpm_set_fused_steps(mpm_sim *sim, int32_t enable) {
   if (!sim || enable < 0 || enable > 1) return MPM_ERR_INVALID_ARG;
   sim->fused = enable == 1;
+  sim->sched_ready = false;
   return MPM_OK;
 }
 
@@ -2281,7 +2348,11 @@ int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget
   if (!sim || max_interval < 0 || mover_budget < 0) return MPM_ERR_INVALID_ARG;
   const uint32_t budget = mover_budget > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)mover_budget;
   k_set_sort_policy<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(sim->d, (uint32_t)max_interval, budget);
-  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return MPM_ERR_HIP;
+  sim->sort_interval = max_interval;
+  sim->mover_budget = mover_budget;
+  sim->sched_ready = false;
+  return MPM_OK;
 }
 
 int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms) {
@@ -2291,14 +2362,19 @@ int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel
     return MPM_OK;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int mode = step_mode(sim);
   hipEvent_t ev[NUM_KERNELS + 1];
   for (int k = 0; k <= NUM_KERNELS; ++k)
     if (hipEventCreate(&ev[k]) != hipSuccess) return MPM_ERR_HIP;
   int rc = MPM_OK;
   for (int32_t s = 0; s < n_steps && rc == MPM_OK; ++s) {
+    // the same kernels as the graphs (a kernel a step does not run takes no time)
+    bool run[NUM_KERNELS];
+    int sched;
+    step_plan(sim, sim->steps, mode, mode == 2 && sim->sched_ready, run, sched);
     if (hipEventRecord(ev[0], st) != hipSuccess) { rc = MPM_ERR_HIP; break; }
     for (int k = 0; k < NUM_KERNELS && rc == MPM_OK; ++k) {
-      rc = launch_kernel(sim, k, st, (int)(sim->steps % NACC), sim->fused, true);
+      if (run[k]) rc = launch_kernel(sim, k, st, (int)(sim->steps % NACC), mode != 0, true, sched);
       if (rc == MPM_OK && hipEventRecord(ev[k + 1], st) != hipSuccess) rc = MPM_ERR_HIP;
     }
     if (rc != MPM_OK) break;
@@ -2310,6 +2386,7 @@ int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel
     }
     sim->cur ^= 1;
     sim->steps += 1;
+    sim->sched_ready = mode == 2;
   }
   for (int k = 0; k <= NUM_KERNELS; ++k) (void)hipEventDestroy(ev[k]);
   return rc;

@@ -4,11 +4,12 @@ is read back from wherever that kernel left it.  The physics is the same as
 separate kernels, so the oracle and the tolerances of the per-step-sort
 parity tests apply unchanged.
 
-Cases: the free-zone scenes (no sort after creation, a sort every 4 steps,
+Cases: the free-zone scenes (no sort after creation, a sort every 3 steps,
 a mover budget), the equality with per-step sorting, batched graphs against
 single steps, readback between launches that end on a fused pass, switching
 fusion off and on, and the default policy (every step sorts, so no step is
-fused)."""
+fused); then the host-scheduled sorts (a power-of-two interval and no mover
+budget), where a step after a fused pass launches the fused kernel alone."""
 import numpy as np
 import pytest
 
@@ -24,8 +25,9 @@ CASES = {
     # no sort after creation: every step after the first is fused, and many
     # particles leave their bins (direct deposits and gathers)
     "swirl_never": (lambda: swirl(71, cscale=2.0), 8, NEVER),
-    # the three jelly spheres, sorted every 4 steps (plain G2P before each sort)
-    "jelly3_every4": (scenes.jelly3_55k, 10, (4, 1 << 40)),
+    # the three jelly spheres, sorted every 3 steps (plain G2P before each sort;
+    # 3 is not a power of two, so the device decides)
+    "jelly3_every3": (scenes.jelly3_55k, 10, (3, 1 << 40)),
     # fluid with per-particle modulus, sorted when more than 50 particles left their bins
     "swirl_fluid_budget50": (lambda: swirl(72, material=scenes.J_FLUID, E=400.0, per_particle_E=True), 8,
                              (1 << 30, 50)),
@@ -124,5 +126,77 @@ def test_switch_fusion_off_and_on():
     finally:
         sim.close()
     orc, env = pu.envelope(sc, 10)
+    assert_particle_parity(sc, got, orc, env)
+    assert_grid_parity(sc, got, orc, tol=max(1e-5, 20 * env["v"]))
+
+
+# A fixed power-of-two interval with no mover budget: the host schedules the
+# sorts, and a step after a fused pass launches the fused kernel alone.
+SCHED_CASES = {
+    "swirl_every4": (lambda: swirl(77, cscale=2.0), 13, (4, 1 << 40)),
+    "swirl_fluid_every2": (lambda: swirl(78, material=scenes.J_FLUID, E=400.0), 9, (2, 1 << 40)),
+    "swirl_E_every8": (lambda: swirl(79, cscale=2.0, per_particle_E=True), 19, (8, 1 << 40)),
+    "jelly3_every16": (scenes.jelly3_55k, 21, (16, 1 << 40)),
+}
+
+
+@pytest.mark.parametrize("name", list(SCHED_CASES))
+def test_scheduled_fused_steps_match_oracle(name):
+    make, steps, policy = SCHED_CASES[name]
+    sc = make()
+    pu.log(f"scheduled fused {name}: N={sc.N} n={sc.n} steps={steps} policy={policy}")
+    gpu = pu.gpu_run(sc, steps, sort_policy=policy, fused=True)
+    orc, env = pu.envelope(sc, steps)
+    assert_particle_parity(sc, gpu, orc, env)
+    assert_grid_parity(sc, gpu, orc, tol=max(1e-5, 20 * env["v"]))
+    assert gpu["status"][0] == 0
+
+
+def test_scheduled_batches_single_steps_and_mode_changes():
+    """K = 4 without a budget: 21 steps as one call against single-step calls
+    with readbacks (lean graphs of every phase, the first full step under the
+    schedule), then the modes in turn (scheduled, device-decided, separate,
+    scheduled again), all against the oracle."""
+    sc = swirl(80, cscale=2.0)
+    steps = 21
+    a = pu.gpu_run(sc, steps, sort_policy=(4, 1 << 40), fused=True)
+    sim = mpm.Simulation(sc)
+    try:
+        sim.set_sort_policy(4, 1 << 40)
+        sim.set_fused_steps(True)
+        for k in range(steps):
+            sim.step(1)
+            if k in (2, 9):
+                mid = _read(sim)
+                orc, env = pu.envelope(sc, k + 1)
+                pu.log(f"scheduled: after {k + 1} single steps")
+                assert_particle_parity(sc, mid, orc, env)
+        b = _read(sim)
+    finally:
+        sim.close()
+    for f in ("x", "v", "C", "F", "m", "p"):
+        err = _rel(a[f], b[f])
+        pu.log(f"scheduled, {steps} steps batched vs single: {f} {err:.2e}")
+        assert err < 1e-5, (f, err)
+    orc, env = pu.envelope(sc, steps)
+    assert_particle_parity(sc, a, orc, env)
+
+    sim = mpm.Simulation(sc)
+    try:
+        sim.set_fused_steps(True)
+        sim.set_sort_policy(4, 1 << 40)  # scheduled
+        sim.step(6)
+        sim.set_sort_policy(3, 1 << 40)  # device-decided (3 is not a power of two)
+        sim.step(5)
+        sim.set_fused_steps(False)       # separate kernels
+        sim.step(3)
+        sim.set_fused_steps(True)
+        sim.set_sort_policy(2, 1 << 40)  # scheduled again, other interval
+        sim.step(9)
+        got = _read(sim)
+        got["status"] = sim.status()
+    finally:
+        sim.close()
+    orc, env = pu.envelope(sc, 23)
     assert_particle_parity(sc, got, orc, env)
     assert_grid_parity(sc, got, orc, tol=max(1e-5, 20 * env["v"]))
