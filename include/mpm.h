@@ -154,12 +154,16 @@ int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget
  * mpm_set_sort_policy) runs its G2P fused with the successor's P2G, so that
  * between sorts the state carried from step to step is x, F (or J) and the
  * modulus only.  The successor's sort decision is then taken one step
- * earlier, on the movers counted by the step before.  enable = 0 (the
- * default): separate P2G and G2P kernels.  Under the default policy (sort
- * every step) both settings run the same work.  The results equal those of
- * separate kernels up to the order of float additions; mpm_read_particles
- * and mpm_read_grid read the same state.  The first mpm_step after enabling
- * captures the fused graphs (host work, no device allocation).  A host-side
+ * earlier, on the movers counted by the step before.  With a power-of-two
+ * max_interval K <= 32 and a mover budget of at least the particle count,
+ * the sorts follow the step number instead (step n sorts when n mod K = 0,
+ * after one step that sorts or not by the policy), and a step after a
+ * fused pass launches the fused kernel alone.  enable = 0 (the default):
+ * separate P2G and G2P kernels.  Under the default policy (sort every step)
+ * both settings run the same work.  The results equal those of separate
+ * kernels up to the order of float additions; mpm_read_particles and
+ * mpm_read_grid read the same state.  The first mpm_step in a new setting
+ * captures its graphs (host work, no device allocation).  A host-side
  * setting: no stream.  enable outside {0, 1} returns MPM_ERR_INVALID_ARG. */
 int mpm_set_fused_steps(mpm_sim *sim, int32_t enable);
 
