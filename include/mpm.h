@@ -55,6 +55,7 @@ extern "C" {
 /* ---- materials ---- */
 #define MPM_FIXED_COROTATED 0 /* elastic solid, state F (3x3) */
 #define MPM_J_FLUID 1         /* weakly compressible fluid, state J (scalar) */
+#define MPM_SAND 2            /* Drucker-Prager sand, state F (3x3, elastic part) */
 
 /* ---- status word bits (see mpm_status) ---- */
 #define MPM_STATUS_NONFINITE 0x1u  /* a NaN or Inf appeared in particle velocity, C or position */
@@ -80,7 +81,8 @@ typedef struct mpm_sim mpm_sim;
  *                 used when no per-particle modulus is given.
  *   nu          : Poisson ratio, 0 <= nu < 0.5 (ignored for MPM_J_FLUID).
  *   rho, p_vol  : density and initial particle volume (> 0); particle mass
- *                 is rho * p_vol. */
+ *                 is rho * p_vol.
+ *   friction_deg: MPM_SAND only: friction angle in degrees, 0 < friction_deg < 90. */
 typedef struct {
   uint32_t struct_size;
   int32_t grid_n;
@@ -92,6 +94,7 @@ typedef struct {
   float nu;
   float rho;
   float p_vol;
+  float friction_deg;
 } mpm_params;
 
 /* Bytes of device workspace a simulation of n_particles needs (0 when the

@@ -28,6 +28,7 @@ MPM_ERR_STATE = -4
 
 MPM_FIXED_COROTATED = 0
 MPM_J_FLUID = 1
+MPM_SAND = 2
 
 MPM_STATUS_NONFINITE = 0x1
 MPM_STATUS_CLAMPED = 0x2
@@ -53,10 +54,11 @@ class MpmError(RuntimeError):
 class mpm_params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("grid_n", ctypes.c_int32), ("dt", ctypes.c_float),
                 ("gravity", ctypes.c_float * 3), ("wall_nodes", ctypes.c_int32), ("material", ctypes.c_int32),
-                ("E", ctypes.c_float), ("nu", ctypes.c_float), ("rho", ctypes.c_float), ("p_vol", ctypes.c_float)]
+                ("E", ctypes.c_float), ("nu", ctypes.c_float), ("rho", ctypes.c_float), ("p_vol", ctypes.c_float),
+                ("friction_deg", ctypes.c_float)]
 
 
-def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol) -> mpm_params:
+def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=30.0) -> mpm_params:
     p = mpm_params()
     p.struct_size = ctypes.sizeof(mpm_params)
     p.grid_n, p.dt = int(n), float(dt)
@@ -64,6 +66,7 @@ def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol) -> mpm_params
         p.gravity[a] = float(gravity[a])
     p.wall_nodes, p.material = int(wall), int(material)
     p.E, p.nu, p.rho, p.p_vol = float(E), float(nu), float(rho), float(p_vol)
+    p.friction_deg = float(friction_deg)
     return p
 
 

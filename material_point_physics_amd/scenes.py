@@ -27,6 +27,7 @@ import numpy as np
 
 FIXED_COROTATED = 0
 J_FLUID = 1
+SAND = 2
 
 
 @dataclass
@@ -50,6 +51,7 @@ class Scene:
     F: Optional[np.ndarray] = None   # (N,3,3) float32 initial deformation gradient (None -> I)
     J: Optional[np.ndarray] = None   # (N,) float32 initial volume ratio (None -> 1)
     extra: dict = field(default_factory=dict)
+    friction_deg: float = 30.0       # SAND: friction angle in degrees
 
     @property
     def N(self) -> int:
@@ -62,7 +64,7 @@ class Scene:
                     gravity=tuple(f32(g) for g in self.gravity),
                     wall=int(self.wall), material=int(self.material),
                     E=f32(self.E), nu=f32(self.nu), rho=f32(self.rho),
-                    p_vol=f32(self.p_vol))
+                    p_vol=f32(self.p_vol), friction_deg=f32(self.friction_deg))
 
 
 def _stratified(rng, cells: np.ndarray, ppc: int, dx: float) -> np.ndarray:
@@ -223,7 +225,7 @@ def random_rotation(rng, m: int) -> np.ndarray:
 def random_scene(N: int, n: int, seed: int, *, lo=None, hi=None, vscale=1.0,
                  cscale=0.0, fstretch=0.0, material=FIXED_COROTATED,
                  per_particle_E=False, dt=1e-4, gravity=(0.0, -9.8, 0.0),
-                 wall=3, E=1e4, nu=0.3, rho=1.0) -> Scene:
+                 wall=3, E=1e4, nu=0.3, rho=1.0, friction_deg=30.0) -> Scene:
     """A generic seeded scene for parity and edge-case tests.
 
     Positions are i.i.d. uniform in the box [lo, hi] (default: the region
@@ -257,4 +259,5 @@ def random_scene(N: int, n: int, seed: int, *, lo=None, hi=None, vscale=1.0,
     return Scene(f"random_{N}_{n}_{seed}", "random test scene",
                  x.astype(np.float32), v.astype(np.float32), E_p,
                  n=n, dt=dt, gravity=tuple(gravity), wall=wall, material=material,
-                 E=E, nu=nu, rho=rho, p_vol=dx ** 3 / 4, steps=1, C=C, F=F, J=J)
+                 E=E, nu=nu, rho=rho, p_vol=dx ** 3 / 4, steps=1, C=C, F=F, J=J,
+                 friction_deg=friction_deg)

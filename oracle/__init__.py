@@ -39,7 +39,8 @@ class OrcParams(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("wall", ctypes.c_int32), ("material", ctypes.c_int32),
                 ("pad", ctypes.c_int32), ("dt", ctypes.c_double),
                 ("gravity", ctypes.c_double * 3), ("E", ctypes.c_double),
-                ("nu", ctypes.c_double), ("rho", ctypes.c_double), ("p_vol", ctypes.c_double)]
+                ("nu", ctypes.c_double), ("rho", ctypes.c_double), ("p_vol", ctypes.c_double),
+                ("friction_deg", ctypes.c_double)]
 
 
 _loaded = {}
@@ -64,6 +65,11 @@ def lib(prec: str = "f64") -> ctypes.CDLL:
     L.orc_kirchhoff_fc.argtypes = [P, R, R, P]
     L.orc_kirchhoff_fluid.argtypes = [R, R]
     L.orc_kirchhoff_fluid.restype = R
+    L.orc_sand_alpha.argtypes = [R]
+    L.orc_sand_alpha.restype = R
+    L.orc_sand_project.argtypes = [P, R, R]
+    L.orc_sand_project.restype = ctypes.c_int
+    L.orc_kirchhoff_sand.argtypes = [P, R, R, P]
     pp = ctypes.POINTER(OrcParams)
     L.orc_grid_clear.argtypes = [pp, P, P]
     L.orc_p2g.argtypes = [pp, ctypes.c_int64, P, P, P, P, P, P, P, P]
@@ -78,13 +84,14 @@ def lib(prec: str = "f64") -> ctypes.CDLL:
     return L
 
 
-def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol) -> OrcParams:
+def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=30.0) -> OrcParams:
     P = OrcParams()
     P.n, P.wall, P.material, P.pad = int(n), int(wall), int(material), 0
     P.dt = float(dt)
     for a in range(3):
         P.gravity[a] = float(gravity[a])
     P.E, P.nu, P.rho, P.p_vol = float(E), float(nu), float(rho), float(p_vol)
+    P.friction_deg = float(friction_deg)
     return P
 
 
@@ -143,6 +150,21 @@ class Oracle:
 
     def kirchhoff_fluid(self, J, K):
         return float(self.L.orc_kirchhoff_fluid(J, K))
+
+    def sand_alpha(self, friction_deg):
+        return float(self.L.orc_sand_alpha(friction_deg))
+
+    def sand_project(self, F, nu, alpha):
+        """Returns (projected F, case: 0 unchanged, 1 tip, 2 cone surface)."""
+        F = self.arr(F, (3, 3)).copy()
+        kind = int(self.L.orc_sand_project(_ptr(F, self.prec), nu, alpha))
+        return F, kind
+
+    def kirchhoff_sand(self, F, mu, lam):
+        F = self.arr(F, (3, 3))
+        tau = np.zeros((3, 3), self.dtype)
+        self.L.orc_kirchhoff_sand(_ptr(F, self.prec), mu, lam, _ptr(tau, self.prec))
+        return tau
 
 
 class OracleSim:

@@ -12,7 +12,10 @@
  * moving least squares material point method with displacement discontinuity
  * and two-way rigid body coupling"; Jiang et al. 2015, "The affine
  * particle-in-cell method"), with the fixed-corotated elastic model
- * (Stomakhin et al. 2012).  Each step below names the passage of [RT-MPM] it
+ * (Stomakhin et al. 2012), and for sand the Drucker-Prager plasticity of
+ * Klar et al. 2016 ("Drucker-Prager elastoplasticity for sand animation":
+ * Hencky-strain elasticity and its return mapping, here with a constant
+ * friction angle).  Each step below names the passage of [RT-MPM] it
  * matches:
  *   - P2G adds weighted mass and momenta to grid nodes            [RT-MPM §4.3]
  *   - three quadratic B-spline weights per axis ("nine floats")   [RT-MPM, on-chip
@@ -46,7 +49,7 @@ typedef ORC_REAL real;
 typedef struct {
   int32_t n;          /* grid nodes per axis */
   int32_t wall;       /* sticky-wall thickness, in nodes */
-  int32_t material;   /* 0 fixed-corotated elastic, 1 weakly compressible fluid */
+  int32_t material;   /* 0 fixed-corotated elastic, 1 weakly compressible fluid, 2 sand */
   int32_t pad;
   double dt;
   double gravity[3];
@@ -54,6 +57,7 @@ typedef struct {
   double nu;          /* Poisson ratio */
   double rho;         /* density */
   double p_vol;       /* initial particle volume V0 */
+  double friction_deg; /* sand: friction angle, degrees */
 } orc_params;
 
 int orc_real_bytes(void) { return (int)sizeof(real); }
@@ -251,6 +255,101 @@ void orc_kirchhoff_fc(const real F[9], real mu, real lam, real tau[9]) {
  * tau = -p J I = K J (J - 1) I.  Returns the diagonal value. */
 real orc_kirchhoff_fluid(real J, real K) { return K * J * (J - 1); }
 
+/* ------------------------------------------------------------------ sand
+ * Drucker-Prager elastoplasticity in Hencky strain (Klar et al. 2016), with
+ * unsigned singular values: F^T F = V diag(l) V^T, s_i = sqrt(l_i), and the
+ * principal Hencky strain e_i = ln s_i = ln(l_i) / 2.  A value l_i below
+ * ORC_SAND_LFLOOR is taken as that floor (an element crushed to less than
+ * 1/1000 of its length along a principal axis). */
+#define ORC_SAND_LFLOOR 1e-6
+
+/* Principal strains of F: V (eigenvectors of F^T F as columns), l (its
+ * eigenvalues, floored) and e = ln(l) / 2. */
+static void sand_principal(const real F[9], real V[9], real l[3], real e[3]) {
+  real S[9];
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c) {
+      real a = 0;
+      for (int k = 0; k < 3; ++k) a += F[k * 3 + r] * F[k * 3 + c];
+      S[r * 3 + c] = a;
+    }
+  jacobi_eigen_sym3(S, V);
+  for (int i = 0; i < 3; ++i) {
+    l[i] = S[i * 4] > (real)ORC_SAND_LFLOOR ? S[i * 4] : (real)ORC_SAND_LFLOOR;
+    e[i] = (real)0.5 * log(l[i]);
+  }
+}
+
+/* F V diag(m) V^T: F with its principal stretches s_i scaled by m_i. */
+static void sand_scale(const real F[9], const real V[9], const real m[3], real out[9]) {
+  real M[9];
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c) M[r * 3 + c] = V[r * 3 + 0] * m[0] * V[c * 3 + 0] + V[r * 3 + 1] * m[1] * V[c * 3 + 1] +
+                                           V[r * 3 + 2] * m[2] * V[c * 3 + 2];
+  real t[9];
+  mat_mul(F, M, t);
+  for (int i = 0; i < 9; ++i) out[i] = t[i];
+}
+
+/* Cone slope alpha = sqrt(2/3) 2 sin(phi) / (3 - sin(phi)) of the friction
+ * angle phi (degrees). */
+real orc_sand_alpha(real friction_deg) {
+  const real sp = sin(friction_deg * (real)3.14159265358979323846 / 180);
+  return sqrt((real)2 / 3) * 2 * sp / (3 - sp);
+}
+
+/* Return mapping of F (in place) onto the Drucker-Prager cone in principal
+ * Hencky strain e:  with the trace t = sum e and the deviator d = e - t/3,
+ *   t > 0   : expansion, projected to the cone's tip, e = 0 (F -> U V^T);
+ *   else, with g = |d| + (3 lam + 2 mu) / (2 mu) t alpha
+ *   g <= 0  : inside the cone, unchanged (this includes a purely volumetric
+ *             compression, d = 0, which the published mapping sends to the
+ *             tip with the expansions);
+ *   g > 0   : e <- e - g d / |d| (onto the cone's surface; |d| > 0 here).
+ * (3 lam + 2 mu) / (2 mu) = (1 + nu) / (1 - 2 nu) depends on nu only.
+ * Returns 0 (unchanged), 1 (tip) or 2 (surface). */
+int orc_sand_project(real F[9], real nu, real alpha) {
+  real V[9], l[3], e[3];
+  sand_principal(F, V, l, e);
+  const real t = e[0] + e[1] + e[2];
+  real d[3], nd2 = 0;
+  for (int i = 0; i < 3; ++i) {
+    d[i] = e[i] - t / 3;
+    nd2 += d[i] * d[i];
+  }
+  const real nd = sqrt(nd2);
+  real h[3];
+  int kind;
+  if (t > 0) {
+    kind = 1;
+    for (int i = 0; i < 3; ++i) h[i] = 0;
+  } else {
+    const real g = nd + (1 + nu) / (1 - 2 * nu) * t * alpha;
+    if (g <= 0) return 0;
+    kind = 2;
+    for (int i = 0; i < 3; ++i) h[i] = e[i] - g * d[i] / nd;
+  }
+  real m[3];
+  for (int i = 0; i < 3; ++i) m[i] = exp(h[i] - e[i]); /* new stretch / old stretch */
+  sand_scale(F, V, m, F);
+  return kind;
+}
+
+/* Kirchhoff stress of the Hencky (St. Venant-Kirchhoff in log strain)
+ * energy psi = mu sum e_i^2 + lam/2 (sum e_i)^2:
+ *   tau = U diag(2 mu e_i + lam sum e) U^T,  U = F V diag(1/s),
+ * i.e. tau = F V diag((2 mu e_i + lam sum e) / l_i) V^T F^T. */
+void orc_kirchhoff_sand(const real F[9], real mu, real lam, real tau[9]) {
+  real V[9], l[3], e[3];
+  sand_principal(F, V, l, e);
+  const real t = e[0] + e[1] + e[2];
+  real m[3];
+  for (int i = 0; i < 3; ++i) m[i] = (2 * mu * e[i] + lam * t) / l[i];
+  real G[9];
+  sand_scale(F, V, m, G);
+  mat_mul_bt(G, F, tau);
+}
+
 /* ------------------------------------------------------------ MPM phases */
 
 static int64_t node_index(int64_t n, int64_t i, int64_t j, int64_t k) { return i + n * (j + n * k); }
@@ -276,8 +375,9 @@ void orc_grid_clear(const orc_params *P, real *gm, real *gp) {
 }
 
 /* Particle-to-grid transfer, particles in index order.  Adds into gm (mass)
- * and gp (momentum).  For the elastic material F holds the deformation
- * gradients; for the fluid J holds the volume ratios.  E_p may be NULL.
+ * and gp (momentum).  For the elastic materials (fixed-corotated, sand) F
+ * holds the deformation gradients; for the fluid J holds the volume ratios.
+ * E_p may be NULL.
  * Returns the number of particles skipped because their stencil left the
  * grid (0 for valid input). */
 int64_t orc_p2g(const orc_params *P, int64_t N, const real *x, const real *v, const real *C,
@@ -296,6 +396,10 @@ int64_t orc_p2g(const orc_params *P, int64_t N, const real *x, const real *v, co
     if (P->material == 1) {
       real t = orc_kirchhoff_fluid(J[p], E);
       for (int i = 0; i < 9; ++i) tau[i] = (i % 4 == 0) ? t : 0;
+    } else if (P->material == 2) {
+      real mu, lam;
+      orc_lame(E, (real)P->nu, &mu, &lam);
+      orc_kirchhoff_sand(F + 9 * p, mu, lam, tau);
     } else {
       real mu, lam;
       orc_lame(E, (real)P->nu, &mu, &lam);
@@ -339,8 +443,9 @@ void orc_grid_update(const orc_params *P, const real *gm, const real *gp, real *
 }
 
 /* Grid-to-particle transfer with the APIC affine matrix, deformation-gradient
- * (or volume-ratio) update, advection and the position clamp to
- * [2dx, (n-2)dx].  Returns the number of clamped components. */
+ * (or volume-ratio) update (for sand followed by the plasticity projection),
+ * advection and the position clamp to [2dx, (n-2)dx].  Returns the number of
+ * clamped components. */
 int64_t orc_g2p(const orc_params *P, int64_t N, real *x, real *v, real *C, real *F, real *J,
                 const real *gv) {
   const real dx = (real)1 / (real)P->n;
@@ -373,6 +478,9 @@ int64_t orc_g2p(const orc_params *P, int64_t N, real *x, real *v, real *C, real 
       J[p] = J[p] * mat_det(G);
     } else {
       mat_mul(G, F + 9 * p, F + 9 * p);
+      /* sand: the plasticity projection of the updated F ([RT-MPM] merges the
+       * SVD, the plasticity projection and the stress into one particle phase) */
+      if (P->material == 2) orc_sand_project(F + 9 * p, (real)P->nu, orc_sand_alpha((real)P->friction_deg));
     }
     for (int i = 0; i < 9; ++i) C[9 * p + i] = Cn[i];
     for (int a = 0; a < 3; ++a) {

@@ -118,5 +118,15 @@ def test_error_strings_and_kernel_names():
 
 
 def test_params_struct_matches_header():
-    # uint32 + int32 + float + float[3] + int32 + int32 + 4 floats = 48 bytes
-    assert ctypes.sizeof(mpm.mpm_params) == 48
+    # the binding's fields are the header's, in order, with the same C types
+    import re
+    hdr = open(os.path.join(ROOT, "include", "mpm.h")).read()
+    body = re.search(r"typedef struct \{(.*?)\} mpm_params;", hdr, re.S).group(1)
+    decl = [re.match(r"\s*(\w+)\s+(\w+)(\[\d+\])?;", l).groups() for l in body.strip().splitlines()]
+    ctype = {"uint32_t": ctypes.c_uint32, "int32_t": ctypes.c_int32, "float": ctypes.c_float}
+    assert [f[0] for f in mpm.mpm_params._fields_] == [d[1] for d in decl]
+    for (name, ct), (ty, _, arr) in zip(mpm.mpm_params._fields_, decl):
+        want = ctype[ty] * int(arr[1:-1]) if arr else ctype[ty]
+        assert ctypes.sizeof(ct) == ctypes.sizeof(want), name
+    # uint32 + int32 + float + float[3] + int32 + int32 + 5 floats = 52 bytes
+    assert ctypes.sizeof(mpm.mpm_params) == 52

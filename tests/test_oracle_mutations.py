@@ -52,6 +52,17 @@ MUTANTS = [
     ("G2P advects with pre-gravity velocity", "real xa = x[3 * p + a] + dt * vn[a];",
      "real xa = x[3 * p + a] + dt * (vn[a] - dt * (real)P->gravity[a]);"),
     ("G2P velocity of neighbour axis", "vn[a] += wt * vi[a];", "vn[a] += wt * vi[(a + 1) % 3];"),
+    ("sand tip on compression", "  if (t > 0) {\n    kind = 1;", "  if (t < 0) {\n    kind = 1;"),
+    ("sand cone factor doubled", "const real g = nd + (1 + nu) / (1 - 2 * nu) * t * alpha;",
+     "const real g = nd + 2 * (1 + nu) / (1 - 2 * nu) * t * alpha;"),
+    ("sand strain without the half", "e[i] = (real)0.5 * log(l[i]);", "e[i] = log(l[i]);"),
+    ("sand stress drops lambda", "m[i] = (2 * mu * e[i] + lam * t) / l[i];", "m[i] = (2 * mu * e[i]) / l[i];"),
+    ("sand alpha with cos", "const real sp = sin(friction_deg", "const real sp = cos(friction_deg"),
+    ("sand projection moves the trace", "h[i] = e[i] - g * d[i] / nd;", "h[i] = e[i] - g * e[i] / nd;"),
+    ("sand no projection in G2P", "if (P->material == 2) orc_sand_project(", "if (0) orc_sand_project("),
+    ("sand stress of the fixed-corotated model", "orc_kirchhoff_sand(F + 9 * p, mu, lam, tau);",
+     "orc_kirchhoff_fc(F + 9 * p, mu, lam, tau);"),
+    ("sand stretch scaled inversely", "m[i] = exp(h[i] - e[i]);", "m[i] = exp(e[i] - h[i]);"),
 ]
 
 
@@ -75,6 +86,12 @@ def _all_pins():
         lambda o: pins.test_walls_zero_velocity(),
         lambda o: pins.test_stress_force_is_energy_gradient(),
         lambda o: pins.test_fluid_J_matches_det_F(),
+        pins.test_sand_alpha_is_the_mohr_coulomb_fit,
+        pins.test_sand_stress_closed_form_and_energy,
+        pins.test_sand_projection_cases,
+        pins.test_sand_projection_is_objective,
+        lambda o: pins.test_sand_step_projects_in_g2p(),
+        lambda o: pins.test_sand_stress_force_is_energy_gradient(),
     ]
     del rng
     return out

@@ -355,3 +355,178 @@ def test_fluid_J_matches_det_F():
         fl.step()
     assert np.allclose(fl.J, np.linalg.det(el.F), rtol=1e-12)
     assert np.allclose(fl.x, el.x, atol=1e-15)
+
+
+# ------------------------------------------------------------ sand pins
+# Drucker-Prager sand in Hencky strain (Klar et al. 2016).  The energy, the
+# yield cone in stress space and the closed forms below are written from
+# numpy's SVD, independently of the oracle's eigen-decomposition.
+
+def _hencky_tau(F, mu, lam):
+    u, s, vt = np.linalg.svd(F)
+    e = np.log(s)
+    return u @ np.diag(2 * mu * e + lam * e.sum()) @ u.T
+
+
+def _psi_sand(F, mu, lam):
+    e = np.log(np.linalg.svd(F, compute_uv=False))
+    return mu * np.sum(e ** 2) + 0.5 * lam * e.sum() ** 2
+
+
+def _dp_yield(tau, friction_deg):
+    """Drucker-Prager yield value a I1 + sqrt(J2) - 0 of a Kirchhoff stress,
+    with a = 2 sin(phi) / (sqrt(3) (3 - sin(phi))), the cone through the
+    compressive meridian of the Mohr-Coulomb surface (the textbook fit).
+    <= 0 inside the cone (compression is negative)."""
+    sp = np.sin(np.radians(friction_deg))
+    a = 2 * sp / (np.sqrt(3) * (3 - sp))
+    i1 = np.trace(tau)
+    dev = tau - i1 / 3 * np.eye(3)
+    return a * i1 + np.sqrt(0.5 * np.sum(dev * dev))
+
+
+def test_sand_alpha_is_the_mohr_coulomb_fit(orc64):
+    """The strain-space cone slope alpha, divided by sqrt(2), is the textbook
+    Drucker-Prager parameter in the (I1, sqrt(J2)) form: ||dev tau|| =
+    sqrt(2 J2).  No friction gives no cone."""
+    assert orc64.sand_alpha(0.0) == 0.0
+    for phi in [10.0, 25.0, 30.0, 35.0, 45.0]:
+        sp = np.sin(np.radians(phi))
+        a = 2 * sp / (np.sqrt(3) * (3 - sp))
+        assert np.isclose(orc64.sand_alpha(phi) / np.sqrt(2), a, rtol=1e-12)
+
+
+def test_sand_stress_closed_form_and_energy(orc64):
+    """tau = U diag(2 mu ln s + lam sum ln s) U^T, and tau = P F^T with P the
+    finite-difference derivative of psi = mu sum (ln s)^2 + lam/2 (sum ln s)^2."""
+    rng = np.random.default_rng(300)
+    mu, lam = 2.0, 3.0
+    assert np.allclose(orc64.kirchhoff_sand(np.eye(3), mu, lam), 0, atol=1e-14)
+    R = scenes.random_rotation(rng, 1)[0]
+    assert np.allclose(orc64.kirchhoff_sand(R, mu, lam), 0, atol=1e-12)
+    for _ in range(8):
+        F = _rand_F(rng)
+        assert np.allclose(orc64.kirchhoff_sand(F, mu, lam), _hencky_tau(F, mu, lam), atol=1e-10)
+        h = 1e-6
+        P = np.zeros((3, 3))
+        for r in range(3):
+            for c in range(3):
+                Fp, Fm = F.copy(), F.copy()
+                Fp[r, c] += h
+                Fm[r, c] -= h
+                P[r, c] = (_psi_sand(Fp, mu, lam) - _psi_sand(Fm, mu, lam)) / (2 * h)
+        assert np.allclose(orc64.kirchhoff_sand(F, mu, lam), P @ F.T, atol=1e-7)
+
+
+def _dp_F(rng, s):
+    U, V = scenes.random_rotation(rng, 2)
+    return U @ np.diag(s) @ V.T, U, V
+
+
+def test_sand_projection_cases(orc64):
+    """Tension goes to the cone's tip (F becomes the rotation U V^T); a state
+    inside the cone is unchanged; a state outside lands on the cone: its
+    stress satisfies the yield condition with equality, its log-volume (trace
+    of the Hencky strain) and its singular vectors are kept, the deviator
+    keeps its direction; projecting again changes nothing."""
+    rng = np.random.default_rng(301)
+    nu, phi, mu = 0.3, 30.0, 1.0
+    lam = 2 * mu * nu / (1 - 2 * nu)
+    alpha = orc64.sand_alpha(phi)
+    # tension
+    F, U, V = _dp_F(rng, [1.02, 1.01, 0.999])
+    G, kind = orc64.sand_project(F, nu, alpha)
+    assert kind == 1 and np.allclose(G, U @ V.T, atol=1e-12)
+    # inside the cone: compression with a small deviator
+    F, U, V = _dp_F(rng, [0.99, 0.985, 0.988])
+    assert _dp_yield(_hencky_tau(F, mu, lam), phi) < 0
+    G, kind = orc64.sand_project(F, nu, alpha)
+    assert kind == 0 and np.array_equal(G, F)
+    # outside: compression with a large deviator
+    for s in ([1.02, 0.99, 0.96], [1.03, 1.0, 0.96], [1.01, 0.999, 0.975]):
+        F, U, V = _dp_F(rng, s)
+        assert _dp_yield(_hencky_tau(F, mu, lam), phi) > 0
+        G, kind = orc64.sand_project(F, nu, alpha)
+        assert kind == 2
+        y = _dp_yield(_hencky_tau(G, mu, lam), phi)
+        assert abs(y) < 1e-12 * np.abs(_hencky_tau(F, mu, lam)).max() + 1e-14
+        e0 = np.log(np.asarray(s))
+        e1 = np.log(np.diag(U.T @ G @ V))              # same singular vectors
+        assert np.allclose(U.T @ G @ V, np.diag(np.exp(e1)), atol=1e-12)
+        assert np.isclose(e1.sum(), e0.sum(), atol=1e-13)
+        d0, d1 = e0 - e0.mean(), e1 - e1.mean()
+        assert np.allclose(d1 / np.linalg.norm(d1), d0 / np.linalg.norm(d0), atol=1e-10)
+        assert np.linalg.norm(d1) < np.linalg.norm(d0)
+        G2, kind2 = orc64.sand_project(G, nu, alpha)
+        assert np.allclose(G2, G, atol=1e-12)
+
+
+def test_sand_projection_is_objective(orc64):
+    """project(Q F) = Q project(F) and project(F Q) = project(F) Q."""
+    rng = np.random.default_rng(302)
+    alpha = orc64.sand_alpha(35.0)
+    for s in ([1.02, 0.99, 0.96], [1.03, 1.0, 0.99], [0.99, 0.985, 0.988]):
+        F, _, _ = _dp_F(rng, s)
+        Q = scenes.random_rotation(rng, 1)[0]
+        G, k = orc64.sand_project(F, 0.25, alpha)
+        GQ, kq = orc64.sand_project(Q @ F, 0.25, alpha)
+        QG, kr = orc64.sand_project(F @ Q, 0.25, alpha)
+        assert k == kq == kr
+        assert np.allclose(GQ, Q @ G, atol=1e-11) and np.allclose(QG, G @ Q, atol=1e-11)
+
+
+def test_sand_step_projects_in_g2p():
+    """A step of sand started with C = c I (no gravity): under expansion the
+    updated F is projected to the cone's tip, a rotation; under compression
+    (the gathered C is close to c I, so the deviator stays small) it stays
+    inside the cone and equals (I + dt C) F exactly."""
+    for c, tip in ((40.0, True), (-40.0, False)):
+        sc = scenes.random_scene(50, 16, 17, lo=[0.4] * 3, hi=[0.6] * 3, vscale=0.0, gravity=(0, 0, 0),
+                                 wall=0, material=scenes.SAND, E=100.0, friction_deg=30.0)
+        sc.C = np.tile(c * np.eye(3, dtype=np.float32), (sc.N, 1, 1))
+        sim = oracle.OracleSim(sc, "f64")
+        sim.p2g()
+        sim.grid_update()
+        sim.g2p()
+        s = np.linalg.svd(sim.F, compute_uv=False)
+        if tip:
+            assert np.allclose(s, 1.0, atol=1e-12)
+        else:
+            G = np.eye(3) + sc.dt * sim.C
+            assert np.allclose(sim.F, G, atol=1e-14)
+            assert np.all(np.linalg.det(sim.F) < 1.0)
+
+
+def test_sand_stress_force_is_energy_gradient():
+    """Work conjugacy for sand inside the cone (no projection for small grid
+    displacements): P2G's stress momentum is dt f with f = -dE/du, E the
+    Hencky energy of the G2P-updated F."""
+    n = 16
+    rng = np.random.default_rng(303)
+    sc = scenes.random_scene(3, n, 18, lo=[0.4] * 3, hi=[0.6] * 3, vscale=0.0, gravity=(0, 0, 0), wall=0,
+                             material=scenes.SAND, E=50.0, nu=0.3, friction_deg=40.0)
+    # initial F: compression inside the cone
+    sc.F = np.stack([_dp_F(rng, [0.97, 0.975, 0.972])[0] for _ in range(sc.N)]).astype(np.float32)
+    P = sc.params()
+    sim = oracle.OracleSim(sc, "f64")
+    mu, lam = sim.orc.lame(P["E"], P["nu"])
+    dt = P["dt"]
+    sim.p2g()
+    force = sim.gp / dt
+
+    def energy(u_nodes):
+        s2 = oracle.OracleSim(sc, "f64")
+        s2.gv[:] = u_nodes / dt
+        s2.g2p()
+        return sum(P["p_vol"] * _psi_sand(s2.F[p], mu, lam) for p in range(sc.N))
+
+    touched = np.nonzero(sim.gm > 0)[0]
+    h = 1e-7
+    for node in rng.choice(touched, 10, replace=False):
+        for a in range(3):
+            up = np.zeros((n ** 3, 3))
+            um = np.zeros((n ** 3, 3))
+            up[node, a] = h
+            um[node, a] = -h
+            dE = (energy(up) - energy(um)) / (2 * h)
+            assert abs(force[node, a] + dE) <= 1e-6 * np.abs(force).max() + 1e-12
