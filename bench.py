@@ -39,7 +39,7 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
                  fused=False) -> dict:
     """Algorithmic HBM bytes per launch of each kernel (what the method must
     move through that kernel; see the byte model in the design notes).
-    fp32 everywhere; F is 9 floats (elastic) or 1 (fluid J).  With
+    fp32 everywhere; F is 9 floats (elastic, sand) or 1 (fluid J).  With
     sorted_steps=False (free-zone steps without a sort) the scatter moves
     nothing and P2G reads the key word (4 B) instead of perm and the cell
     byte (5 B).  With fused=True (fused steps without a sort) the separate
@@ -47,7 +47,7 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
     back, plus v and C (stored on the last step of each launch, and on every
     profiled step), and per active node reads the window once, writes the
     next accumulator and clears the one of two steps before."""
-    f = 36 if material == 0 else 4
+    f = 4 if material == 1 else 36  # fluid J, else F (elastic, sand)
     e = 4 if has_E else 0
     if fused:
         kb = kernel_bytes(N, active_nodes, nbins, material, has_E, sorted_steps=False)
@@ -243,7 +243,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{sc.name}: {sc.description}", "particles": sc.N, "grid": f"{n}^3",
-                   "dt": sc.dt, "material": "fixed-corotated" if sc.material == 0 else "J-fluid",
+                   "dt": sc.dt, "material": {0: "fixed-corotated", 1: "J-fluid", 2: "Drucker-Prager sand"}[sc.material],
                    "sort": (f"free zone: at least every {args.sort_interval} steps or above {budget} movers "
                             "(byte model assumes no sort in the timed steps)") if free_zone else "every step",
                    "fused_g2p2g": bool(args.fused)},

@@ -114,6 +114,7 @@ struct SimDev {
   float g[3];
   float mass, vol, E;
   float mu_per_E, lam_per_E;  // Lame parameters per unit Young's modulus
+  float alpha, dp_c;          // sand: cone slope of the friction angle, (1 + nu) / (1 - 2 nu)
   float stress_k;             // dt * V0 * 4 / dx^2
   float c_scale;              // 4 / dx (G2P: C = 4/dx^2 * sum w v (x_i - x_p), offsets in cells)
   float lo, hi;               // position clamp
@@ -873,6 +874,138 @@ __device__ __forceinline__ uint32_t affine_momentum(const SimDev &s, const float
   return st;
 }
 
+// ------------------------------------------------------------------ sand
+// Drucker-Prager elastoplasticity in Hencky strain (Klar et al. 2016,
+// "Drucker-Prager elastoplasticity for sand animation"), with a constant
+// friction angle.  [RT-MPM] merges the SVD, the plasticity projection and
+// the stress into the particle phase of P2G; so does the sand instance of
+// P2G here, after the deferred F update.  Principal stretches are unsigned:
+// F^T F = V diag(l) V^T, s = sqrt(l), Hencky strain e = ln(l) / 2, with l
+// floored at 1e-6 (an element crushed below 1/1000 of its length).
+
+// Eigen-decomposition of a symmetric 3x3 matrix by cyclic Jacobi rotations
+// (Rutishauser's formulation, Golub & Van Loan, "Matrix Computations"):
+// A becomes diagonal, W's columns the eigenvectors.
+__device__ __forceinline__ void eigen_sym3(float a[3][3], float W[3][3]) {
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) W[r][c] = (r == c) ? 1.f : 0.f;
+  for (int sweep = 0; sweep < 10; ++sweep) {
+    const float off = a[0][1] * a[0][1] + a[0][2] * a[0][2] + a[1][2] * a[1][2];
+    const float dia = a[0][0] * a[0][0] + a[1][1] * a[1][1] + a[2][2] * a[2][2];
+    if (off <= 1e-14f * dia) break;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int p = k == 2 ? 1 : 0, q = k == 0 ? 1 : 2;
+      const float apq = a[p][q];
+      if (apq == 0.f) continue;
+      const float theta = (a[q][q] - a[p][p]) / (2.f * apq);
+      const float t = copysignf(1.f, theta) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+      const float c = rsqrtf(t * t + 1.f), sn = t * c;
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {  // columns p, q
+        const float xp = a[r][p], xq = a[r][q];
+        a[r][p] = c * xp - sn * xq;
+        a[r][q] = sn * xp + c * xq;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {  // rows p, q
+        const float xp = a[p][r], xq = a[q][r];
+        a[p][r] = c * xp - sn * xq;
+        a[q][r] = sn * xp + c * xq;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const float xp = W[r][p], xq = W[r][q];
+        W[r][p] = c * xp - sn * xq;
+        W[r][q] = sn * xp + c * xq;
+      }
+    }
+  }
+}
+
+// F V diag(m) V^T (F with its principal stretches scaled by m).
+__device__ __forceinline__ void stretch_scaled(const float F[9], const float W[3][3], const float m[3], float out[9]) {
+  float M[9];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      M[r * 3 + c] = W[r][0] * m[0] * W[c][0] + W[r][1] * m[1] * W[c][1] + W[r][2] * m[2] * W[c][2];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      out[r * 3 + c] = F[r * 3 + 0] * M[0 * 3 + c] + F[r * 3 + 1] * M[1 * 3 + c] + F[r * 3 + 2] * M[2 * 3 + c];
+}
+
+// Sand, per particle: the plasticity projection of F (in place, when
+// project) and the APIC affine momentum A = m C - dt V0 (4/dx^2) tau with the
+// Hencky Kirchhoff stress tau = U diag(2 mu h + lam sum h) U^T of the
+// projected principal strains h (U = F V diag(1/s) is unchanged by the
+// projection, so tau is formed from the trial F and its l).  Return
+// mapping, with t = sum e and the deviator d = e - t/3: t > 0 -> tip
+// (h = 0); else g = |d| + (1 + nu)/(1 - 2 nu) t alpha, g <= 0 -> unchanged,
+// g > 0 -> h = e - g d / |d|.  Returns status bits (det F <= 0).
+__device__ __forceinline__ uint32_t sand_affine(const SimDev &s, float Fp[9], float E, const float Cp[9], float A[9],
+                                                bool project) {
+  float a[3][3], W[3][3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) a[r][c] = Fp[0 * 3 + r] * Fp[0 * 3 + c] + Fp[1 * 3 + r] * Fp[1 * 3 + c] + Fp[2 * 3 + r] * Fp[2 * 3 + c];
+  eigen_sym3(a, W);
+  float l[3], e[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    l[i] = fmaxf(a[i][i], 1e-6f);
+    e[i] = 0.5f * logf(l[i]);
+  }
+  const uint32_t st = det3(Fp) > 0.f ? 0u : (uint32_t)MPM_STATUS_INVERTED;
+  float h[3] = {e[0], e[1], e[2]};
+  bool moved = false;
+  if (project) {
+    const float t = e[0] + e[1] + e[2];
+    const float d[3] = {e[0] - t / 3.f, e[1] - t / 3.f, e[2] - t / 3.f};
+    const float nd = sqrtf(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    if (t > 0.f) {
+      h[0] = h[1] = h[2] = 0.f;
+      moved = true;
+    } else {
+      const float g = nd + s.dp_c * t * s.alpha;
+      if (g > 0.f) {
+        const float k = g / nd;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) h[i] = e[i] - k * d[i];
+        moved = true;
+      }
+    }
+  }
+  // tau = F V diag((2 mu h + lam sum h) / l) V^T F^T, F the trial F
+  const float mu = E * s.mu_per_E, lam = E * s.lam_per_E, ht = h[0] + h[1] + h[2];
+  float q[3], G[9];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) q[i] = (2.f * mu * h[i] + lam * ht) / l[i];
+  stretch_scaled(Fp, W, q, G);
+#pragma unroll
+  for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) {
+      const float tau = G[r2 * 3 + 0] * Fp[c2 * 3 + 0] + G[r2 * 3 + 1] * Fp[c2 * 3 + 1] + G[r2 * 3 + 2] * Fp[c2 * 3 + 2];
+      A[r2 * 3 + c2] = s.mass * Cp[r2 * 3 + c2] - s.stress_k * tau;
+    }
+  if (moved) {  // F becomes the projected one: its stretches scaled by exp(h - e)
+    float m[3], Fn[9];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) m[i] = expf(h[i] - e[i]);
+    stretch_scaled(Fp, W, m, Fn);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
+  }
+  return st;
+}
+
 // Base node b = floor(x/dx - 1/2), fractional offset f and quadratic
 // B-spline weights w[axis][o] of a position.
 __device__ __forceinline__ void particle_weights(const float xp[3], float fn, int b[3], float f[3], float w[3][3]) {
@@ -1281,13 +1414,16 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
       if (pending) update_F<MAT>(Fp, Cp, dt);
       const float E = HAS_E ? at_byte(in.E, io) : s.E;
+      float A[9];
+      uint32_t st = 0;
+      // sand: the plasticity projection of the updated F, with the stress
+      if (MAT == MPM_SAND) st = sand_affine(s, Fp, E, Cp, A, pending);
       if (valid) {
 #pragma unroll
         for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
         if (HAS_E) stream_store(E, at_byte(out.E, od));
       }
-      float A[9];
-      const uint32_t st = affine_momentum<MAT>(s, Fp, E, Cp, A);
+      if (MAT != MPM_SAND) st = affine_momentum<MAT>(s, Fp, E, Cp, A);
       if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
       int b[3];
       float f[3], w[3][3], q0[3], Ad[9];
@@ -1721,6 +1857,9 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
       // P2G of step n + 1: F update with the new C, stress, deposit at xn
       update_F<MAT>(Fp, Cn, dt);
+      float A[9];
+      uint32_t st = 0;
+      if (MAT == MPM_SAND) st = sand_affine(s, Fp, E, Cn, A, true);  // projection and stress
       if (valid) {
 #pragma unroll
         for (int k = 0; k < 3; ++k) at_byte(out.x + k * Np, so) = xn[k];
@@ -1736,8 +1875,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
         if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
-      float A[9];
-      const uint32_t st = affine_momentum<MAT>(s, Fp, E, Cn, A);
+      if (MAT != MPM_SAND) st = affine_momentum<MAT>(s, Fp, E, Cn, A);
       if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
       int b[3];
       float f[3], w[3][3], q0[3], Ad[9];
@@ -1847,14 +1985,14 @@ __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float 
       } else {
         float Fp[9];
         for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
-        for (int rr = 0; rr < 3; ++rr)
-          for (int cc = 0; cc < 3; ++cc) {
-            float val = Fp[rr * 3 + cc];
-            if (pending)
-              val += dt * (Cp[rr * 3 + 0] * Fp[0 * 3 + cc] + Cp[rr * 3 + 1] * Fp[1 * 3 + cc] +
-                           Cp[rr * 3 + 2] * Fp[2 * 3 + cc]);
-            F[9 * id + rr * 3 + cc] = val;
+        if (pending) {
+          update_F<MPM_FIXED_COROTATED>(Fp, Cp, dt);
+          if (MAT == MPM_SAND) {  // and the plasticity projection that follows the update
+            float A[9];
+            (void)sand_affine(s, Fp, s.E, Cp, A, true);
           }
+        }
+        for (int k = 0; k < 9; ++k) F[9 * id + k] = Fp[k];
       }
     }
   }
@@ -1907,9 +2045,10 @@ bool valid_params(const mpm_params *p) {
   for (int a = 0; a < 3; ++a)
     if (!std::isfinite(p->gravity[a])) return false;
   if (p->wall_nodes < 0 || p->wall_nodes > p->grid_n / 2) return false;
-  if (p->material != MPM_FIXED_COROTATED && p->material != MPM_J_FLUID) return false;
+  if (p->material != MPM_FIXED_COROTATED && p->material != MPM_J_FLUID && p->material != MPM_SAND) return false;
+  if (p->material == MPM_SAND && !(p->friction_deg > 0.f && p->friction_deg < 90.f)) return false;
   if (!(p->E >= 0.f) || !std::isfinite(p->E)) return false;
-  if (p->material == MPM_FIXED_COROTATED && !(p->nu >= 0.f && p->nu < 0.5f)) return false;
+  if (p->material != MPM_J_FLUID && !(p->nu >= 0.f && p->nu < 0.5f)) return false;
   if (!(p->rho > 0.f) || !std::isfinite(p->rho)) return false;
   if (!(p->p_vol > 0.f) || !std::isfinite(p->p_vol)) return false;
   return true;
@@ -1983,6 +2122,11 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     // Fluid: tau = K J (J-1) I uses E as K directly; mu/lam unused.
     d->mu_per_E = (float)(1.0 / (2.0 * (1.0 + nu)));
     d->lam_per_E = (float)(nu / ((1.0 + nu) * (1.0 - 2.0 * nu)));
+    // sand (Klar et al. 2016): alpha = sqrt(2/3) 2 sin(phi) / (3 - sin(phi)), and
+    // (3 lam + 2 mu) / (2 mu) = (1 + nu) / (1 - 2 nu)
+    const double sp = std::sin((double)p->friction_deg * 3.14159265358979323846 / 180.0);
+    d->alpha = p->material == MPM_SAND ? (float)(std::sqrt(2.0 / 3.0) * 2.0 * sp / (3.0 - sp)) : 0.f;
+    d->dp_c = (float)((1.0 + nu) / (1.0 - 2.0 * nu));
     d->stress_k = (float)((double)p->dt * (double)p->p_vol * 4.0 * (double)n * (double)n);
     d->c_scale = (float)(4.0 * n);
     d->lo = 2.0f * d->dx;
@@ -2088,6 +2232,9 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
       if (d.material == MPM_J_FLUID) {
         if (d.has_E) k_p2g<MPM_J_FLUID, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
         else k_p2g<MPM_J_FLUID, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
+      } else if (d.material == MPM_SAND) {
+        if (d.has_E) k_p2g<MPM_SAND, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
+        else k_p2g<MPM_SAND, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
       } else {
         if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
         else k_p2g<MPM_FIXED_COROTATED, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
@@ -2100,11 +2247,15 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
         if (d.material == MPM_J_FLUID) {
           if (d.has_E) k_g2p2g<MPM_J_FLUID, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
           else k_g2p2g<MPM_J_FLUID, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+        } else if (d.material == MPM_SAND) {
+          if (d.has_E) k_g2p2g<MPM_SAND, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          else k_g2p2g<MPM_SAND, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
         } else {
           if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
           else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
         }
       } else {
+        // (the gather does not depend on the material: sand uses the elastic instance)
         if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
         else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
       }
@@ -2248,6 +2399,8 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     int occ_f = 0;
     const void *fk = d.material == MPM_J_FLUID
                          ? (d.has_E ? (const void *)k_g2p2g<MPM_J_FLUID, true> : (const void *)k_g2p2g<MPM_J_FLUID, false>)
+                     : d.material == MPM_SAND
+                         ? (d.has_E ? (const void *)k_g2p2g<MPM_SAND, true> : (const void *)k_g2p2g<MPM_SAND, false>)
                          : (d.has_E ? (const void *)k_g2p2g<MPM_FIXED_COROTATED, true>
                                     : (const void *)k_g2p2g<MPM_FIXED_COROTATED, false>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, fk, 64, 0) != hipSuccess || occ_f <= 0) occ_f = 8;
@@ -2398,6 +2551,7 @@ int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int g = sim->grid_g2p;
   if (sim->d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
+  else if (sim->d.material == MPM_SAND) k_read_particles<MPM_SAND><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
   else k_read_particles<MPM_FIXED_COROTATED><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }

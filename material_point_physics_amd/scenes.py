@@ -203,12 +203,33 @@ def dambreak_4m(seed: int = 5) -> Scene:
                  p_vol=dx ** 3 / 16, steps=100)
 
 
+def sand_3m(seed: int = 6) -> Scene:
+    """3,112,960 particles in a sand column collapsing under gravity, 128^3 grid.
+
+    Stands in for the page's falling-sand scene (3.1M particles): a column of
+    64 x 95 x 64 cells (x and z cells [32,96), y cells [4,99), resting on the
+    floor's wall layer), 8 particles per cell, at rest; Drucker-Prager sand
+    with a 30-degree friction angle.
+    """
+    n = 128
+    dx = 1.0 / n
+    rng = np.random.default_rng(seed)
+    x = _stratified(rng, _box_cells((32, 4, 32), (96, 99, 96)), 8, dx)
+    v = np.zeros_like(x)
+    return Scene("sand_3m", "collapsing sand column, 3112960 particles, 128^3 grid",
+                 x.astype(np.float32), v.astype(np.float32), None,
+                 n=n, dt=2e-5, gravity=(0.0, -9.8, 0.0), wall=3,
+                 material=SAND, E=1e5, nu=0.3, rho=1.0,
+                 p_vol=dx ** 3 / 8, steps=100, friction_deg=30.0)
+
+
 SCENES = {
     "cube_8k": cube_8k,
     "jelly3_55k": jelly3_55k,
     "blocks_1m": blocks_1m,
     "slab_12m": slab_12m,
     "dambreak_4m": dambreak_4m,
+    "sand_3m": sand_3m,
 }
 
 
