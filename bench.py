@@ -77,9 +77,15 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
 
 
 def source_sha1() -> str:
+    """sha1 of the kernel sources: every file of csrc/ in name order."""
     import hashlib
-    with open(os.path.join(ROOT, "material_point_physics_amd", "csrc", "mpm.hip"), "rb") as f:
-        return hashlib.sha1(f.read()).hexdigest()
+    d = os.path.join(ROOT, "material_point_physics_amd", "csrc")
+    h = hashlib.sha1()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def committed_traffic(workload: str, kernel: str, mode: str = ""):

@@ -1,0 +1,285 @@
+// g2p.h -- G2P: velocity window with the grid update, gather, advection, next keys
+// Part of mpm.hip: included there, inside its anonymous namespace, after the
+// parts before it; not a standalone header.
+
+// The grid update -- v = p/m + dt g where m > 0, sticky walls -- is
+// evaluated by G2P on its window nodes as it loads them (grid_velocity), and
+// the accumulator is cleared by the next step's P2G, so the step needs no
+// separate pass over the grid.
+__device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int gx, int gy, int gz) {
+  const int n = s.n, wall = s.wall;
+  float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
+  const bool in_wall = gx < wall || gy < wall || gz < wall || gx >= n - wall || gy >= n - wall || gz >= n - wall;
+  if (acc.x > 0.f && !in_wall) {
+    // one division per node (G2P evaluates each node once per window that
+    // covers it): p (1/m) is within an ulp of p/m
+    const float inv = 1.f / acc.x;
+    o.x = acc.y * inv + s.dt * s.g[0];
+    o.y = acc.z * inv + s.dt * s.g[1];
+    o.z = acc.w * inv + s.dt * s.g[2];
+  }
+  return o;
+}
+
+// G2P: gather, APIC C, advection and clamp.  Persistent single-wavefront
+// workgroups walk the same per-XCD chunk list as P2G.  A chunk's particles
+// occupy the consecutive slots [start, start + count) (P2G stored them
+// there), and all of their stencils lie in the bin's 6^3-node window, which
+// is loaded once into LDS; each particle then gathers its 27 nodes from LDS.
+
+// Window load in whole cubes (one 128-byte line each): lane = (cube, node in
+// cube), 8 cubes per load instruction, 4 instructions.  This lane's window
+// node of instruction t, packed wx | wy << 8 | wz << 16 (all ones when cube
+// 8t + lane / 8 is past the 27th).
+__device__ __forceinline__ void window_lanes(uint32_t wpack[4]) {
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int cb = 8 * t + (lane >> 3), j = lane & 7;
+    const int wx = 2 * (cb % 3) + (j & 1), wy = 2 * ((cb / 3) % 3) + ((j >> 1) & 1), wz = 2 * (cb / 9) + (j >> 2);
+    wpack[t] = cb < 27 ? (uint32_t)(wx | (wy << 8) | (wz << 16)) : 0xFFFFFFFFu;
+  }
+}
+
+// Requests the accumulator values (m, p) of the window at (ox0, oy0, oz0)
+// from accumulator a; nodes outside the grid read as zero.
+__device__ __forceinline__ void fetch_window(const SimDev &s, int a, int ox0, int oy0, int oz0, const uint32_t wpack[4],
+                                             float4 acc[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int gx = ox0 + (int)(wpack[t] & 0xFFu), gy = oy0 + (int)((wpack[t] >> 8) & 0xFFu),
+              gz = oz0 + (int)((wpack[t] >> 16) & 0xFFu);
+    if (wpack[t] != 0xFFFFFFFFu && gx < s.n && gy < s.n && gz < s.n) acc[t] = s.gridA[a][node_index(s, gx, gy, gz)];
+  }
+}
+
+// Converts fetched window values to grid velocities (the grid update) in LDS.
+__device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4], const uint32_t wpack[4], int ox0,
+                                             int oy0, int oz0, float4 *win) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (wpack[t] == 0xFFFFFFFFu) continue;
+    const int wx = (int)(wpack[t] & 0xFFu), wy = (int)((wpack[t] >> 8) & 0xFFu), wz = (int)((wpack[t] >> 16) & 0xFFu);
+    const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+    win[(wz * PW + wy) * PW + wx] =
+        (gx < s.n && gy < s.n && gz < s.n) ? grid_velocity(s, acc[t], gx, gy, gz) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Gather of one particle at xp: v = sum w v_i and B = sum w v_i (o - f)^T
+// (C = 4/dx^2 B dx, applied by the caller), from the velocity window of the
+// bin at (ox0, oy0, oz0), or from accumulator a with the grid update for a
+// particle whose stencil is outside the window (it left the chunk's bin
+// since the last sort: only in steps without a sort; rare).
+__device__ __forceinline__ void gather_particle(const SimDev &s, const float4 *win, int a, const float xp[3], int ox0,
+                                                int oy0, int oz0, float v[3], float B[9]) {
+  int b[3];
+  float w[3][3], d[3][3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const float xn = xp[k] * s.fn;
+    b[k] = base_node(xn);
+    const float f = xn - (float)b[k];
+    bspline_weights(f, w[k]);
+    d[k][0] = -f;
+    d[k][1] = 1.f - f;
+    d[k][2] = 2.f - f;
+  }
+  const bool outside = b[0] - ox0 < 0 || b[0] - ox0 >= CB || b[1] - oy0 < 0 || b[1] - oy0 >= CB || b[2] - oz0 < 0 ||
+                       b[2] - oz0 >= CB;
+  const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
+            lz = min(max(b[2] - oz0, 0), CB - 1);
+  const int li0 = (lz * PW + ly) * PW + lx;
+  // The quadratic B-spline's first moment sum_o w_o (o - f) = 0 gives the
+  // columns of B as B_a = sum w o_a v_i - f_a v.  Reduced along x first for
+  // each (y, z) row: S = sum_x w_x v_i and U = sum_x w_x ox v_i; offsets
+  // equal to zero add nothing, so rows with oy = 0 (oz = 0) skip the y (z)
+  // column.
+  const float w2x = 2.f * w[0][2];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) v[k] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) B[k] = 0.f;
+  if (outside) {
+    // node rows of three, their loads issued together
+#pragma unroll 1
+    for (int r = 0; r < 9; ++r) {
+      const int oy = r % 3, oz = r / 3;
+      const int gy = b[1] + oy, gz = b[2] + oz;
+      float4 acc[3];
+#pragma unroll
+      for (int ox = 0; ox < 3; ++ox) {
+        const int gx = b[0] + ox;
+        acc[ox] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gx >= 0 && gy >= 0 && gz >= 0 && gx < s.n && gy < s.n && gz < s.n)
+          acc[ox] = s.gridA[a][node_index(s, gx, gy, gz)];
+      }
+#pragma unroll
+      for (int ox = 0; ox < 3; ++ox) {
+        const float4 g = grid_velocity(s, acc[ox], b[0] + ox, gy, gz);
+        const float wt = w[0][ox] * w[1][oy] * w[2][oz];
+        const float vel[3] = {g.x, g.y, g.z};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          v[k] = fmaf(wt, vel[k], v[k]);
+          B[k * 3 + 0] = fmaf(wt * (float)ox, vel[k], B[k * 3 + 0]);
+          B[k * 3 + 1] = fmaf(wt * (float)oy, vel[k], B[k * 3 + 1]);
+          B[k * 3 + 2] = fmaf(wt * (float)oz, vel[k], B[k * 3 + 2]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int oz = 0; oz < 3; ++oz)
+#pragma unroll
+      for (int oy = 0; oy < 3; ++oy) {
+        float S[3], U[3];
+        const float4 g0 = win[li0 + (oz * PW + oy) * PW + 0];
+        const float4 g1 = win[li0 + (oz * PW + oy) * PW + 1];
+        const float4 g2 = win[li0 + (oz * PW + oy) * PW + 2];
+        S[0] = w[0][0] * g0.x;
+        S[1] = w[0][0] * g0.y;
+        S[2] = w[0][0] * g0.z;
+        U[0] = w[0][1] * g1.x;
+        U[1] = w[0][1] * g1.y;
+        U[2] = w[0][1] * g1.z;
+        S[0] = fmaf(w[0][1], g1.x, S[0]);
+        S[1] = fmaf(w[0][1], g1.y, S[1]);
+        S[2] = fmaf(w[0][1], g1.z, S[2]);
+        S[0] = fmaf(w[0][2], g2.x, S[0]);
+        S[1] = fmaf(w[0][2], g2.y, S[1]);
+        S[2] = fmaf(w[0][2], g2.z, S[2]);
+        U[0] = fmaf(w2x, g2.x, U[0]);
+        U[1] = fmaf(w2x, g2.y, U[1]);
+        U[2] = fmaf(w2x, g2.z, U[2]);
+        const float wyz = w[1][oy] * w[2][oz];
+        const float wyz2 = wyz + wyz;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          v[k] = fmaf(wyz, S[k], v[k]);
+          B[k * 3 + 0] = fmaf(wyz, U[k], B[k * 3 + 0]);
+          if (oy > 0) B[k * 3 + 1] = fmaf(oy == 1 ? wyz : wyz2, S[k], B[k * 3 + 1]);
+          if (oz > 0) B[k * 3 + 2] = fmaf(oz == 1 ? wyz : wyz2, S[k], B[k * 3 + 2]);
+        }
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) B[k * 3 + c2] = fmaf(d[c2][0], v[k], B[k * 3 + c2]);  // d[c2][0] = -f_c2
+}
+
+// Advection x + dt v, clamped to the box; status bits for a clamp or a
+// non-finite value (of x, v or C = c_scale B, which the caller stores).
+__device__ __forceinline__ void advect(const SimDev &s, const float xp[3], const float v[3], const float B[9],
+                                       float xn[3], float C[9], bool &clamped, bool &nonfinite) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float xa = xp[k] + s.dt * v[k];
+    if (!isfinite(xa) || !isfinite(v[k])) nonfinite = true;
+    if (xa < s.lo || xa > s.hi) clamped = true;
+    xn[k] = fminf(fmaxf(xa, s.lo), s.hi);
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    C[k] = s.c_scale * B[k];
+    if (!isfinite(C[k])) nonfinite = true;
+  }
+}
+
+// The G2P of the step that accumulated into a: particles of layout lay (the
+// one P2G built), x, v, C written in place, and the next step's bin keys and
+// counts.
+template <int MAT>
+__device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4 *win) {
+  const PBuf out = s.buf[lay];
+  const int lane = threadIdx.x;
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
+  const float fn = s.fn;
+  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + lay];
+  uint4 *chunks = s.chunks[lay];
+  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  uint32_t wpack[4];
+  window_lanes(wpack);
+  for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
+    const uint4 ch = chunks[c];
+    const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
+    const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
+    // The window's accumulator values and the first round's positions are
+    // requested together, then the window is converted to velocities (the
+    // grid update) in LDS.
+    float4 acc[4];
+    fetch_window(s, a, ox0, oy0, oz0, wpack, acc);
+    float xnext[3] = {0.f, 0.f, 0.f};  // positions of the next round, written by this step's P2G in this order
+    if ((uint32_t)lane < count) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) xnext[k] = at_byte(out.x + k * Np, 4u * (start + (uint32_t)lane));
+    }
+    store_window(s, acc, wpack, ox0, oy0, oz0, win);
+    __syncthreads();
+    uint32_t nstay = 0;
+    for (uint32_t r0 = 0; r0 < count; r0 += 64) {
+      const uint32_t slot = start + r0 + (uint32_t)lane, so = 4u * slot;
+      const bool valid = r0 + (uint32_t)lane < count;
+      float xp[3] = {xnext[0], xnext[1], xnext[2]};
+      if (r0 + 64u < count && r0 + 64u + (uint32_t)lane < count) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) xnext[k] = at_byte(out.x + k * Np, so + 256u);
+      }
+      uint32_t key = 0;
+      if (valid) {
+        float v[3], B[9], xn[3], Cn[9];
+        gather_particle(s, win, a, xp, ox0, oy0, oz0, v, B);
+        bool clamped = false, nonfinite = false;
+        advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
+        int b[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          stream_store(xn[k], at_byte(out.x + k * Np, so));
+          stream_store(v[k], at_byte(out.v + k * Np, so));
+          b[k] = base_node(xn[k] * fn);
+        }
+#pragma unroll
+        for (int k = 0; k < 9; ++k) stream_store(Cn[k], at_byte(out.C + k * Np, so));
+        // the next bin: nearly always the chunk's own (Morton encoding only
+        // when some lane of the wavefront left it)
+        const bool same_bin = (b[0] >> 2) == (ox0 >> 2) && (b[1] >> 2) == (oy0 >> 2) && (b[2] >> 2) == (oz0 >> 2);
+        key = (__ballot(!same_bin) == 0ull) ? bin : bin_key(s, b[0], b[1], b[2]);
+        at_byte(s.key, so) = key | (cell_in_bin(b[0], b[1], b[2]) << KEY_CELL_SHIFT);
+        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
+        if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
+      }
+      wave_aggregated_increment(s.bin_count, key, valid);
+      nstay += (uint32_t)__popcll(__ballot(valid && key == bin));
+    }
+    // The chunk's particles that stay in its bin: the next scatter keeps them
+    // in this order, after the stayers of the bin's earlier chunks.
+    if (lane == 0) {
+      chunks[c].w = nstay;
+      if (nstay) atomicAdd(s.stay_count + bin, nstay);
+      if (nstay < count) atomicAdd(s.ctr + CTR_MOVERS, count - nstay);  // for the next sort decision
+    }
+    __syncthreads();  // the window is reloaded for the next chunk
+  }
+}
+
+// The control words a G2P leaves for the next step (that reads buffer lay):
+// F is one update behind, and that step's P2G and sort decision are its own.
+__device__ __forceinline__ void g2p_handoff(const SimDev &s, int lay) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    s.ctr[CTR_PENDING] = 1u;
+    s.ctr[CTR_LOOK + lay] = 0u;
+    s.ctr[CTR_PRESET + lay] = 0u;
+  }
+}
+
+// G2P of a step that reads buffer src (accumulator a): writes x, v, C in
+// place in layout src ^ 1 and the next step's bin keys and counts.
+template <int MAT>
+__global__ __launch_bounds__(64) void k_g2p(SimDev s, int src, int a) {
+  __shared__ float4 win[PW3];
+  g2p_step<MAT>(s, src ^ 1, a, win);
+  g2p_handoff(s, src ^ 1);
+}

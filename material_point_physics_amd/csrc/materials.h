@@ -1,0 +1,190 @@
+// materials.h -- per-particle material updates: deformation gradient, stress, sand plasticity
+// Part of mpm.hip: included there, inside its anonymous namespace, after the
+// parts before it; not a standalone header.
+
+// Deferred deformation-gradient update with the C of the G2P before it:
+// F <- (I + dt C) F, or for the fluid J <- J det(I + dt C).
+template <int MAT>
+__device__ __forceinline__ void update_F(float *Fp, const float Cp[9], float dt) {
+  if (MAT == MPM_J_FLUID) {
+    const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
+                        dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
+    Fp[0] = Fp[0] * det3(G);
+  } else {
+    float Fn[9];
+#pragma unroll
+    for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+      for (int c2 = 0; c2 < 3; ++c2)
+        Fn[r2 * 3 + c2] = Fp[r2 * 3 + c2] + dt * (Cp[r2 * 3 + 0] * Fp[0 * 3 + c2] + Cp[r2 * 3 + 1] * Fp[1 * 3 + c2] +
+                                                  Cp[r2 * 3 + 2] * Fp[2 * 3 + c2]);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
+  }
+}
+
+// Kirchhoff stress of the fixed-corotated model, tau = 2 mu (F - R) F^T +
+// lam (J - 1) J I with R the rotation closest to F (fluid: tau = K J (J - 1) I,
+// K = E), and the APIC affine momentum matrix A = m C - dt V0 (4/dx^2) tau.
+// Returns status bits (inverted or unconverged F; fluid: J <= 0).
+template <int MAT>
+__device__ __forceinline__ uint32_t affine_momentum(const SimDev &s, const float *Fp, float E, const float Cp[9],
+                                                    float A[9]) {
+  const float mass = s.mass;
+  if (MAT == MPM_J_FLUID) {
+    const float J = Fp[0];
+    const float tau_diag = E * J * (J - 1.f);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) A[k] = mass * Cp[k] - s.stress_k * ((k % 4 == 0) ? tau_diag : 0.f);
+    return (J > 0.f) ? 0u : (uint32_t)MPM_STATUS_INVERTED;
+  }
+  const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
+  float R[9];
+  const uint32_t st = rotation_of(Fp, R);
+  const float J = det3(Fp);
+  float D[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) D[k] = 2.f * mu * (Fp[k] - R[k]);
+  const float vl = lam * (J - 1.f) * J;
+#pragma unroll
+  for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) {
+      const float tau = D[r2 * 3 + 0] * Fp[c2 * 3 + 0] + D[r2 * 3 + 1] * Fp[c2 * 3 + 1] + D[r2 * 3 + 2] * Fp[c2 * 3 + 2] +
+                        (r2 == c2 ? vl : 0.f);
+      A[r2 * 3 + c2] = mass * Cp[r2 * 3 + c2] - s.stress_k * tau;
+    }
+  return st;
+}
+
+// ------------------------------------------------------------------ sand
+// Drucker-Prager elastoplasticity in Hencky strain (Klar et al. 2016,
+// "Drucker-Prager elastoplasticity for sand animation"), with a constant
+// friction angle.  [RT-MPM] merges the SVD, the plasticity projection and
+// the stress into the particle phase of P2G; so does the sand instance of
+// P2G here, after the deferred F update.  Principal stretches are unsigned:
+// F^T F = V diag(l) V^T, s = sqrt(l), Hencky strain e = ln(l) / 2, with l
+// floored at 1e-6 (an element crushed below 1/1000 of its length).
+
+// Eigen-decomposition of a symmetric 3x3 matrix by cyclic Jacobi rotations
+// (Rutishauser's formulation, Golub & Van Loan, "Matrix Computations"):
+// A becomes diagonal, W's columns the eigenvectors.
+__device__ __forceinline__ void eigen_sym3(float a[3][3], float W[3][3]) {
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) W[r][c] = (r == c) ? 1.f : 0.f;
+  for (int sweep = 0; sweep < 10; ++sweep) {
+    const float off = a[0][1] * a[0][1] + a[0][2] * a[0][2] + a[1][2] * a[1][2];
+    const float dia = a[0][0] * a[0][0] + a[1][1] * a[1][1] + a[2][2] * a[2][2];
+    if (off <= 1e-14f * dia) break;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int p = k == 2 ? 1 : 0, q = k == 0 ? 1 : 2;
+      const float apq = a[p][q];
+      if (apq == 0.f) continue;
+      const float theta = (a[q][q] - a[p][p]) / (2.f * apq);
+      const float t = copysignf(1.f, theta) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+      const float c = rsqrtf(t * t + 1.f), sn = t * c;
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {  // columns p, q
+        const float xp = a[r][p], xq = a[r][q];
+        a[r][p] = c * xp - sn * xq;
+        a[r][q] = sn * xp + c * xq;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {  // rows p, q
+        const float xp = a[p][r], xq = a[q][r];
+        a[p][r] = c * xp - sn * xq;
+        a[q][r] = sn * xp + c * xq;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const float xp = W[r][p], xq = W[r][q];
+        W[r][p] = c * xp - sn * xq;
+        W[r][q] = sn * xp + c * xq;
+      }
+    }
+  }
+}
+
+// F V diag(m) V^T (F with its principal stretches scaled by m).
+__device__ __forceinline__ void stretch_scaled(const float F[9], const float W[3][3], const float m[3], float out[9]) {
+  float M[9];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      M[r * 3 + c] = W[r][0] * m[0] * W[c][0] + W[r][1] * m[1] * W[c][1] + W[r][2] * m[2] * W[c][2];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      out[r * 3 + c] = F[r * 3 + 0] * M[0 * 3 + c] + F[r * 3 + 1] * M[1 * 3 + c] + F[r * 3 + 2] * M[2 * 3 + c];
+}
+
+// Sand, per particle: the plasticity projection of F (in place, when
+// project) and the APIC affine momentum A = m C - dt V0 (4/dx^2) tau with the
+// Hencky Kirchhoff stress tau = U diag(2 mu h + lam sum h) U^T of the
+// projected principal strains h (U = F V diag(1/s) is unchanged by the
+// projection, so tau is formed from the trial F and its l).  Return
+// mapping, with t = sum e and the deviator d = e - t/3: t > 0 -> tip
+// (h = 0); else g = |d| + (1 + nu)/(1 - 2 nu) t alpha, g <= 0 -> unchanged,
+// g > 0 -> h = e - g d / |d|.  Returns status bits (det F <= 0).
+__device__ __forceinline__ uint32_t sand_affine(const SimDev &s, float Fp[9], float E, const float Cp[9], float A[9],
+                                                bool project) {
+  float a[3][3], W[3][3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) a[r][c] = Fp[0 * 3 + r] * Fp[0 * 3 + c] + Fp[1 * 3 + r] * Fp[1 * 3 + c] + Fp[2 * 3 + r] * Fp[2 * 3 + c];
+  eigen_sym3(a, W);
+  float l[3], e[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    l[i] = fmaxf(a[i][i], 1e-6f);
+    e[i] = 0.5f * logf(l[i]);
+  }
+  const uint32_t st = det3(Fp) > 0.f ? 0u : (uint32_t)MPM_STATUS_INVERTED;
+  float h[3] = {e[0], e[1], e[2]};
+  bool moved = false;
+  if (project) {
+    const float t = e[0] + e[1] + e[2];
+    const float d[3] = {e[0] - t / 3.f, e[1] - t / 3.f, e[2] - t / 3.f};
+    const float nd = sqrtf(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    if (t > 0.f) {
+      h[0] = h[1] = h[2] = 0.f;
+      moved = true;
+    } else {
+      const float g = nd + s.dp_c * t * s.alpha;
+      if (g > 0.f) {
+        const float k = g / nd;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) h[i] = e[i] - k * d[i];
+        moved = true;
+      }
+    }
+  }
+  // tau = F V diag((2 mu h + lam sum h) / l) V^T F^T, F the trial F
+  const float mu = E * s.mu_per_E, lam = E * s.lam_per_E, ht = h[0] + h[1] + h[2];
+  float q[3], G[9];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) q[i] = (2.f * mu * h[i] + lam * ht) / l[i];
+  stretch_scaled(Fp, W, q, G);
+#pragma unroll
+  for (int r2 = 0; r2 < 3; ++r2)
+#pragma unroll
+    for (int c2 = 0; c2 < 3; ++c2) {
+      const float tau = G[r2 * 3 + 0] * Fp[c2 * 3 + 0] + G[r2 * 3 + 1] * Fp[c2 * 3 + 1] + G[r2 * 3 + 2] * Fp[c2 * 3 + 2];
+      A[r2 * 3 + c2] = s.mass * Cp[r2 * 3 + c2] - s.stress_k * tau;
+    }
+  if (moved) {  // F becomes the projected one: its stretches scaled by exp(h - e)
+    float m[3], Fn[9];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) m[i] = expf(h[i] - e[i]);
+    stretch_scaled(Fp, W, m, Fn);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Fp[k] = Fn[k];
+  }
+  return st;
+}

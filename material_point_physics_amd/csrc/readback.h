@@ -1,0 +1,83 @@
+// readback.h -- readback of particles (creation order) and of the grid
+// Part of mpm.hip: included there, inside its anonymous namespace, after the
+// parts before it; not a standalone header.
+
+// Readback: unpermute to creation order, apply the pending F (or J) update.
+// Single-wavefront workgroups walk the chunk list of layout cur (the slots
+// between bins are padding).  After a fused G2P2G pass the state is in the
+// same slots of the other buffer, with F current.
+template <int MAT>
+__global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float *__restrict__ x, float *__restrict__ v,
+                                                       float *__restrict__ C, float *__restrict__ F) {
+  const bool fused = s.ctr[CTR_LOOK + cur] != 0u;
+  const PBuf b = s.buf[fused ? cur ^ 1 : cur];
+  const size_t Np = (size_t)s.Np;
+  const bool pending = !fused && s.ctr[CTR_PENDING] != 0u;
+  const float dt = s.dt;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + cur];
+  for (uint32_t c = blockIdx.x; c < nch; c += gridDim.x) {
+    const uint4 ch = s.chunks[cur][c];
+    for (uint32_t r = threadIdx.x; r < ch.y; r += 64) {
+      const size_t slot = (size_t)ch.x + r;
+      if (slot >= Np) break;
+      const size_t id = b.id[slot];
+      if (id >= (size_t)s.N) continue;
+      float Cp[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) Cp[k] = b.C[k * Np + slot];
+      for (int a = 0; a < 3; ++a) {
+        if (x) x[3 * id + a] = b.x[a * Np + slot];
+        if (v) v[3 * id + a] = b.v[a * Np + slot];
+      }
+      if (C)
+        for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
+      if (!F) continue;
+      if (MAT == MPM_J_FLUID) {
+        float J = b.F[slot];
+        if (pending) {
+          const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
+                              dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
+          J = J * det3(G);
+        }
+        F[id] = J;
+      } else {
+        float Fp[9];
+        for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
+        if (pending) {
+          update_F<MPM_FIXED_COROTATED>(Fp, Cp, dt);
+          if (MAT == MPM_SAND) {  // and the plasticity projection that follows the update
+            float A[9];
+            (void)sand_affine(s, Fp, s.E, Cp, A, true);
+          }
+        }
+        for (int k = 0; k < 9; ++k) F[9 * id + k] = Fp[k];
+      }
+    }
+  }
+}
+
+// Readback of the grid after the last step (parity q): the node-blocks it
+// marked, updated as G2P saw them (v = p/m + dt g, walls) -> dense
+// (i + n (j + n k)) arrays of m and m v.
+__global__ __launch_bounds__(WG) void k_read_grid(SimDev s, int q, float *__restrict__ mass, float *__restrict__ mom) {
+  const int n = s.n;
+  for (uint32_t blk = blockIdx.x; blk < (uint32_t)s.nblk; blk += gridDim.x) {
+    if (s.active_flag[q][blk] == 0u) continue;
+    const int bx = (int)(blk % (uint32_t)s.nb), by = (int)((blk / (uint32_t)s.nb) % (uint32_t)s.nb),
+              bz = (int)(blk / ((uint32_t)s.nb * (uint32_t)s.nb));
+    for (int local = threadIdx.x; local < 512; local += WG) {
+      int lx, ly, lz;
+      block_local_coords(local, lx, ly, lz);
+      const int gx = bx * NB + lx, gy = by * NB + ly, gz = bz * NB + lz;
+      if (gx >= n || gy >= n || gz >= n) continue;
+      const float4 g = grid_velocity(s, s.gridA[q][((size_t)blk << 9) + local], gx, gy, gz);
+      const size_t lin = (size_t)gx + (size_t)n * ((size_t)gy + (size_t)n * gz);
+      if (mass) mass[lin] = g.w;
+      if (mom) {
+        mom[3 * lin + 0] = g.w * g.x;
+        mom[3 * lin + 1] = g.w * g.y;
+        mom[3 * lin + 2] = g.w * g.z;
+      }
+    }
+  }
+}
