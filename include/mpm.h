@@ -76,7 +76,11 @@ typedef struct mpm_sim mpm_sim;
  *   wall_nodes  : sticky-wall thickness: all velocity components are zeroed
  *                 on nodes with any index < wall_nodes or >= grid_n - wall_nodes
  *                 (0 <= wall_nodes <= grid_n/2).
- *   material    : MPM_FIXED_COROTATED or MPM_J_FLUID.
+ *   material    : MPM_FIXED_COROTATED, MPM_J_FLUID or MPM_SAND (Drucker-
+ *                 Prager plasticity in Hencky strain with a constant friction
+ *                 angle, projected after every deformation-gradient update:
+ *                 the page merges the SVD, the plasticity projection and the
+ *                 stress into the particle phase of P2G).
  *   E           : Young's modulus (bulk modulus K for MPM_J_FLUID), >= 0;
  *                 used when no per-particle modulus is given.
  *   nu          : Poisson ratio, 0 <= nu < 0.5 (ignored for MPM_J_FLUID).
@@ -115,7 +119,9 @@ size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles);
  *   v0          : device, (N,3) velocities, or NULL for zero.
  *   C0          : device, (N,3,3) row-major APIC affine matrices, or NULL for zero.
  *   F0          : device, (N,3,3) deformation gradients for MPM_FIXED_COROTATED
- *                 or (N) volume ratios J for MPM_J_FLUID; NULL for I (or 1).
+ *                 and MPM_SAND (its elastic part, used as given until the
+ *                 first update), or (N) volume ratios J for MPM_J_FLUID; NULL
+ *                 for I (or 1).
  *   E_p         : device, (N) per-particle Young's modulus, or NULL for params->E.
  *   workspace   : device, at least mpm_workspace_bytes(params, N) bytes,
  *                 256-byte aligned, owned by the caller, and must outlive the
@@ -172,7 +178,8 @@ int mpm_set_fused_steps(mpm_sim *sim, int32_t enable);
 
 /* Copy the particle state after the last step, in creation order, into
  * caller-owned device arrays: x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)
- * for the elastic material or (N) for the fluid.  Any output may be NULL.
+ * for the elastic material and sand (for sand the elastic part after the
+ * step's plasticity projection) or (N) for the fluid.  Any output may be NULL.
  * Asynchronous on `stream`. */
 int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J, void *stream);
 
