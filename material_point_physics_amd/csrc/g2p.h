@@ -4,8 +4,8 @@
 
 // The grid update -- v = p/m + dt g where m > 0, sticky walls -- is
 // evaluated by G2P on its window nodes as it loads them (grid_velocity), and
-// the accumulator is cleared by the next step's P2G, so the step needs no
-// separate pass over the grid.
+// the accumulator is cleared by the P2G two steps later, so the step needs
+// no separate pass over the grid.
 __device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int gx, int gy, int gz) {
   const int n = s.n, wall = s.wall;
   float4 o = make_float4(0.f, 0.f, 0.f, acc.x);

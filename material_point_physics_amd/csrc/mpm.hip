@@ -5,9 +5,11 @@
 // Modern GPUs" (below [RT-MPM]) splits a step into particle sorting, P2G,
 // grid update and G2P; the equations are the textbook MLS-MPM with quadratic
 // B-splines, APIC transfer and the fixed-corotated model (Hu et al. 2018;
-// Jiang et al. 2015; Stomakhin et al. 2012).
+// Jiang et al. 2015; Stomakhin et al. 2012), plus a weakly compressible
+// fluid and Drucker-Prager sand (Klar et al. 2016).
 //
-// Step = 5 kernels, captured once into a HIP graph per buffer parity:
+// Step = 5 kernels, captured into HIP graphs per phase (step number mod 4:
+// the particle buffer and the grid accumulator the step uses):
 //   k_scan_*      two-phase exclusive scan of per-bin counts -> bin starts,
 //                 chunk list (<= KMAX particles of one bin per chunk)
 //   k_scatter     bucket scatter by 4^3-cell bin (first radix digit), one
@@ -25,6 +27,9 @@
 //                 sticky walls) of the bin's 6^3-node window, staged in LDS;
 //                 gather, APIC C, advection + clamp in the storage order P2G
 //                 chose; the next step's bin keys/counts
+//
+// Between sorts (mpm_set_sort_policy), k_g2p2g can replace k_g2p: the G2P of
+// the step and the P2G of the next in one pass (mpm_set_fused_steps).
 //
 // Deferred deformation gradient: [RT-MPM] (kernel-merging discussion) notes
 // that the F update at the end of G2P can be postponed to the start of P2G

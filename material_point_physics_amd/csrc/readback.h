@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float 
   }
 }
 
-// Readback of the grid after the last step (parity q): the node-blocks it
+// Readback of the grid after the last step (its accumulator q): the node-blocks it
 // marked, updated as G2P saw them (v = p/m + dt g, walls) -> dense
 // (i + n (j + n k)) arrays of m and m v.
 __global__ __launch_bounds__(WG) void k_read_grid(SimDev s, int q, float *__restrict__ mass, float *__restrict__ mom) {
