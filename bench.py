@@ -77,14 +77,19 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
 
 
 def source_sha1() -> str:
-    """sha1 of the kernel sources: every file of csrc/ in name order."""
+    """sha1 of the kernel code: every file of csrc/ in name order, with
+    comments and whitespace removed (a comment edit does not change a kernel)."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "material_point_physics_amd", "csrc")
     h = hashlib.sha1()
     for name in sorted(os.listdir(d)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(d, name)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
