@@ -200,3 +200,31 @@ def test_scheduled_batches_single_steps_and_mode_changes():
     orc, env = pu.envelope(sc, 23)
     assert_particle_parity(sc, got, orc, env)
     assert_grid_parity(sc, got, orc, tol=max(1e-5, 20 * env["v"]))
+
+
+@pytest.mark.parametrize("policy", [(1 << 30, 1 << 40), (4, 1 << 40)], ids=["device_decided", "scheduled"])
+def test_fused_profiled_steps_match_graph_steps(policy):
+    """Eager per-kernel-timed steps (the benchmark's timing path) run the same
+    kernels as the fused graphs: 11 steps either way, then particles and grid
+    compared; in the scheduled mode the kernels a step does not launch take
+    no time."""
+    sc = swirl(86, cscale=2.0)
+    pu.log(f"fused profiled vs graph, policy {policy}")
+    a = mpm.Simulation(sc)
+    b = mpm.Simulation(sc)
+    try:
+        for s in (a, b):
+            s.set_sort_policy(*policy)
+            s.set_fused_steps(True)
+        a.step(11)
+        ms = mpm.mpm_step_profiled(b.handle, 11, b.stream)
+        assert all(v >= 0 for v in ms.values()) and ms["k_g2p"] > 0
+        assert mpm.mpm_steps_taken(a.handle) == mpm.mpm_steps_taken(b.handle) == 11
+        ra, rb = _read(a), _read(b)
+    finally:
+        a.close()
+        b.close()
+    for f in ("x", "v", "C", "F", "m", "p"):
+        err = _rel(ra[f], rb[f])
+        pu.log(f"profiled vs graph {f}: {err:.2e}")
+        assert err < 1e-5, (f, err)
