@@ -184,6 +184,26 @@ def slab_12m(seed: int = 4, N: int = 12_000_000) -> Scene:
                  p_vol=vol / N, steps=50)
 
 
+def slab_12m_shard8(part: int = 3, parts: int = 8) -> Scene:
+    """One GPU's share of the 12M slab split over 8 GPUs: the particles of
+    slab_12m whose initial x lies in the part-th of 8 equal ranges of the
+    slab's x extent (static partition by initial position, about 1.5M
+    particles in a slab about 31 nodes thick), on the same 256^3 grid.  Part 3
+    is an interior piece: both of its x faces border another piece."""
+    full = slab_12m()
+    dx = 1.0 / full.n
+    lo, hi = 3 * dx, 1 - 3 * dx
+    w = (hi - lo) / parts
+    x0 = full.x[:, 0].astype(np.float64)
+    keep = (x0 >= lo + part * w) & (x0 < lo + (part + 1) * w)
+    return Scene(f"slab_12m_shard{parts}", f"piece {part} of {parts} of the 12M slab (x partition), "
+                 f"{int(keep.sum())} particles, 256^3 grid",
+                 np.ascontiguousarray(full.x[keep]), np.ascontiguousarray(full.v[keep]),
+                 np.ascontiguousarray(full.E_p[keep]),
+                 n=full.n, dt=full.dt, gravity=full.gravity, wall=full.wall, material=full.material,
+                 E=full.E, nu=full.nu, rho=full.rho, p_vol=full.p_vol, steps=full.steps)
+
+
 def dambreak_4m(seed: int = 5) -> Scene:
     """4,000,000 particles of weakly compressible fluid in a corner column, 256^3 grid.
 
@@ -228,6 +248,7 @@ SCENES = {
     "jelly3_55k": jelly3_55k,
     "blocks_1m": blocks_1m,
     "slab_12m": slab_12m,
+    "slab_12m_shard8": slab_12m_shard8,
     "dambreak_4m": dambreak_4m,
     "sand_3m": sand_3m,
 }
