@@ -196,14 +196,18 @@ int mpm_status(mpm_sim *sim, uint32_t *status_device, void *stream);
 /* Steps taken since creation (host-side counter, no synchronisation). */
 int64_t mpm_steps_taken(const mpm_sim *sim);
 
-/* Number of kernels a step launches, and the name of kernel k. */
+/* Number of kernel slots of a step (scan tiles, scan bins, scatter, P2G, G2P;
+ * with fused steps the last slot is the G2P2G kernel, and a step between
+ * host-scheduled sorts launches that slot alone), and the name of slot k. */
 int32_t mpm_num_kernels(void);
 const char *mpm_kernel_name(int32_t k);
 
 /* Measurement helper: run n_steps steps eagerly (the same kernels and launch
  * shapes as the graph), bracketing every kernel with HIP events on `stream`,
  * then synchronise `stream` and add each kernel's elapsed milliseconds into
- * kernel_ms[k] (host, mpm_num_kernels() entries, caller-initialised). */
+ * kernel_ms[k] (host, mpm_num_kernels() entries, caller-initialised); a
+ * slot the step does not launch adds about 0.  Unlike mpm_step, every step
+ * stores v and C. */
 int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms);
 
 /* Release the handle and its graphs (not the caller's workspace).  Waits for
