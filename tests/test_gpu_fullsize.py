@@ -61,14 +61,21 @@ def test_full_size_sampled_parity(name):
     assert gpu["status"][0] == 0
 
 
-def test_conservation_100_steps():
+@pytest.mark.parametrize("mode", ["separate", "fused_device", "fused_scheduled"])
+def test_conservation_100_steps(mode):
     """Colliding blocks with gravity off and no wall contact: grid mass equals
     particle mass and total momentum is unchanged, within 1e-6 relative
-    (momentum normalised by sum m|v|, since the blocks' momenta cancel)."""
+    (momentum normalised by sum m|v|, since the blocks' momenta cancel).  Also
+    with fused steps, sorts decided on the device (every 5 steps) or
+    scheduled by the host (every 4): 100 steps of lookahead passes, movers
+    and re-sorts as the blocks collide."""
     sc = scenes.blocks_1m(gravity=False)
-    pu.log("conservation over 100 steps")
+    pu.log(f"conservation over 100 steps, {mode}")
     sim = mpm.Simulation(sc)
     try:
+        if mode != "separate":
+            sim.set_sort_policy(5 if mode == "fused_device" else 4, 1 << 40)
+            sim.set_fused_steps(True)
         m_p = np.float64(sc.params()["rho"]) * sc.params()["p_vol"]
         v0 = sc.v.astype(np.float64)
         P0 = m_p * v0.sum(0)
