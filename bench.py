@@ -127,6 +127,9 @@ def main():
                     help="free-zone sort policy: sort at least every K steps (0 = sort every step, the default)")
     ap.add_argument("--fused", action="store_true",
                     help="fused G2P2G steps between sorts (mpm_set_fused_steps; use with --sort-interval)")
+    ap.add_argument("--alt-fused-interval", type=int, default=32,
+                    help="also time the same workload with fused steps and host-scheduled sorts every K steps "
+                         "(reported as fused_steps; 0 = skip)")
     ap.add_argument("--mover-budget", type=int, default=-1,
                     help="free-zone sort policy: also sort when more particles than this left their bins "
                          "(default: N/1000)")
@@ -186,6 +189,31 @@ def main():
     active_blocks = int(pad.reshape(nb, 8, nb, 8, nb, 8).any(axis=(1, 3, 5)).sum())
     status = sim.status()
     sim.close()
+    del sim
+    # The same workload with fused G2P2G steps between host-scheduled sorts
+    # (a sort every K steps, no mover budget), timed the same way: reported
+    # beside the headline value, which sorts every step.
+    alt = None
+    if args.alt_fused_interval > 0 and not args.fused and not free_zone:
+        K = args.alt_fused_interval
+        sim2 = mpm.Simulation(sc)
+        sim2.set_sort_policy(K, 1 << 40)
+        sim2.set_fused_steps(True)
+        sim2.step(max(args.warmup, 8))
+        torch.cuda.synchronize()
+        n_alt = max(args.steps, 2 * K)
+        t_a = time.perf_counter()
+        sim2.step(n_alt)
+        torch.cuda.synchronize()
+        t_alt = time.perf_counter() - t_a
+        st2 = sim2.status()
+        sim2.close()
+        del sim2
+        alt = {"value": round(sc.N * n_alt / t_alt, 1), "unit": "particle-steps/s",
+               "ms_per_step": round(1e3 * t_alt / n_alt, 5), "steps": n_alt,
+               "sort": f"every {K} steps, scheduled by the host; between sorts one fused G2P2G launch per step",
+               "status_clean": bool(st2[0] == 0)}
+        log(f"fused steps (sort every {K}): {alt['ms_per_step']:.4f} ms/step")
     # The practical HBM ceiling on this device: a plain 1 GiB device copy
     # (read 1 GiB, write 1 GiB), median of 5, outside the timed region.  The
     # same copy calibrates the HBM-byte counters of a rocprofv3 run.
@@ -268,6 +296,7 @@ def main():
         "device": device,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "fused_steps": alt,
     }
     print(json.dumps(out), flush=True)
 
