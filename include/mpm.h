@@ -86,7 +86,12 @@ typedef struct mpm_sim mpm_sim;
  *   nu          : Poisson ratio, 0 <= nu < 0.5 (ignored for MPM_J_FLUID).
  *   rho, p_vol  : density and initial particle volume (> 0); particle mass
  *                 is rho * p_vol.
- *   friction_deg: MPM_SAND only: friction angle in degrees, 0 < friction_deg < 90. */
+ *   friction_deg: MPM_SAND only: friction angle in degrees, 0 < friction_deg < 90.
+ *   snow_M, snow_beta, snow_xi, snow_alpha0: the snow material's
+ *                 critical-state slope M > 0 (the page's friction
+ *                 coefficient), cohesion beta >= 0, hardening xi >= 0 and the
+ *                 log plastic volume ln J_P every particle starts with
+ *                 (finite); read only for the snow material. */
 typedef struct {
   uint32_t struct_size;
   int32_t grid_n;
@@ -99,6 +104,10 @@ typedef struct {
   float rho;
   float p_vol;
   float friction_deg;
+  float snow_M;
+  float snow_beta;
+  float snow_xi;
+  float snow_alpha0;
 } mpm_params;
 
 /* Bytes of device workspace a simulation of n_particles needs (0 when the

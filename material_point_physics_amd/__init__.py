@@ -55,10 +55,12 @@ class mpm_params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("grid_n", ctypes.c_int32), ("dt", ctypes.c_float),
                 ("gravity", ctypes.c_float * 3), ("wall_nodes", ctypes.c_int32), ("material", ctypes.c_int32),
                 ("E", ctypes.c_float), ("nu", ctypes.c_float), ("rho", ctypes.c_float), ("p_vol", ctypes.c_float),
-                ("friction_deg", ctypes.c_float)]
+                ("friction_deg", ctypes.c_float), ("snow_M", ctypes.c_float), ("snow_beta", ctypes.c_float),
+                ("snow_xi", ctypes.c_float), ("snow_alpha0", ctypes.c_float)]
 
 
-def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=30.0) -> mpm_params:
+def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=30.0,
+                snow_M=0.8, snow_beta=0.9, snow_xi=5.0, snow_alpha0=-0.01) -> mpm_params:
     p = mpm_params()
     p.struct_size = ctypes.sizeof(mpm_params)
     p.grid_n, p.dt = int(n), float(dt)
@@ -67,6 +69,7 @@ def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=
     p.wall_nodes, p.material = int(wall), int(material)
     p.E, p.nu, p.rho, p.p_vol = float(E), float(nu), float(rho), float(p_vol)
     p.friction_deg = float(friction_deg)
+    p.snow_M, p.snow_beta, p.snow_xi, p.snow_alpha0 = float(snow_M), float(snow_beta), float(snow_xi), float(snow_alpha0)
     return p
 
 

@@ -28,6 +28,7 @@ import numpy as np
 FIXED_COROTATED = 0
 J_FLUID = 1
 SAND = 2
+SNOW = 3
 
 
 @dataclass
@@ -52,6 +53,10 @@ class Scene:
     J: Optional[np.ndarray] = None   # (N,) float32 initial volume ratio (None -> 1)
     extra: dict = field(default_factory=dict)
     friction_deg: float = 30.0       # SAND: friction angle in degrees
+    snow_M: float = 0.8              # SNOW: critical-state slope M (friction)
+    snow_beta: float = 0.9           # SNOW: cohesion beta
+    snow_xi: float = 5.0             # SNOW: hardening xi
+    snow_alpha0: float = -0.01       # SNOW: initial log plastic volume ln J_P
 
     @property
     def N(self) -> int:
@@ -64,7 +69,9 @@ class Scene:
                     gravity=tuple(f32(g) for g in self.gravity),
                     wall=int(self.wall), material=int(self.material),
                     E=f32(self.E), nu=f32(self.nu), rho=f32(self.rho),
-                    p_vol=f32(self.p_vol), friction_deg=f32(self.friction_deg))
+                    p_vol=f32(self.p_vol), friction_deg=f32(self.friction_deg),
+                    snow_M=f32(self.snow_M), snow_beta=f32(self.snow_beta),
+                    snow_xi=f32(self.snow_xi), snow_alpha0=f32(self.snow_alpha0))
 
 
 def _stratified(rng, cells: np.ndarray, ppc: int, dx: float) -> np.ndarray:
@@ -267,7 +274,8 @@ def random_rotation(rng, m: int) -> np.ndarray:
 def random_scene(N: int, n: int, seed: int, *, lo=None, hi=None, vscale=1.0,
                  cscale=0.0, fstretch=0.0, material=FIXED_COROTATED,
                  per_particle_E=False, dt=1e-4, gravity=(0.0, -9.8, 0.0),
-                 wall=3, E=1e4, nu=0.3, rho=1.0, friction_deg=30.0) -> Scene:
+                 wall=3, E=1e4, nu=0.3, rho=1.0, friction_deg=30.0,
+                 snow=None) -> Scene:
     """A generic seeded scene for parity and edge-case tests.
 
     Positions are i.i.d. uniform in the box [lo, hi] (default: the region
@@ -275,7 +283,8 @@ def random_scene(N: int, n: int, seed: int, *, lo=None, hi=None, vscale=1.0,
     velocities uniform in [-vscale, vscale]; when cscale > 0 an initial C with
     entries uniform in [-cscale, cscale]; when fstretch > 0 an initial
     F = R diag(s) Q^T with random rotations and stretches s in
-    [1-fstretch, 1+fstretch] (for J_FLUID: J = product of s).
+    [1-fstretch, 1+fstretch] (for J_FLUID: J = product of s).  snow: a dict
+    of Scene's snow_* fields to override (material SNOW).
     """
     rng = np.random.default_rng(seed)
     dx = 1.0 / n
@@ -302,4 +311,4 @@ def random_scene(N: int, n: int, seed: int, *, lo=None, hi=None, vscale=1.0,
                  x.astype(np.float32), v.astype(np.float32), E_p,
                  n=n, dt=dt, gravity=tuple(gravity), wall=wall, material=material,
                  E=E, nu=nu, rho=rho, p_vol=dx ** 3 / 4, steps=1, C=C, F=F, J=J,
-                 friction_deg=friction_deg)
+                 friction_deg=friction_deg, **(snow or {}))

@@ -40,7 +40,8 @@ class OrcParams(ctypes.Structure):
                 ("pad", ctypes.c_int32), ("dt", ctypes.c_double),
                 ("gravity", ctypes.c_double * 3), ("E", ctypes.c_double),
                 ("nu", ctypes.c_double), ("rho", ctypes.c_double), ("p_vol", ctypes.c_double),
-                ("friction_deg", ctypes.c_double)]
+                ("friction_deg", ctypes.c_double), ("snow_M", ctypes.c_double),
+                ("snow_beta", ctypes.c_double), ("snow_xi", ctypes.c_double)]
 
 
 _loaded = {}
@@ -70,6 +71,10 @@ def lib(prec: str = "f64") -> ctypes.CDLL:
     L.orc_sand_project.argtypes = [P, R, R]
     L.orc_sand_project.restype = ctypes.c_int
     L.orc_kirchhoff_sand.argtypes = [P, R, R, P]
+    L.orc_snow_p0.argtypes = [R, R, R]
+    L.orc_snow_p0.restype = R
+    L.orc_snow_project.argtypes = [P, P, R, R, R, R, R]
+    L.orc_snow_project.restype = ctypes.c_int
     pp = ctypes.POINTER(OrcParams)
     L.orc_grid_clear.argtypes = [pp, P, P]
     L.orc_p2g.argtypes = [pp, ctypes.c_int64, P, P, P, P, P, P, P, P]
@@ -84,7 +89,10 @@ def lib(prec: str = "f64") -> ctypes.CDLL:
     return L
 
 
-def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=30.0) -> OrcParams:
+def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=30.0,
+                snow_M=0.8, snow_beta=0.9, snow_xi=5.0, snow_alpha0=0.0) -> OrcParams:
+    """snow_alpha0 is part of the initial state (the log plastic volume every
+    particle starts with), not of the step: OracleSim puts it in J."""
     P = OrcParams()
     P.n, P.wall, P.material, P.pad = int(n), int(wall), int(material), 0
     P.dt = float(dt)
@@ -92,6 +100,7 @@ def make_params(n, dt, gravity, wall, material, E, nu, rho, p_vol, friction_deg=
         P.gravity[a] = float(gravity[a])
     P.E, P.nu, P.rho, P.p_vol = float(E), float(nu), float(rho), float(p_vol)
     P.friction_deg = float(friction_deg)
+    P.snow_M, P.snow_beta, P.snow_xi = float(snow_M), float(snow_beta), float(snow_xi)
     return P
 
 
@@ -160,6 +169,17 @@ class Oracle:
         kind = int(self.L.orc_sand_project(_ptr(F, self.prec), nu, alpha))
         return F, kind
 
+    def snow_p0(self, a, kappa, xi):
+        return float(self.L.orc_snow_p0(a, kappa, xi))
+
+    def snow_project(self, F, a, mu, lam, M, beta, xi):
+        """Returns (projected F, new log plastic volume, case: 0 elastic,
+        1 compression tip, 2 tension tip, 3 onto the ellipse)."""
+        F = self.arr(F, (3, 3)).copy()
+        av = np.array([a], dtype=self.dtype)
+        kind = int(self.L.orc_snow_project(_ptr(F, self.prec), _ptr(av, self.prec), mu, lam, M, beta, xi))
+        return F, float(av[0]), kind
+
     def kirchhoff_sand(self, F, mu, lam):
         F = self.arr(F, (3, 3))
         tau = np.zeros((3, 3), self.dtype)
@@ -171,7 +191,8 @@ class OracleSim:
     """Particle state plus a dense grid, stepped by the oracle.
 
     Arrays are AoS in the oracle's precision: x, v (N,3); C, F (N,3,3);
-    J (N,); E_p (N,) or None.  The grid after the last step is kept in
+    J (N,) (for snow: the log plastic volume a = ln J_P, starting at the
+    scene's snow_alpha0); E_p (N,) or None.  The grid after the last step is kept in
     gm (n^3), gp (n^3,3) (P2G momentum) and gv (n^3,3) (updated velocity),
     indexed [k, j, i] = node (i, j, k).
     """
@@ -194,7 +215,12 @@ class OracleSim:
         F0 = F if F is not None else scene.F
         self.F = np.tile(np.eye(3, dtype=dt), (N, 1, 1)) if F0 is None else own(F0, (N, 3, 3))
         J0 = J if J is not None else scene.J
-        self.J = np.ones(N, dt) if J0 is None else own(J0, (N,))
+        if J0 is not None:
+            self.J = own(J0, (N,))
+        elif p["material"] == 3:
+            self.J = np.full(N, p["snow_alpha0"], dt)
+        else:
+            self.J = np.ones(N, dt)
         self.E_p = None if scene.E_p is None else own(scene.E_p, (N,))
         nn = self.n ** 3
         self.gm = np.zeros(nn, dt)

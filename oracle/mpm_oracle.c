@@ -15,8 +15,12 @@
  * (Stomakhin et al. 2012), and for sand the Drucker-Prager plasticity of
  * Klar et al. 2016 ("Drucker-Prager elastoplasticity for sand animation":
  * Hencky-strain elasticity and its return mapping, here with a constant
- * friction angle).  Each step below names the passage of [RT-MPM] it
- * matches:
+ * friction angle), and for snow the non-associative Cam-clay (NACC) model
+ * of Wolper et al. 2019 ("CD-MPM: continuum damage material point methods
+ * for dynamic fracture animation"), which [RT-MPM] names for its snow scene
+ * together with its parameters (bulk modulus, Poisson ratio, friction M,
+ * cohesion beta, hardening xi), here on the same Hencky elasticity as sand.
+ * Each step below names the passage of [RT-MPM] it matches:
  *   - P2G adds weighted mass and momenta to grid nodes            [RT-MPM §4.3]
  *   - three quadratic B-spline weights per axis ("nine floats")   [RT-MPM, on-chip
  *                                                                  memory principle, §6.2.5]
@@ -49,7 +53,7 @@ typedef ORC_REAL real;
 typedef struct {
   int32_t n;          /* grid nodes per axis */
   int32_t wall;       /* sticky-wall thickness, in nodes */
-  int32_t material;   /* 0 fixed-corotated elastic, 1 weakly compressible fluid, 2 sand */
+  int32_t material;   /* 0 fixed-corotated elastic, 1 weakly compressible fluid, 2 sand, 3 snow */
   int32_t pad;
   double dt;
   double gravity[3];
@@ -58,6 +62,9 @@ typedef struct {
   double rho;         /* density */
   double p_vol;       /* initial particle volume V0 */
   double friction_deg; /* sand: friction angle, degrees */
+  double snow_M;      /* snow: slope M of the critical-state line (the page's friction coefficient) */
+  double snow_beta;   /* snow: cohesion beta (tension tip at -beta p0) */
+  double snow_xi;     /* snow: hardening xi */
 } orc_params;
 
 int orc_real_bytes(void) { return (int)sizeof(real); }
@@ -350,6 +357,77 @@ void orc_kirchhoff_sand(const real F[9], real mu, real lam, real tau[9]) {
   mat_mul_bt(G, F, tau);
 }
 
+/* ------------------------------------------------------------------ snow
+ * Non-associative Cam-clay (Wolper et al. 2019; [RT-MPM]'s snow scene) on
+ * the Hencky elasticity above.  In principal Hencky strain e, with trace
+ * t = sum e and deviator d = e - t/3, the Kirchhoff stress has
+ *   pressure      p = -tr(tau)/3 = -kappa t          (kappa = lam + 2 mu / 3)
+ *   shear measure q = sqrt(3/2) |dev tau| = sqrt(6) mu |d|.
+ * Yield surface (an ellipse in the p-q plane between p = -beta p0 and p0):
+ *   y(p, q) = (1 + 2 beta) q^2 + M^2 (p + beta p0) (p - p0) <= 0,
+ * with the hardening p0 = kappa sinh(xi max(-a, 0)), where a = ln J_P is the
+ * log of the plastic volume ratio carried by each particle.  The exponent is
+ * capped at ORC_SNOW_XCAP so that p0 stays finite in single precision (a
+ * state 10^17 times the bulk modulus, never reached in practice).
+ * Return mapping of the trial strain (non-associative: q moves, p stays,
+ * except at the tips):
+ *   p > p0        : compression tip, e = (-p0 / kappa) / 3 per axis (d = 0);
+ *   p < -beta p0  : tension tip, e = (beta p0 / kappa) / 3 per axis;
+ *   y <= 0        : elastic, unchanged;
+ *   y > 0         : d scaled so that q lands on the surface, t kept.
+ * The total volume ratio J = J_E J_P is not changed by a projection, so the
+ * log plastic volume takes what leaves the elastic one: a += t - t_new
+ * (compaction lowers a and raises p0; expansion past the tension tip
+ * softens). */
+#define ORC_SNOW_XCAP 40
+
+/* Hardening p0 = kappa sinh(xi max(-a, 0)), exponent capped. */
+real orc_snow_p0(real a, real kappa, real xi) {
+  real x = xi * (a < 0 ? -a : 0);
+  if (x > (real)ORC_SNOW_XCAP) x = (real)ORC_SNOW_XCAP;
+  return kappa * sinh(x);
+}
+
+/* The NACC return mapping of F (in place) and of the log plastic volume *a.
+ * Returns 0 (elastic), 1 (compression tip), 2 (tension tip) or 3 (onto the
+ * ellipse). */
+int orc_snow_project(real F[9], real *a, real mu, real lam, real M, real beta, real xi) {
+  real V[9], l[3], e[3];
+  sand_principal(F, V, l, e);
+  const real kappa = lam + 2 * mu / 3;
+  const real t = e[0] + e[1] + e[2];
+  real d[3], nd2 = 0;
+  for (int i = 0; i < 3; ++i) {
+    d[i] = e[i] - t / 3;
+    nd2 += d[i] * d[i];
+  }
+  const real p = -kappa * t;
+  const real p0 = orc_snow_p0(*a, kappa, xi);
+  real t_new = t, k = 1;
+  int kind;
+  if (p > p0) {
+    kind = 1;
+    t_new = -p0 / kappa;
+    k = 0;
+  } else if (p < -beta * p0) {
+    kind = 2;
+    t_new = beta * p0 / kappa;
+    k = 0;
+  } else {
+    const real q2 = 6 * mu * mu * nd2;
+    const real y = (1 + 2 * beta) * q2 + M * M * (p + beta * p0) * (p - p0);
+    if (y <= 0) return 0;
+    kind = 3;
+    /* q_new^2 = M^2 (p + beta p0) (p0 - p) / (1 + 2 beta); q2 > 0 here */
+    k = sqrt(M * M * (p + beta * p0) * (p0 - p) / ((1 + 2 * beta) * q2));
+  }
+  real m[3];
+  for (int i = 0; i < 3; ++i) m[i] = exp(t_new / 3 + k * d[i] - e[i]); /* new stretch / old stretch */
+  sand_scale(F, V, m, F);
+  *a += t - t_new;
+  return kind;
+}
+
 /* ------------------------------------------------------------ MPM phases */
 
 static int64_t node_index(int64_t n, int64_t i, int64_t j, int64_t k) { return i + n * (j + n * k); }
@@ -375,9 +453,10 @@ void orc_grid_clear(const orc_params *P, real *gm, real *gp) {
 }
 
 /* Particle-to-grid transfer, particles in index order.  Adds into gm (mass)
- * and gp (momentum).  For the elastic materials (fixed-corotated, sand) F
- * holds the deformation gradients; for the fluid J holds the volume ratios.
- * E_p may be NULL.
+ * and gp (momentum).  For the elastic materials (fixed-corotated, sand, snow)
+ * F holds the deformation gradients (snow, sand: their elastic parts); for the
+ * fluid J holds the volume ratios, for snow the log plastic volumes a.
+ * E_p may be NULL (and is NULL for snow, whose modulus is P->E).
  * Returns the number of particles skipped because their stencil left the
  * grid (0 for valid input). */
 int64_t orc_p2g(const orc_params *P, int64_t N, const real *x, const real *v, const real *C,
@@ -396,7 +475,7 @@ int64_t orc_p2g(const orc_params *P, int64_t N, const real *x, const real *v, co
     if (P->material == 1) {
       real t = orc_kirchhoff_fluid(J[p], E);
       for (int i = 0; i < 9; ++i) tau[i] = (i % 4 == 0) ? t : 0;
-    } else if (P->material == 2) {
+    } else if (P->material == 2 || P->material == 3) { /* Hencky elasticity (sand, snow) */
       real mu, lam;
       orc_lame(E, (real)P->nu, &mu, &lam);
       orc_kirchhoff_sand(F + 9 * p, mu, lam, tau);
@@ -443,7 +522,8 @@ void orc_grid_update(const orc_params *P, const real *gm, const real *gp, real *
 }
 
 /* Grid-to-particle transfer with the APIC affine matrix, deformation-gradient
- * (or volume-ratio) update (for sand followed by the plasticity projection),
+ * (or volume-ratio) update (for sand and snow followed by the plasticity
+ * projection; snow's also updates its log plastic volume in J),
  * advection and the position clamp to [2dx, (n-2)dx].  Returns the number of
  * clamped components. */
 int64_t orc_g2p(const orc_params *P, int64_t N, real *x, real *v, real *C, real *F, real *J,
@@ -481,6 +561,11 @@ int64_t orc_g2p(const orc_params *P, int64_t N, real *x, real *v, real *C, real 
       /* sand: the plasticity projection of the updated F ([RT-MPM] merges the
        * SVD, the plasticity projection and the stress into one particle phase) */
       if (P->material == 2) orc_sand_project(F + 9 * p, (real)P->nu, orc_sand_alpha((real)P->friction_deg));
+      if (P->material == 3) {
+        real mu, lam;
+        orc_lame((real)P->E, (real)P->nu, &mu, &lam);
+        orc_snow_project(F + 9 * p, J + p, mu, lam, (real)P->snow_M, (real)P->snow_beta, (real)P->snow_xi);
+      }
     }
     for (int i = 0; i < 9; ++i) C[9 * p + i] = Cn[i];
     for (int a = 0; a < 3; ++a) {

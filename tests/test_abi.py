@@ -128,5 +128,5 @@ def test_params_struct_matches_header():
     for (name, ct), (ty, _, arr) in zip(mpm.mpm_params._fields_, decl):
         want = ctype[ty] * int(arr[1:-1]) if arr else ctype[ty]
         assert ctypes.sizeof(ct) == ctypes.sizeof(want), name
-    # uint32 + int32 + float + float[3] + int32 + int32 + 5 floats = 52 bytes
-    assert ctypes.sizeof(mpm.mpm_params) == 52
+    # uint32 + int32 + float + float[3] + int32 + int32 + 9 floats = 68 bytes
+    assert ctypes.sizeof(mpm.mpm_params) == 68

@@ -63,6 +63,22 @@ MUTANTS = [
     ("sand stress of the fixed-corotated model", "orc_kirchhoff_sand(F + 9 * p, mu, lam, tau);",
      "orc_kirchhoff_fc(F + 9 * p, mu, lam, tau);"),
     ("sand stretch scaled inversely", "m[i] = exp(h[i] - e[i]);", "m[i] = exp(e[i] - h[i]);"),
+    ("snow hardens on expansion", "real x = xi * (a < 0 ? -a : 0);", "real x = xi * (a > 0 ? a : 0);"),
+    ("snow hardening uncapped", "if (x > (real)ORC_SNOW_XCAP) x = (real)ORC_SNOW_XCAP;", ""),
+    ("snow hardening cosh", "return kappa * sinh(x);", "return kappa * (cosh(x) - 1);"),
+    ("snow bulk modulus is lambda", "const real kappa = lam + 2 * mu / 3;", "const real kappa = lam;"),
+    ("snow q without sqrt(3/2)", "const real q2 = 6 * mu * mu * nd2;", "const real q2 = 4 * mu * mu * nd2;"),
+    ("snow tension tip without beta", "t_new = beta * p0 / kappa;", "t_new = p0 / kappa;"),
+    ("snow tension test without beta", "} else if (p < -beta * p0) {", "} else if (p < -p0) {"),
+    ("snow plastic volume sign", "*a += t - t_new;", "*a += t_new - t;"),
+    ("snow yield with M unsquared", "const real y = (1 + 2 * beta) * q2 + M * M * (p + beta * p0) * (p - p0);",
+     "const real y = (1 + 2 * beta) * q2 + M * (p + beta * p0) * (p - p0);"),
+    ("snow surface without the cohesion factor", "((1 + 2 * beta) * q2));", "(q2));"),
+    ("snow surface moves the trace", "m[i] = exp(t_new / 3 + k * d[i] - e[i]);", "m[i] = exp(k * e[i] - e[i]);"),
+    ("snow compression tip sign", "t_new = -p0 / kappa;", "t_new = p0 / kappa;"),
+    ("snow no projection in G2P", "if (P->material == 3) {", "if (0) {"),
+    ("snow stress of the fixed-corotated model", "} else if (P->material == 2 || P->material == 3) {",
+     "} else if (P->material == 2) {"),
 ]
 
 
@@ -92,6 +108,12 @@ def _all_pins():
         pins.test_sand_projection_is_objective,
         lambda o: pins.test_sand_step_projects_in_g2p(),
         lambda o: pins.test_sand_stress_force_is_energy_gradient(),
+        pins.test_snow_hardening_closed_form,
+        pins.test_snow_projection_cases,
+        pins.test_snow_projection_without_hardening,
+        pins.test_snow_projection_is_objective,
+        lambda o: pins.test_snow_step_projects_in_g2p(),
+        lambda o: pins.test_snow_p2g_uses_hencky_stress(),
     ]
     del rng
     return out

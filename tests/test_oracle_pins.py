@@ -530,3 +530,215 @@ def test_sand_stress_force_is_energy_gradient():
             um[node, a] = -h
             dE = (energy(up) - energy(um)) / (2 * h)
             assert abs(force[node, a] + dE) <= 1e-6 * np.abs(force).max() + 1e-12
+
+
+# ------------------------------------------------------------ snow pins
+# Non-associative Cam-clay (Wolper et al. 2019) on the Hencky elasticity of
+# the sand model.  The pressure p = -tr(tau)/3 and the shear measure
+# q = sqrt(3/2) |dev tau| are read off the Kirchhoff stress that numpy's SVD
+# gives (the helpers above), the yield function y(p, q) = (1 + 2 beta) q^2 +
+# M^2 (p + beta p0)(p - p0) is the model's definition, and the bulk modulus is
+# written as E / (3 (1 - 2 nu)), not through the oracle's Lame constants.
+
+SNOW = dict(E=6e5, nu=0.3, M=0.8, beta=0.9, xi=5.0)   # kappa = 5e5, the page's snow
+
+
+def _snow_moduli(E=SNOW["E"], nu=SNOW["nu"]):
+    mu = E / (2 * (1 + nu))
+    lam = E * nu / ((1 + nu) * (1 - 2 * nu))
+    return mu, lam, E / (3 * (1 - 2 * nu))
+
+
+def _pq(F, mu, lam):
+    tau = _hencky_tau(F, mu, lam)
+    p = -np.trace(tau) / 3
+    dev = tau + p * np.eye(3)
+    return p, np.sqrt(1.5 * np.sum(dev * dev))
+
+
+def _nacc_y(p, q, p0, M=SNOW["M"], beta=SNOW["beta"]):
+    return (1 + 2 * beta) * q * q + M * M * (p + beta * p0) * (p - p0)
+
+
+def _strain_F(rng, t, d):
+    """F = U diag(exp(e)) V^T with principal Hencky strains e = t/3 + d
+    (d is made traceless here)."""
+    d = np.asarray(d, np.float64)
+    e = t / 3 + d - d.mean()
+    U, V = scenes.random_rotation(rng, 2)
+    return U @ np.diag(np.exp(e)) @ V.T, U, V, e
+
+
+def _snow_project(orc, F, a):
+    mu, lam, _ = _snow_moduli()
+    return orc.snow_project(F, a, mu, lam, SNOW["M"], SNOW["beta"], SNOW["xi"])
+
+
+def test_snow_hardening_closed_form(orc64):
+    """p0 = kappa sinh(xi max(-a, 0)): no cohesion or compaction strength at
+    a >= 0, growth with compaction (a < 0), the exponent capped at 40."""
+    kappa, xi = 5e5, 5.0
+    assert orc64.snow_p0(0.0, kappa, xi) == 0.0
+    assert orc64.snow_p0(0.3, kappa, xi) == 0.0
+    for a in (-1e-4, -0.01, -0.2, -1.0):
+        assert np.isclose(orc64.snow_p0(a, kappa, xi), kappa * np.sinh(-xi * a), rtol=1e-13)
+    assert orc64.snow_p0(-0.02, kappa, xi) > orc64.snow_p0(-0.01, kappa, xi)
+    assert np.isclose(orc64.snow_p0(-100.0, kappa, xi), kappa * np.sinh(40.0), rtol=1e-13)
+
+
+def _volume_kept(F, a, G, a1):
+    """The projection moves volume between the elastic and the plastic part:
+    ln det F_E + ln J_P is unchanged."""
+    assert np.isclose(np.log(np.linalg.det(G)) + a1, np.log(np.linalg.det(F)) + a, rtol=0, atol=1e-13)
+
+
+def test_snow_projection_cases(orc64):
+    """Each branch of the return mapping against the model's definitions: an
+    elastic state is left alone; past p0 the state goes to the compression
+    tip (p = p0, q = 0), below -beta p0 to the tension tip; otherwise q is
+    scaled onto the ellipse with p, the singular vectors and the deviator's
+    direction kept.  The log plastic volume takes what leaves the elastic
+    one, and projecting again changes nothing."""
+    rng = np.random.default_rng(320)
+    mu, lam, kappa = _snow_moduli()
+    a = -0.01
+    p0 = kappa * np.sinh(SNOW["xi"] * 0.01)
+    # elastic: p inside (-beta p0, p0), small deviator
+    F, U, V, e = _strain_F(rng, -0.02, [0.004, -0.001, -0.003])
+    p, q = _pq(F, mu, lam)
+    assert -SNOW["beta"] * p0 < p < p0 and _nacc_y(p, q, p0) < 0
+    G, a1, kind = _snow_project(orc64, F, a)
+    assert kind == 0 and np.array_equal(G, F) and a1 == a
+    # compression tip
+    F, U, V, e = _strain_F(rng, -0.2, [0.03, -0.01, -0.02])
+    assert _pq(F, mu, lam)[0] > p0
+    G, a1, kind = _snow_project(orc64, F, a)
+    assert kind == 1
+    s = np.exp(-p0 / kappa / 3)
+    assert np.allclose(G, s * U @ V.T, atol=1e-13)
+    pG, qG = _pq(G, mu, lam)
+    assert np.isclose(pG, p0, rtol=1e-11) and qG < 1e-8 * p0
+    assert np.isclose(a1, a + e.sum() + p0 / kappa, rtol=0, atol=1e-14)
+    _volume_kept(F, a, G, a1)
+    # tension tip
+    F, U, V, e = _strain_F(rng, 0.1, [0.02, 0.0, -0.02])
+    assert _pq(F, mu, lam)[0] < -SNOW["beta"] * p0
+    G, a1, kind = _snow_project(orc64, F, a)
+    assert kind == 2
+    assert np.allclose(G, np.exp(SNOW["beta"] * p0 / kappa / 3) * U @ V.T, atol=1e-13)
+    assert np.isclose(_pq(G, mu, lam)[0], -SNOW["beta"] * p0, rtol=1e-11)
+    assert a1 > a
+    _volume_kept(F, a, G, a1)
+    # tension between -p0 and -beta p0 (past the cohesion limit) also goes to that tip
+    F, U, V, e = _strain_F(rng, 0.0475, [0.01, 0.0, -0.01])
+    assert -p0 < _pq(F, mu, lam)[0] < -SNOW["beta"] * p0
+    G, a1, kind = _snow_project(orc64, F, a)
+    assert kind == 2 and np.isclose(_pq(G, mu, lam)[0], -SNOW["beta"] * p0, rtol=1e-11)
+    # just outside the ellipse: (1 + 2 beta) q^2 = 1.125 M^2 (p + beta p0)(p0 - p)
+    t = -0.02
+    X = (-kappa * t + SNOW["beta"] * p0) * (p0 + kappa * t)
+    qt = np.sqrt(1.125 * SNOW["M"] ** 2 * X / (1 + 2 * SNOW["beta"]))
+    dn = np.array([1.0, -0.3, -0.7])
+    dn = (dn - dn.mean()) / np.linalg.norm(dn - dn.mean())
+    F, U, V, e = _strain_F(rng, t, qt / (np.sqrt(6) * mu) * dn)
+    p, q = _pq(F, mu, lam)
+    assert np.isclose(q, qt, rtol=1e-9) and np.isclose(_nacc_y(p, q, p0), (1 + 2 * SNOW["beta"]) * q * q / 9, rtol=1e-6)
+    G, a1, kind = _snow_project(orc64, F, a)
+    assert kind == 3 and abs(_nacc_y(*_pq(G, mu, lam), p0)) < 1e-10 * q * q
+    # onto the ellipse
+    for t, d in ((-0.02, [0.05, -0.01, -0.04]), (0.005, [0.03, 0.01, -0.04]), (-0.045, [0.08, -0.05, -0.03])):
+        F, U, V, e = _strain_F(rng, t, d)
+        p, q = _pq(F, mu, lam)
+        assert -SNOW["beta"] * p0 < p < p0 and _nacc_y(p, q, p0) > 0
+        G, a1, kind = _snow_project(orc64, F, a)
+        assert kind == 3 and a1 == a
+        pG, qG = _pq(G, mu, lam)
+        assert np.isclose(pG, p, rtol=1e-11)
+        assert abs(_nacc_y(pG, qG, p0)) < 1e-10 * q * q
+        assert np.isclose(qG ** 2, SNOW["M"] ** 2 * (p + SNOW["beta"] * p0) * (p0 - p) / (1 + 2 * SNOW["beta"]),
+                          rtol=1e-10)
+        e1 = np.log(np.diag(U.T @ G @ V))
+        assert np.allclose(U.T @ G @ V, np.diag(np.exp(e1)), atol=1e-12)
+        d0, d1 = e - e.mean(), e1 - e1.mean()
+        assert np.allclose(d1 / np.linalg.norm(d1), d0 / np.linalg.norm(d0), atol=1e-10)
+        _volume_kept(F, a, G, a1)
+        G2, a2, kind2 = _snow_project(orc64, G, a1)
+        assert np.allclose(G2, G, atol=1e-12) and a2 == a1
+
+
+def test_snow_projection_without_hardening(orc64):
+    """With a >= 0 the ellipse collapses to the point p = 0: every state but
+    the undeformed one goes to J_E = 1 with no deviator (a rotation), and the
+    whole log-volume change moves to the plastic part."""
+    rng = np.random.default_rng(321)
+    for t in (-0.02, 0.02):
+        F, U, V, e = _strain_F(rng, t, [0.01, 0.0, -0.01])
+        G, a1, kind = _snow_project(orc64, F, 0.05)
+        assert kind in (1, 2)
+        assert np.allclose(G, U @ V.T, atol=1e-13)
+        assert np.isclose(a1, 0.05 + e.sum(), atol=1e-14)
+
+
+def test_snow_projection_is_objective(orc64):
+    """project(Q F) = Q project(F) and project(F Q) = project(F) Q, with the
+    same log plastic volume."""
+    rng = np.random.default_rng(322)
+    for t, d in ((-0.02, [0.05, -0.01, -0.04]), (-0.2, [0.03, -0.01, -0.02]), (0.1, [0.02, 0.0, -0.02]),
+                 (-0.02, [0.004, -0.001, -0.003])):
+        F = _strain_F(rng, t, d)[0]
+        Q = scenes.random_rotation(rng, 1)[0]
+        G, a, k = _snow_project(orc64, F, -0.01)
+        GQ, aq, kq = _snow_project(orc64, Q @ F, -0.01)
+        QG, ar, kr = _snow_project(orc64, F @ Q, -0.01)
+        assert k == kq == kr
+        assert np.allclose(GQ, Q @ G, atol=1e-11) and np.allclose(QG, G @ Q, atol=1e-11)
+        assert np.isclose(aq, a, atol=1e-14) and np.isclose(ar, a, atol=1e-14)
+
+
+def test_snow_step_projects_in_g2p():
+    """G2P of snow from the affine grid field v(x) = c (x - 1/2) (gathered
+    exactly, C = c I: the affine-reproduction pin), F = I and a = -0.001: the
+    updated F = (1 + dt c) I lies past the compression tip for c < 0 and past
+    the tension tip for c > 0, and ends there, with the singular values and
+    the log plastic volume of the closed forms (t = 3 ln(1 + dt c))."""
+    E = 100.0
+    for c, sgn in ((-40.0, 1), (40.0, -1)):
+        sc = scenes.random_scene(50, 16, 19, lo=[0.4] * 3, hi=[0.6] * 3, vscale=0.0, gravity=(0, 0, 0), wall=0,
+                                 material=scenes.SNOW, E=E, nu=SNOW["nu"],
+                                 snow=dict(snow_M=SNOW["M"], snow_beta=SNOW["beta"], snow_xi=SNOW["xi"],
+                                           snow_alpha0=-0.001))
+        P = sc.params()
+        n = P["n"]
+        sim = oracle.OracleSim(sc, "f64")
+        a0 = P["snow_alpha0"]
+        assert np.all(sim.J == a0)
+        k, j, i = np.meshgrid(np.arange(n), np.arange(n), np.arange(n), indexing="ij")
+        nodes = np.stack([i, j, k], axis=-1).reshape(-1, 3) / n
+        sim.gv[:] = c * (nodes - 0.5)
+        sim.g2p()
+        assert np.allclose(sim.C, c * np.eye(3), atol=1e-10)
+        # the parameters as the scene rounds them (float32, as the C ABI takes them)
+        mu, lam, kappa = _snow_moduli(E=P["E"], nu=P["nu"])
+        beta = P["snow_beta"]
+        t = 3 * np.log1p(P["dt"] * c)
+        p0 = kappa * np.sinh(P["snow_xi"] * -a0)
+        assert (-kappa * t > p0) if sgn > 0 else (-kappa * t < -beta * p0)
+        tn = -p0 / kappa if sgn > 0 else beta * p0 / kappa
+        s = np.linalg.svd(sim.F, compute_uv=False)
+        assert np.allclose(s, np.exp(tn / 3), rtol=1e-12)
+        assert np.allclose(sim.J, a0 + t - tn, rtol=0, atol=1e-12)
+
+
+def test_snow_p2g_uses_hencky_stress():
+    """Snow's P2G stress is the Hencky stress of its elastic F, the same as
+    the sand model's (pinned by its energy above): equal grids from equal
+    states."""
+    grids = []
+    for mat in (scenes.SAND, scenes.SNOW):
+        sc = scenes.random_scene(40, 16, 20, lo=[0.35] * 3, hi=[0.65] * 3, fstretch=0.05, cscale=3.0,
+                                 material=mat, E=50.0)
+        sim = oracle.OracleSim(sc, "f64")
+        sim.p2g()
+        grids.append(sim.gp.copy())
+    assert np.abs(grids[0]).max() > 0
+    assert np.array_equal(grids[0], grids[1])
