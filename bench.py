@@ -47,7 +47,7 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
     back, plus v and C (stored on the last step of each launch, and on every
     profiled step), and per active node reads the window once, writes the
     next accumulator and clears the one of two steps before."""
-    f = 4 if material == 1 else 36  # fluid J, else F (elastic, sand)
+    f = 4 if material == 1 else 36  # fluid J, else F (elastic, sand, snow)
     e = 4 if has_E else 0
     if fused:
         kb = kernel_bytes(N, active_nodes, nbins, material, has_E, sorted_steps=False)
@@ -235,7 +235,8 @@ def main():
               "compute_units": props.multi_processor_count,
               "memory_GB": round(props.total_memory / 1e9, 1)}
     log(f"device {device}; plain 1 GiB copy {copy_gbps:.0f} GB/s")
-    kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None,
+    # (snow's per-particle slot carries its log plastic volume, read and written like E_p)
+    kb = kernel_bytes(sc.N, active_nodes, ((n + 3) // 4) ** 3, sc.material, sc.E_p is not None or sc.material == 3,
                       sorted_steps=not free_zone, fused=args.fused)
     kernels = {k: {"avg_ms": round(kavg[k], 5), "alg_bytes": kb[k],
                    "GBps": round(kb[k] / (kavg[k] * 1e-3) / 1e9, 1)} for k in kavg}
@@ -282,7 +283,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{sc.name}: {sc.description}", "particles": sc.N, "grid": f"{n}^3",
-                   "dt": sc.dt, "material": {0: "fixed-corotated", 1: "J-fluid", 2: "Drucker-Prager sand"}[sc.material],
+                   "dt": sc.dt, "material": {0: "fixed-corotated", 1: "J-fluid", 2: "Drucker-Prager sand", 3: "NACC snow"}[sc.material],
                    "sort": (f"free zone: at least every {args.sort_interval} steps or above {budget} movers "
                             "(byte model assumes no sort in the timed steps)") if free_zone else "every step",
                    "fused_g2p2g": bool(args.fused)},

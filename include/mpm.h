@@ -56,6 +56,8 @@ extern "C" {
 #define MPM_FIXED_COROTATED 0 /* elastic solid, state F (3x3) */
 #define MPM_J_FLUID 1         /* weakly compressible fluid, state J (scalar) */
 #define MPM_SAND 2            /* Drucker-Prager sand, state F (3x3, elastic part) */
+#define MPM_SNOW 3            /* non-associative Cam-clay snow, state F (3x3, elastic part)
+                                 and the log plastic volume ln J_P (scalar) */
 
 /* ---- status word bits (see mpm_status) ---- */
 #define MPM_STATUS_NONFINITE 0x1u  /* a NaN or Inf appeared in particle velocity, C or position */
@@ -76,11 +78,18 @@ typedef struct mpm_sim mpm_sim;
  *   wall_nodes  : sticky-wall thickness: all velocity components are zeroed
  *                 on nodes with any index < wall_nodes or >= grid_n - wall_nodes
  *                 (0 <= wall_nodes <= grid_n/2).
- *   material    : MPM_FIXED_COROTATED, MPM_J_FLUID or MPM_SAND (Drucker-
+ *   material    : MPM_FIXED_COROTATED, MPM_J_FLUID, MPM_SAND (Drucker-
  *                 Prager plasticity in Hencky strain with a constant friction
  *                 angle, projected after every deformation-gradient update:
  *                 the page merges the SVD, the plasticity projection and the
- *                 stress into the particle phase of P2G).
+ *                 stress into the particle phase of P2G) or MPM_SNOW (the
+ *                 non-associative Cam-clay model of Wolper et al. 2019, which
+ *                 the page names for its snow scene with bulk modulus,
+ *                 Poisson ratio, M, beta and xi: yield ellipse (1 + 2 beta)
+ *                 q^2 + M^2 (p + beta p0)(p - p0) <= 0 in the pressure p and
+ *                 shear measure q of the Hencky stress, hardening p0 = K
+ *                 sinh(xi max(-a, 0)) with the log plastic volume a, projected
+ *                 as MPM_SAND is; E > 0).
  *   E           : Young's modulus (bulk modulus K for MPM_J_FLUID), >= 0;
  *                 used when no per-particle modulus is given.
  *   nu          : Poisson ratio, 0 <= nu < 0.5 (ignored for MPM_J_FLUID).
@@ -131,7 +140,9 @@ size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles);
  *                 and MPM_SAND (its elastic part, used as given until the
  *                 first update), or (N) volume ratios J for MPM_J_FLUID; NULL
  *                 for I (or 1).
- *   E_p         : device, (N) per-particle Young's modulus, or NULL for params->E.
+ *   E_p         : device, (N) per-particle Young's modulus, or NULL for params->E;
+ *                 must be NULL for MPM_SNOW (MPM_ERR_INVALID_ARG otherwise), whose
+ *                 particles carry their log plastic volume instead.
  *   workspace   : device, at least mpm_workspace_bytes(params, N) bytes,
  *                 256-byte aligned, owned by the caller, and must outlive the
  *                 handle.  The library never allocates device memory.
@@ -187,10 +198,18 @@ int mpm_set_fused_steps(mpm_sim *sim, int32_t enable);
 
 /* Copy the particle state after the last step, in creation order, into
  * caller-owned device arrays: x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)
- * for the elastic material and sand (for sand the elastic part after the
- * step's plasticity projection) or (N) for the fluid.  Any output may be NULL.
- * Asynchronous on `stream`. */
+ * for the elastic material, sand and snow (for sand and snow the elastic part
+ * after the step's plasticity projection) or (N) for the fluid.  Any output
+ * may be NULL.  Asynchronous on `stream`. */
 int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J, void *stream);
+
+/* Snow only: copy each particle's log plastic volume a = ln J_P after the last
+ * step (after its plasticity projection, as mpm_read_particles reads F), in
+ * creation order, into the caller-owned device array alpha (N).  The snow
+ * model's hardening state (the page's snow scene; Wolper et al. 2019).
+ * Before any step: params->snow_alpha0.  MPM_ERR_INVALID_ARG for a NULL
+ * alpha or another material.  Asynchronous on `stream`. */
+int mpm_read_plastic_state(mpm_sim *sim, float *alpha, void *stream);
 
 /* Copy the grid state of the last step into caller-owned dense device arrays:
  * mass (n^3) and momentum (n^3 x 3) = m_i * v_i after gravity and walls.

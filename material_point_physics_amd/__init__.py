@@ -29,6 +29,7 @@ MPM_ERR_STATE = -4
 MPM_FIXED_COROTATED = 0
 MPM_J_FLUID = 1
 MPM_SAND = 2
+MPM_SNOW = 3
 
 MPM_STATUS_NONFINITE = 0x1
 MPM_STATUS_CLAMPED = 0x2
@@ -39,7 +40,7 @@ MPM_STATUS_WORDS = 8
 
 # Every symbol include/mpm.h declares.
 EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_set_sort_policy", "mpm_set_fused_steps",
-           "mpm_read_particles",
+           "mpm_read_particles", "mpm_read_plastic_state",
            "mpm_read_grid",
            "mpm_status", "mpm_steps_taken", "mpm_num_kernels", "mpm_kernel_name", "mpm_step_profiled",
            "mpm_destroy", "mpm_error_string")
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.mpm_set_fused_steps.argtypes = [vp, i32]
     L.mpm_set_fused_steps.restype = ctypes.c_int
     L.mpm_read_particles.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.mpm_read_plastic_state.argtypes = [vp, vp, vp]
+    L.mpm_read_plastic_state.restype = ctypes.c_int
     L.mpm_read_particles.restype = ctypes.c_int
     L.mpm_read_grid.argtypes = [vp, vp, vp, vp]
     L.mpm_read_grid.restype = ctypes.c_int
@@ -177,6 +180,10 @@ def mpm_set_fused_steps(sim: int, enable: int) -> None:
 def mpm_read_particles(sim: int, x=None, v=None, C=None, F_or_J=None, stream=None) -> None:
     _check(lib().mpm_read_particles(sim, _addr(x), _addr(v), _addr(C), _addr(F_or_J), _stream(stream)),
            "mpm_read_particles")
+
+
+def mpm_read_plastic_state(sim: int, alpha, stream=None) -> None:
+    _check(lib().mpm_read_plastic_state(sim, _addr(alpha), _stream(stream)), "mpm_read_plastic_state")
 
 
 def mpm_read_grid(sim: int, mass=None, momentum=None, stream=None) -> None:
@@ -277,6 +284,13 @@ class Simulation:
         mpm_read_particles(self.handle, x, v, C, F, self.stream)
         self.stream.synchronize()
         return x, v, C, F
+
+    def read_plastic_state(self):
+        """Snow: each particle's log plastic volume ln J_P, (N,)."""
+        a = self.torch.empty((self.N,), dtype=self.torch.float32, device=self.device)
+        mpm_read_plastic_state(self.handle, a, self.stream)
+        self.stream.synchronize()
+        return a
 
     def read_grid(self):
         torch = self.torch

@@ -65,6 +65,9 @@ struct SimDev {
   float mass, vol, E;
   float mu_per_E, lam_per_E;  // Lame parameters per unit Young's modulus
   float alpha, dp_c;          // sand: cone slope of the friction angle, (1 + nu) / (1 - 2 nu)
+  float kappa_per_E;          // snow: bulk modulus per unit Young's modulus, 1 / (3 (1 - 2 nu))
+  float snow_m2, snow_beta, snow_xi, snow_1p2b;  // snow: M^2, beta, xi, 1 + 2 beta
+  float snow_a0;              // snow: initial log plastic volume
   float stress_k;             // dt * V0 * 4 / dx^2
   float c_scale;              // 4 / dx (G2P: C = 4/dx^2 * sum w v (x_i - x_p), offsets in cells)
   float lo, hi;               // position clamp

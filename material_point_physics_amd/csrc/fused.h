@@ -78,7 +78,8 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       float xp[3] = {xq[0], xq[1], xq[2]}, Fp[FW];
 #pragma unroll
       for (int k = 0; k < FW; ++k) Fp[k] = Fq[k];
-      const float E = Eq;
+      const float E = MAT == MPM_SNOW ? s.E : Eq;  // snow: the slot holds the log plastic volume
+      float ap = Eq;
       if (valid) stream_store(idq, at_byte(out.id, so));
       if (r0 + 64u < count) {
         const bool vn = r0 + 64u + (uint32_t)lane < count;
@@ -98,13 +99,13 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       update_F<MAT>(Fp, Cn, dt);
       float A[9];
       uint32_t st = 0;
-      if (MAT == MPM_SAND) st = sand_affine(s, Fp, E, Cn, A, true);  // projection and stress
+      if (MAT == MPM_SAND || MAT == MPM_SNOW) st = plastic_affine<MAT>(s, Fp, E, ap, Cn, A, true);  // projection and stress
       if (valid) {
 #pragma unroll
         for (int k = 0; k < 3; ++k) at_byte(out.x + k * Np, so) = xn[k];
 #pragma unroll
         for (int k = 0; k < FW; ++k) stream_store(Fp[k], at_byte(out.F + k * Np, so));
-        if (HAS_E) stream_store(E, at_byte(out.E, so));
+        if (HAS_E) stream_store(MAT == MPM_SNOW ? ap : E, at_byte(out.E, so));
         if (write_vc) {
 #pragma unroll
           for (int k = 0; k < 3; ++k) stream_store(v[k], at_byte(out.v + k * Np, so));
@@ -114,7 +115,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
         if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
-      if (MAT != MPM_SAND) st = affine_momentum<MAT>(s, Fp, E, Cn, A);
+      if (MAT != MPM_SAND && MAT != MPM_SNOW) st = affine_momentum<MAT>(s, Fp, E, Cn, A);
       if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
       int b[3];
       float f[3], w[3][3], q0[3], Ad[9];

@@ -1,4 +1,4 @@
-// materials.h -- per-particle material updates: deformation gradient, stress, sand plasticity
+// materials.h -- per-particle material updates: deformation gradient, stress, sand and snow plasticity
 // Part of mpm.hip: included there, inside its anonymous namespace, after the
 // parts before it; not a standalone header.
 
@@ -123,50 +123,96 @@ __device__ __forceinline__ void stretch_scaled(const float F[9], const float W[3
       out[r * 3 + c] = F[r * 3 + 0] * M[0 * 3 + c] + F[r * 3 + 1] * M[1 * 3 + c] + F[r * 3 + 2] * M[2 * 3 + c];
 }
 
-// Sand, per particle: the plasticity projection of F (in place, when
-// project) and the APIC affine momentum A = m C - dt V0 (4/dx^2) tau with the
-// Hencky Kirchhoff stress tau = U diag(2 mu h + lam sum h) U^T of the
-// projected principal strains h (U = F V diag(1/s) is unchanged by the
-// projection, so tau is formed from the trial F and its l).  Return
-// mapping, with t = sum e and the deviator d = e - t/3: t > 0 -> tip
-// (h = 0); else g = |d| + (1 + nu)/(1 - 2 nu) t alpha, g <= 0 -> unchanged,
-// g > 0 -> h = e - g d / |d|.  Returns status bits (det F <= 0).
-__device__ __forceinline__ uint32_t sand_affine(const SimDev &s, float Fp[9], float E, const float Cp[9], float A[9],
-                                                bool project) {
-  float a[3][3], W[3][3];
+// ------------------------------------------------------------------ snow
+// Non-associative Cam-clay (Wolper et al. 2019, "CD-MPM: continuum damage
+// material point methods for dynamic fracture animation"; [RT-MPM] names it,
+// with its parameters, for its snow scene) on the Hencky elasticity of the
+// sand model.  With t = sum e and d = e - t/3 the Kirchhoff stress has
+// pressure p = -kappa t and shear measure q = sqrt(3/2) |dev tau| =
+// sqrt(6) mu |d|, so the return mapping onto the yield ellipse
+// (1 + 2 beta) q^2 + M^2 (p + beta p0)(p - p0) <= 0 is closed-form: past p0
+// the compression tip (t = -p0 / kappa, d = 0), below -beta p0 the tension
+// tip (t = beta p0 / kappa), between them with y > 0 the deviator scaled so
+// that q lands on the ellipse (t kept).  p0 = kappa sinh(xi max(-a, 0))
+// hardens with the log plastic volume a = ln J_P, which takes the log-volume
+// the projection removes from the elastic part (a += t - t_new); the
+// exponent is capped at 40 so that p0 stays finite.
+
+// Sand and snow, per particle: the plasticity projection of F (in place,
+// when project; snow also updates its log plastic volume a) and the APIC
+// affine momentum A = m C - dt V0 (4/dx^2) tau with the Hencky Kirchhoff
+// stress tau = U diag(2 mu h + lam sum h) U^T of the projected principal
+// strains h (U = F V diag(1/s) is unchanged by the projection, so tau is
+// formed from the trial F and its l).  Sand's return mapping, with the
+// deviator d = e - t/3: t > 0 -> tip (h = 0); else g = |d| + (1 + nu)/(1 -
+// 2 nu) t alpha, g <= 0 -> unchanged, g > 0 -> h = e - g d / |d|.  Returns
+// status bits (det F <= 0).
+template <int MAT>
+__device__ __forceinline__ uint32_t plastic_affine(const SimDev &s, float Fp[9], float E, float &a,
+                                                   const float Cp[9], float A[9], bool project) {
+  float am[3][3], W[3][3];
 #pragma unroll
   for (int r = 0; r < 3; ++r)
 #pragma unroll
-    for (int c = 0; c < 3; ++c) a[r][c] = Fp[0 * 3 + r] * Fp[0 * 3 + c] + Fp[1 * 3 + r] * Fp[1 * 3 + c] + Fp[2 * 3 + r] * Fp[2 * 3 + c];
-  eigen_sym3(a, W);
+    for (int c = 0; c < 3; ++c) am[r][c] = Fp[0 * 3 + r] * Fp[0 * 3 + c] + Fp[1 * 3 + r] * Fp[1 * 3 + c] + Fp[2 * 3 + r] * Fp[2 * 3 + c];
+  eigen_sym3(am, W);
   float l[3], e[3];
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
-    l[i] = fmaxf(a[i][i], 1e-6f);
+    l[i] = fmaxf(am[i][i], 1e-6f);
     e[i] = 0.5f * logf(l[i]);
   }
   const uint32_t st = det3(Fp) > 0.f ? 0u : (uint32_t)MPM_STATUS_INVERTED;
+  const float mu = E * s.mu_per_E, lam = E * s.lam_per_E;
   float h[3] = {e[0], e[1], e[2]};
   bool moved = false;
   if (project) {
     const float t = e[0] + e[1] + e[2];
     const float d[3] = {e[0] - t / 3.f, e[1] - t / 3.f, e[2] - t / 3.f};
-    const float nd = sqrtf(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
-    if (t > 0.f) {
-      h[0] = h[1] = h[2] = 0.f;
-      moved = true;
-    } else {
-      const float g = nd + s.dp_c * t * s.alpha;
-      if (g > 0.f) {
-        const float k = g / nd;
-#pragma unroll
-        for (int i = 0; i < 3; ++i) h[i] = e[i] - k * d[i];
+    const float nd2 = d[0] * d[0] + d[1] * d[1] + d[2] * d[2];
+    if (MAT == MPM_SAND) {
+      const float nd = sqrtf(nd2);
+      if (t > 0.f) {
+        h[0] = h[1] = h[2] = 0.f;
         moved = true;
+      } else {
+        const float g = nd + s.dp_c * t * s.alpha;
+        if (g > 0.f) {
+          const float k = g / nd;
+#pragma unroll
+          for (int i = 0; i < 3; ++i) h[i] = e[i] - k * d[i];
+          moved = true;
+        }
+      }
+    } else {
+      const float kappa = E * s.kappa_per_E;
+      const float p = -kappa * t;
+      const float p0 = kappa * sinhf(fminf(s.snow_xi * fmaxf(-a, 0.f), 40.f));
+      float tn = t, k = 0.f;
+      if (p > p0) {
+        tn = -p0 / kappa;
+        moved = true;
+      } else if (p < -s.snow_beta * p0) {
+        tn = s.snow_beta * p0 / kappa;
+        moved = true;
+      } else {
+        // y > 0  <=>  (1 + 2 beta) q^2 > X = M^2 (p + beta p0)(p0 - p) >= 0
+        const float q2 = 6.f * mu * mu * nd2;
+        const float X = s.snow_m2 * (p + s.snow_beta * p0) * (p0 - p);
+        if (s.snow_1p2b * q2 > X) {
+          k = sqrtf(X / (s.snow_1p2b * q2));
+          moved = true;
+        }
+      }
+      if (moved) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) h[i] = tn / 3.f + k * d[i];
+        a += t - tn;
       }
     }
   }
   // tau = F V diag((2 mu h + lam sum h) / l) V^T F^T, F the trial F
-  const float mu = E * s.mu_per_E, lam = E * s.lam_per_E, ht = h[0] + h[1] + h[2];
+  const float ht = h[0] + h[1] + h[2];
   float q[3], G[9];
 #pragma unroll
   for (int i = 0; i < 3; ++i) q[i] = (2.f * mu * h[i] + lam * ht) / l[i];

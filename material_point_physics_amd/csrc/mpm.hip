@@ -6,7 +6,8 @@
 // grid update and G2P; the equations are the textbook MLS-MPM with quadratic
 // B-splines, APIC transfer and the fixed-corotated model (Hu et al. 2018;
 // Jiang et al. 2015; Stomakhin et al. 2012), plus a weakly compressible
-// fluid and Drucker-Prager sand (Klar et al. 2016).
+// fluid, Drucker-Prager sand (Klar et al. 2016) and non-associative Cam-clay
+// snow (Wolper et al. 2019), the last two on Hencky elasticity.
 //
 // Step = 5 kernels, captured into HIP graphs per phase (step number mod 4:
 // the particle buffer and the grid accumulator the step uses):
@@ -87,8 +88,16 @@ bool valid_params(const mpm_params *p) {
   for (int a = 0; a < 3; ++a)
     if (!std::isfinite(p->gravity[a])) return false;
   if (p->wall_nodes < 0 || p->wall_nodes > p->grid_n / 2) return false;
-  if (p->material != MPM_FIXED_COROTATED && p->material != MPM_J_FLUID && p->material != MPM_SAND) return false;
+  if (p->material != MPM_FIXED_COROTATED && p->material != MPM_J_FLUID && p->material != MPM_SAND &&
+      p->material != MPM_SNOW)
+    return false;
   if (p->material == MPM_SAND && !(p->friction_deg > 0.f && p->friction_deg < 90.f)) return false;
+  if (p->material == MPM_SNOW) {
+    // (the tips divide by the bulk modulus: E > 0)
+    if (!(p->E > 0.f) || !(p->snow_M > 0.f) || !std::isfinite(p->snow_M)) return false;
+    if (!(p->snow_beta >= 0.f) || !std::isfinite(p->snow_beta)) return false;
+    if (!(p->snow_xi >= 0.f) || !std::isfinite(p->snow_xi) || !std::isfinite(p->snow_alpha0)) return false;
+  }
   if (!(p->E >= 0.f) || !std::isfinite(p->E)) return false;
   if (p->material != MPM_J_FLUID && !(p->nu >= 0.f && p->nu < 0.5f)) return false;
   if (!(p->rho > 0.f) || !std::isfinite(p->rho)) return false;
@@ -169,6 +178,13 @@ size_t layout(const mpm_params *p, int64_t N, bool has_E, char *base, SimDev *d)
     const double sp = std::sin((double)p->friction_deg * 3.14159265358979323846 / 180.0);
     d->alpha = p->material == MPM_SAND ? (float)(std::sqrt(2.0 / 3.0) * 2.0 * sp / (3.0 - sp)) : 0.f;
     d->dp_c = (float)((1.0 + nu) / (1.0 - 2.0 * nu));
+    // snow (non-associative Cam-clay): kappa = lam + 2 mu / 3 = E / (3 (1 - 2 nu))
+    d->kappa_per_E = (float)(1.0 / (3.0 * (1.0 - 2.0 * nu)));
+    d->snow_m2 = (float)((double)p->snow_M * (double)p->snow_M);
+    d->snow_beta = p->snow_beta;
+    d->snow_xi = p->snow_xi;
+    d->snow_1p2b = (float)(1.0 + 2.0 * (double)p->snow_beta);
+    d->snow_a0 = p->snow_alpha0;
     d->stress_k = (float)((double)p->dt * (double)p->p_vol * 4.0 * (double)n * (double)n);
     d->c_scale = (float)(4.0 * n);
     d->lo = 2.0f * d->dx;
@@ -277,6 +293,8 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
       } else if (d.material == MPM_SAND) {
         if (d.has_E) k_p2g<MPM_SAND, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
         else k_p2g<MPM_SAND, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
+      } else if (d.material == MPM_SNOW) {  // (its scalar slot always carries the log plastic volume)
+        k_p2g<MPM_SNOW, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
       } else {
         if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
         else k_p2g<MPM_FIXED_COROTATED, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
@@ -292,12 +310,14 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
         } else if (d.material == MPM_SAND) {
           if (d.has_E) k_g2p2g<MPM_SAND, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
           else k_g2p2g<MPM_SAND, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+        } else if (d.material == MPM_SNOW) {
+          k_g2p2g<MPM_SNOW, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
         } else {
           if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
           else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
         }
       } else {
-        // (the gather does not depend on the material: sand uses the elastic instance)
+        // (the gather does not depend on the material: sand and snow use the elastic instance)
         if (d.material == MPM_J_FLUID) k_g2p<MPM_J_FLUID><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
         else k_g2p<MPM_FIXED_COROTATED><<<sim->grid_g2p, 64, 0, st>>>(d, src, p);
       }
@@ -393,13 +413,15 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
   if (!valid_params(params) || n_particles < 0 || n_particles >= (int64_t(1) << 28)) return MPM_ERR_INVALID_ARG;
   if (slot_capacity(n_particles, (params->grid_n + CB - 1) / CB) >= MAX_SLOTS) return MPM_ERR_INVALID_ARG;
   if (n_particles > 0 && !x0) return MPM_ERR_INVALID_ARG;
+  // snow's per-particle slot holds its log plastic volume: no per-particle modulus
+  if (params->material == MPM_SNOW && E_p) return MPM_ERR_INVALID_ARG;
   const size_t need = mpm_workspace_bytes(params, n_particles);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
     return MPM_ERR_WORKSPACE;
 
   mpm_sim *sim = new (std::nothrow) mpm_sim();
   if (!sim) return MPM_ERR_STATE;
-  const bool has_E = E_p != nullptr;
+  const bool has_E = E_p != nullptr || params->material == MPM_SNOW;
   layout(params, n_particles, has_E, static_cast<char *>(workspace), &sim->d);
   const SimDev &d = sim->d;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -411,10 +433,11 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, sim->device) != hipSuccess || cus <= 0)
       cus = 256;
     sim->grid_particles = (int)(((d.N + WG - 1) / WG + 7) / 8 * 8);
+    // (occupancy of the instance this material launches: snow's needs 130 VGPRs)
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_p2g<MPM_FIXED_COROTATED, false>, 64, 0) != hipSuccess ||
-        occ <= 0)
-      occ = 16;
+    const void *pk = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true>
+                                            : (const void *)k_p2g<MPM_FIXED_COROTATED, false>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pk, 64, 0) != hipSuccess || occ <= 0) occ = 16;
     // Measured: 4 waves per SIMD (16 single-wave workgroups per CU) is
     // P2G's best launch; fewer expose latency and more slowed the kernel.
     occ = occ < 16 ? occ : 16;
@@ -443,6 +466,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
                          ? (d.has_E ? (const void *)k_g2p2g<MPM_J_FLUID, true> : (const void *)k_g2p2g<MPM_J_FLUID, false>)
                      : d.material == MPM_SAND
                          ? (d.has_E ? (const void *)k_g2p2g<MPM_SAND, true> : (const void *)k_g2p2g<MPM_SAND, false>)
+                     : d.material == MPM_SNOW ? (const void *)k_g2p2g<MPM_SNOW, true>
                          : (d.has_E ? (const void *)k_g2p2g<MPM_FIXED_COROTATED, true>
                                     : (const void *)k_g2p2g<MPM_FIXED_COROTATED, false>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, fk, 64, 0) != hipSuccess || occ_f <= 0) occ_f = 8;
@@ -592,9 +616,19 @@ int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J
   if (sim->d.N == 0) return MPM_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int g = sim->grid_g2p;
-  if (sim->d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
-  else if (sim->d.material == MPM_SAND) k_read_particles<MPM_SAND><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
-  else k_read_particles<MPM_FIXED_COROTATED><<<g, 64, 0, st>>>(sim->d, sim->cur, x, v, C, F_or_J);
+  const SimDev &d = sim->d;
+  if (d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
+  else if (d.material == MPM_SAND) k_read_particles<MPM_SAND><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
+  else if (d.material == MPM_SNOW) k_read_particles<MPM_SNOW><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
+  else k_read_particles<MPM_FIXED_COROTATED><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
+int mpm_read_plastic_state(mpm_sim *sim, float *alpha, void *stream) {
+  if (!sim || !alpha || sim->d.material != MPM_SNOW) return MPM_ERR_INVALID_ARG;
+  if (sim->d.N == 0) return MPM_OK;
+  k_read_particles<MPM_SNOW><<<sim->grid_g2p, 64, 0, static_cast<hipStream_t>(stream)>>>(
+      sim->d, sim->cur, nullptr, nullptr, nullptr, nullptr, alpha);
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 

@@ -441,17 +441,20 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
 #pragma unroll
       for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
       if (pending) update_F<MAT>(Fp, Cp, dt);
-      const float E = HAS_E ? at_byte(in.E, io) : s.E;
+      // the per-particle scalar: Young's modulus, or snow's log plastic volume
+      const float Es = HAS_E ? at_byte(in.E, io) : s.E;
+      const float E = MAT == MPM_SNOW ? s.E : Es;
+      float ap = Es;
       float A[9];
       uint32_t st = 0;
-      // sand: the plasticity projection of the updated F, with the stress
-      if (MAT == MPM_SAND) st = sand_affine(s, Fp, E, Cp, A, pending);
+      // sand, snow: the plasticity projection of the updated F, with the stress
+      if (MAT == MPM_SAND || MAT == MPM_SNOW) st = plastic_affine<MAT>(s, Fp, E, ap, Cp, A, pending);
       if (valid) {
 #pragma unroll
         for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
-        if (HAS_E) stream_store(E, at_byte(out.E, od));
+        if (HAS_E) stream_store(MAT == MPM_SNOW ? ap : E, at_byte(out.E, od));
       }
-      if (MAT != MPM_SAND) st = affine_momentum<MAT>(s, Fp, E, Cp, A);
+      if (MAT != MPM_SAND && MAT != MPM_SNOW) st = affine_momentum<MAT>(s, Fp, E, Cp, A);
       if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
       int b[3];
       float f[3], w[3][3], q0[3], Ad[9];

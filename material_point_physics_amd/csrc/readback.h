@@ -2,13 +2,16 @@
 // Part of mpm.hip: included there, inside its anonymous namespace, after the
 // parts before it; not a standalone header.
 
-// Readback: unpermute to creation order, apply the pending F (or J) update.
+// Readback: unpermute to creation order, apply the pending F (or J) update
+// (and for sand and snow the projection that follows it; alpha: snow's log
+// plastic volume after that projection, or NULL).
 // Single-wavefront workgroups walk the chunk list of layout cur (the slots
 // between bins are padding).  After a fused G2P2G pass the state is in the
 // same slots of the other buffer, with F current.
 template <int MAT>
 __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float *__restrict__ x, float *__restrict__ v,
-                                                       float *__restrict__ C, float *__restrict__ F) {
+                                                       float *__restrict__ C, float *__restrict__ F,
+                                                       float *__restrict__ alpha) {
   const bool fused = s.ctr[CTR_LOOK + cur] != 0u;
   const PBuf b = s.buf[fused ? cur ^ 1 : cur];
   const size_t Np = (size_t)s.Np;
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float 
       }
       if (C)
         for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
-      if (!F) continue;
+      if (!F && !alpha) continue;
       if (MAT == MPM_J_FLUID) {
         float J = b.F[slot];
         if (pending) {
@@ -43,14 +46,17 @@ __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float 
       } else {
         float Fp[9];
         for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
+        float ap = MAT == MPM_SNOW ? b.E[slot] : 0.f;
         if (pending) {
           update_F<MPM_FIXED_COROTATED>(Fp, Cp, dt);
-          if (MAT == MPM_SAND) {  // and the plasticity projection that follows the update
+          if (MAT == MPM_SAND || MAT == MPM_SNOW) {  // and the plasticity projection that follows the update
             float A[9];
-            (void)sand_affine(s, Fp, s.E, Cp, A, true);
+            (void)plastic_affine<MAT>(s, Fp, s.E, ap, Cp, A, true);
           }
         }
-        for (int k = 0; k < 9; ++k) F[9 * id + k] = Fp[k];
+        if (F)
+          for (int k = 0; k < 9; ++k) F[9 * id + k] = Fp[k];
+        if (MAT == MPM_SNOW && alpha) alpha[id] = ap;
       }
     }
   }

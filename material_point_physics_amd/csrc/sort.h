@@ -31,7 +31,7 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
     } else {
       for (int k = 0; k < 9; ++k) b.F[k * Np + i] = F0 ? F0[9 * (size_t)i + k] : ((k % 4 == 0) ? 1.f : 0.f);
     }
-    if (s.has_E) b.E[i] = E_p[i];
+    if (s.has_E) b.E[i] = E_p ? E_p[i] : s.snow_a0;  // snow: the slot holds the log plastic volume
     b.id[i] = i;
     key = bin_key(s, base[0], base[1], base[2]);
   }

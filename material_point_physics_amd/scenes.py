@@ -250,6 +250,32 @@ def sand_3m(seed: int = 6) -> Scene:
                  p_vol=dx ** 3 / 8, steps=100, friction_deg=30.0)
 
 
+def snow_1m(seed: int = 7) -> Scene:
+    """1,310,720 particles of snow falling onto the floor, 128^3 grid.
+
+    Stands in for the page's snow scene (1.33M particles of non-associative
+    Cam-clay snow with bulk modulus 5e5, Poisson ratio 0.3, M = 0.8,
+    beta = 0.9, xi = 5; its animated crawling-figure boundary is not
+    available): a block of 64 x 40 x 64 cells (x and z cells [32,96), y cells
+    [3,43), so the bottom layer's stencils reach the sticky floor), 8
+    particles per cell, moving down at 2 m/s.  E = 3 K (1 - 2 nu) = 6e5 gives
+    the page's bulk modulus; density 400 (fresh snow; the page gives none);
+    initial log plastic volume -0.01 (the page gives none).
+    """
+    n = 128
+    dx = 1.0 / n
+    rng = np.random.default_rng(seed)
+    x = _stratified(rng, _box_cells((32, 3, 32), (96, 43, 96)), 8, dx)
+    v = np.zeros_like(x)
+    v[:, 1] = -2.0
+    return Scene("snow_1m", "snow block falling onto the floor, 1310720 particles, 128^3 grid",
+                 x.astype(np.float32), v.astype(np.float32), None,
+                 n=n, dt=2e-5, gravity=(0.0, -9.8, 0.0), wall=3,
+                 material=SNOW, E=6e5, nu=0.3, rho=400.0,
+                 p_vol=dx ** 3 / 8, steps=100, snow_M=0.8, snow_beta=0.9, snow_xi=5.0,
+                 snow_alpha0=-0.01)
+
+
 SCENES = {
     "cube_8k": cube_8k,
     "jelly3_55k": jelly3_55k,
@@ -258,6 +284,7 @@ SCENES = {
     "slab_12m_shard8": slab_12m_shard8,
     "dambreak_4m": dambreak_4m,
     "sand_3m": sand_3m,
+    "snow_1m": snow_1m,
 }
 
 

@@ -35,6 +35,8 @@ def gpu_run(scene, steps: int, read=("particles", "grid"), sort_policy=None, fus
         if "particles" in read:
             x, v, C, F = sim.read_particles()
             out.update(x=x.cpu().numpy(), v=v.cpu().numpy(), C=C.cpu().numpy(), F=F.cpu().numpy())
+        if "particles" in read and scene.material == scenes.SNOW:
+            out["alpha"] = sim.read_plastic_state().cpu().numpy()
         if "grid" in read:
             m, p = sim.read_grid()
             out.update(m=m.cpu().numpy(), p=p.cpu().numpy())

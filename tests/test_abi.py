@@ -55,6 +55,13 @@ def test_workspace_bytes_scales_and_rejects_bad_params():
                 dict(material=7), dict(E=-1.0), dict(nu=0.5), dict(rho=0.0), dict(p_vol=0.0),
                 dict(gravity=(0, float("inf"), 0))]:
         assert mpm.mpm_workspace_bytes(good_params(**bad), 1000) == 0, bad
+    # snow: a positive modulus and M, non-negative beta and xi, a finite initial log plastic volume
+    assert mpm.mpm_workspace_bytes(good_params(material=3), 1000) > 0
+    assert mpm.mpm_workspace_bytes(good_params(material=3, snow_beta=0.0, snow_xi=0.0, snow_alpha0=0.3), 1000) > 0
+    for bad in [dict(E=0.0), dict(snow_M=0.0), dict(snow_M=float("inf")), dict(snow_beta=-0.1),
+                dict(snow_xi=-1.0), dict(snow_xi=float("nan")), dict(snow_alpha0=float("inf"))]:
+        assert mpm.mpm_workspace_bytes(good_params(material=3, **bad), 1000) == 0, bad
+    assert mpm.mpm_workspace_bytes(good_params(material=0, E=0.0, snow_M=0.0), 1000) > 0  # read only for snow
     assert mpm.mpm_workspace_bytes(good_params(), -1) == 0
     assert mpm.mpm_workspace_bytes(good_params(), 1 << 31) == 0
     assert mpm.mpm_workspace_bytes(good_params(), 1 << 28) == 0  # 32-bit element offsets
