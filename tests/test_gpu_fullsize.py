@@ -8,6 +8,8 @@ nodes within 2 cells, hence on particles within 4 cells.  The oracle steps the
 neighbourhood subset (all particles within 4 cells of the sampled particles)
 on the full grid, which makes those sampled values exact.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -61,16 +63,23 @@ def test_full_size_sampled_parity(name):
     assert gpu["status"][0] == 0
 
 
-@pytest.mark.parametrize("mode", ["separate", "fused_device", "fused_scheduled"])
+@pytest.mark.parametrize("mode", ["separate", "fused_device", "fused_scheduled", "snow_separate",
+                                  "snow_fused_scheduled"])
 def test_conservation_100_steps(mode):
     """Colliding blocks with gravity off and no wall contact: grid mass equals
     particle mass and total momentum is unchanged, within 1e-6 relative
     (momentum normalised by sum m|v|, since the blocks' momenta cancel).  Also
     with fused steps, sorts decided on the device (every 5 steps) or
     scheduled by the host (every 4): 100 steps of lookahead passes, movers
-    and re-sorts as the blocks collide."""
+    and re-sorts as the blocks collide.  The snow cases make the blocks
+    Cam-clay snow with little initial hardening (log plastic volume -0.001),
+    so the collision compacts them past the compression tip: the plasticity
+    projection changes F only, and the totals still hold."""
     sc = scenes.blocks_1m(gravity=False)
-    pu.log(f"conservation over 100 steps, {mode}")
+    if mode.startswith("snow"):
+        sc = dataclasses.replace(sc, material=scenes.SNOW, snow_alpha0=-0.001)
+        mode = mode[len("snow_"):]
+    pu.log(f"conservation over 100 steps, {sc.material} {mode}")
     sim = mpm.Simulation(sc)
     try:
         if mode != "separate":
@@ -92,6 +101,10 @@ def test_conservation_100_steps(mode):
             assert np.abs(P - P0).max() / scale < 1e-6
         st = sim.status()
         assert st[0] == 0, st
+        if sc.material == scenes.SNOW:
+            a = sim.read_plastic_state().cpu().numpy()
+            pu.log(f"log plastic volume after 100 steps: [{a.min():.4f}, {a.max():.4f}]")
+            assert a.min() < -0.001  # compacted and hardened where the blocks met
     finally:
         sim.close()
 
