@@ -433,7 +433,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, sim->device) != hipSuccess || cus <= 0)
       cus = 256;
     sim->grid_particles = (int)(((d.N + WG - 1) / WG + 7) / 8 * 8);
-    // (occupancy of the instance this material launches: snow's needs 130 VGPRs)
+    // (occupancy of the instance this material launches)
     int occ = 0;
     const void *pk = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true>
                                             : (const void *)k_p2g<MPM_FIXED_COROTATED, false>;
