@@ -70,9 +70,10 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
         # the new order; accumulator write per active node, and the clear of
         # the previous step's accumulator (one float4 per active node)
         "k_p2g": N * (4 + 1 + 12 + 12 + 36 + f + e + 4 + f + e + 12 + 4) + 32 * active_nodes,
-        # reads x; writes x, v, C, key; reads the accumulator (m, p) once per
-        # active node and applies the grid update to it
-        "k_g2p": N * (12 + 12 + 12 + 36 + 4) + 16 * active_nodes,
+        # reads x; writes v, C, key (the new x is formed again by the next
+        # P2G from x and v); reads the accumulator (m, p) once per active node
+        # and applies the grid update to it
+        "k_g2p": N * (12 + 12 + 36 + 4) + 16 * active_nodes,
     }
 
 

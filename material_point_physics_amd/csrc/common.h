@@ -97,6 +97,14 @@ struct SimDev {
   uint32_t *status;
 };
 
+// x + dt v, clamped into [lo, hi]: G2P's new position.  G2P does not store
+// it; the next P2G and the readback form it again from the stored x and v,
+// with this one expression (an explicit fused multiply-add), so every side
+// gets the same bits.
+__device__ __forceinline__ float advanced(const SimDev &s, float x, float v) {
+  return fminf(fmaxf(fmaf(s.dt, v, x), s.lo), s.hi);
+}
+
 // ------------------------------------------------------------ device utils
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

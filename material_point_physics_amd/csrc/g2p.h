@@ -176,10 +176,10 @@ __device__ __forceinline__ void advect(const SimDev &s, const float xp[3], const
                                        float xn[3], float C[9], bool &clamped, bool &nonfinite) {
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
-    float xa = xp[k] + s.dt * v[k];
+    const float xa = fmaf(s.dt, v[k], xp[k]);
     if (!isfinite(xa) || !isfinite(v[k])) nonfinite = true;
     if (xa < s.lo || xa > s.hi) clamped = true;
-    xn[k] = fminf(fmaxf(xa, s.lo), s.hi);
+    xn[k] = advanced(s, xp[k], v[k]);
   }
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
@@ -189,7 +189,8 @@ __device__ __forceinline__ void advect(const SimDev &s, const float xp[3], const
 }
 
 // The G2P of the step that accumulated into a: particles of layout lay (the
-// one P2G built), x, v, C written in place, and the next step's bin keys and
+// one P2G built), v and C written in place (x stays: the next P2G advances
+// it with that v), and the next step's bin keys and
 // counts.
 template <int MAT>
 __device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4 *win) {
@@ -235,9 +236,10 @@ __device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4
         bool clamped = false, nonfinite = false;
         advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
         int b[3];
+        // (the new position is not stored: the next P2G, or the readback,
+        // forms it again from x and the v stored here, bit for bit)
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-          stream_store(xn[k], at_byte(out.x + k * Np, so));
           stream_store(v[k], at_byte(out.v + k * Np, so));
           b[k] = base_node(xn[k] * fn);
         }

@@ -27,7 +27,9 @@
 //   k_g2p         one wavefront per chunk: the grid update (v = p/m + dt g,
 //                 sticky walls) of the bin's 6^3-node window, staged in LDS;
 //                 gather, APIC C, advection + clamp in the storage order P2G
-//                 chose; the next step's bin keys/counts
+//                 chose; the next step's bin keys/counts (v and C are stored;
+//                 the advected x is not: the next P2G forms it again from x
+//                 and v, bit for bit)
 //
 // Between sorts (mpm_set_sort_policy), k_g2p2g can replace k_g2p: the G2P of
 // the step and the P2G of the next in one pass (mpm_set_fused_steps).

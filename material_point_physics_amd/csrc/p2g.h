@@ -418,8 +418,8 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       // The new state is stored in this processing order, (bin, super-rank,
       // window, cell): the next step's gathers then run over nearly
       // consecutive addresses.  P2G writes x and id there; G2P reads x from
-      // the same slot, without an index indirection, and overwrites it with
-      // the advected position.
+      // the same slot, without an index indirection, and leaves it: the
+      // position it advects to is formed again here from x and its v.
       const uint32_t dst = start + at;
       const uint32_t io = 4u * i, od = 4u * dst;  // byte offsets of the source and destination slots
       float xp[3], vp[3], Cp[9];
@@ -430,6 +430,10 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       }
 #pragma unroll
       for (int k = 0; k < 9; ++k) Cp[k] = stream_load(at_byte(in.C + k * Np, io));
+      // the pending advection of the G2P before (the same bits as its keys)
+      if (pending)
+#pragma unroll
+        for (int a = 0; a < 3; ++a) xp[a] = advanced(s, xp[a], vp[a]);
       if (valid) {
 #pragma unroll
         for (int a = 0; a < 3; ++a) at_byte(out.x + a * Np, od) = xp[a];

@@ -2,7 +2,7 @@
 // Part of mpm.hip: included there, inside its anonymous namespace, after the
 // parts before it; not a standalone header.
 
-// Readback: unpermute to creation order, apply the pending F (or J) update
+// Readback: unpermute to creation order, apply the pending advection and F (or J) update
 // (and for sand and snow the projection that follows it; alpha: snow's log
 // plastic volume after that projection, or NULL).
 // Single-wavefront workgroups walk the chunk list of layout cur (the slots
@@ -29,8 +29,9 @@ __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float 
 #pragma unroll
       for (int k = 0; k < 9; ++k) Cp[k] = b.C[k * Np + slot];
       for (int a = 0; a < 3; ++a) {
-        if (x) x[3 * id + a] = b.x[a * Np + slot];
-        if (v) v[3 * id + a] = b.v[a * Np + slot];
+        const float xa = b.x[a * Np + slot], va = b.v[a * Np + slot];
+        if (x) x[3 * id + a] = pending ? advanced(s, xa, va) : xa;
+        if (v) v[3 * id + a] = va;
       }
       if (C)
         for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
