@@ -43,8 +43,8 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
     sorted_steps=False (free-zone steps without a sort) the scatter moves
     nothing and P2G reads the key word (4 B) instead of perm and the cell
     byte (5 B).  With fused=True (fused steps without a sort) the separate
-    P2G moves nothing and the G2P2G kernel reads x, F, E, id and writes them
-    back, plus v and C (stored on the last step of each launch, and on every
+    P2G moves nothing and the G2P2G kernel reads x, F, E and writes x and F
+    back (ids and moduli stay at their slots between sorts), plus v and C (stored on the last step of each launch, and on every
     profiled step), and per active node reads the window once, writes the
     next accumulator and clears the one of two steps before."""
     f = 4 if material == 1 else 36  # fluid J, else F (elastic, sand, snow)
@@ -52,7 +52,9 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
     if fused:
         kb = kernel_bytes(N, active_nodes, nbins, material, has_E, sorted_steps=False)
         kb["k_p2g"] = 0
-        kb["k_g2p2g"] = N * 2 * (12 + f + e + 4) + N * (12 + 36) + 48 * active_nodes
+        # x, F (and E) read; x and F written (snow also its log plastic volume);
+        # the ids and moduli stay in place between sorts
+        kb["k_g2p2g"] = N * (12 + f + e) + N * (12 + f + (e if material == 3 else 0)) + N * (12 + 36) + 48 * active_nodes
         del kb["k_g2p"]
         return kb
     if not sorted_steps:

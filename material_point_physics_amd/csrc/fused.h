@@ -25,7 +25,8 @@ struct FusedShared {
 // window and pass follow from its occurrence index among the lanes of its
 // round in the same cell.
 template <int MAT, bool HAS_E>
-__device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool write_vc, FusedShared &sm) {
+__device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool write_vc, bool copy_ids,
+                                           FusedShared &sm) {
   const int lay = src ^ 1;
   const PBuf in = s.buf[lay], out = s.buf[src];
   const int a1 = (a + 1) & (NACC - 1);
@@ -65,7 +66,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
 #pragma unroll
       for (int k = 0; k < FW; ++k) Fq[k] = stream_load(at_byte(in.F + k * Np, sn));
       if (HAS_E) Eq = stream_load(at_byte(in.E, sn));
-      idq = stream_load(at_byte(in.id, sn));
+      idq = copy_ids ? stream_load(at_byte(in.id, sn)) : 0u;
     }
     for (int k = lane; k < NWIN * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     store_window(s, acc, wpack, ox0, oy0, oz0, sm.vel);
@@ -80,7 +81,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       for (int k = 0; k < FW; ++k) Fp[k] = Fq[k];
       const float E = MAT == MPM_SNOW ? s.E : Eq;  // snow: the slot holds the log plastic volume
       float ap = Eq;
-      if (valid) stream_store(idq, at_byte(out.id, so));
+      if (valid && copy_ids) stream_store(idq, at_byte(out.id, so));
       if (r0 + 64u < count) {
         const bool vn = r0 + 64u + (uint32_t)lane < count;
         const uint32_t sn = 4u * (start + (vn ? r0 + 64u + (uint32_t)lane : 0u));
@@ -89,7 +90,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
 #pragma unroll
         for (int k = 0; k < FW; ++k) Fq[k] = stream_load(at_byte(in.F + k * Np, sn));
         if (HAS_E) Eq = stream_load(at_byte(in.E, sn));
-        idq = stream_load(at_byte(in.id, sn));
+        if (copy_ids) idq = stream_load(at_byte(in.id, sn));
       }
       float v[3], B[9], xn[3], Cn[9];
       gather_particle(s, sm.vel, a, xp, ox0, oy0, oz0, v, B);
@@ -105,7 +106,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
         for (int k = 0; k < 3; ++k) at_byte(out.x + k * Np, so) = xn[k];
 #pragma unroll
         for (int k = 0; k < FW; ++k) stream_store(Fp[k], at_byte(out.F + k * Np, so));
-        if (HAS_E) stream_store(MAT == MPM_SNOW ? ap : E, at_byte(out.E, so));
+        if (HAS_E && (copy_ids || MAT == MPM_SNOW)) stream_store(MAT == MPM_SNOW ? ap : E, at_byte(out.E, so));
         if (write_vc) {
 #pragma unroll
           for (int k = 0; k < 3; ++k) stream_store(v[k], at_byte(out.v + k * Np, so));
@@ -165,15 +166,19 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
 // Step n reads buffer src and accumulated into a; write_vc: store v and C
 // (the last step of a launch, so that the state can be read back); sched:
 // whether the next step sorts, 0 or 1 when the host schedules the sorts
-// (a fixed interval), -1 to decide here by the policy.  Leaves the next
-// step's sort decision and whether its P2G is done.
+// (a fixed interval), -1 to decide here by the policy; copy_ids: copy the
+// ids and the per-particle modulus to the output buffer (0 only when the
+// host knows that both buffers already hold them at these slots: a fused
+// pass after the first one since a sort, which copied them; snow's log
+// plastic volume changes and is always written).  Leaves the next step's
+// sort decision and whether its P2G is done.
 template <int MAT, bool HAS_E>
-__global__ __launch_bounds__(64) void k_g2p2g(SimDev s, int src, int a, int write_vc, int sched) {
+__global__ __launch_bounds__(64) void k_g2p2g(SimDev s, int src, int a, int write_vc, int sched, int copy_ids) {
   __shared__ FusedShared sm;
   // uniform: the words sort_next_step reads do not change in this kernel
   const bool next_sort = sched < 0 ? sort_next_step(s) : sched != 0;
   if (next_sort) g2p_step<MAT>(s, src ^ 1, a, sm.vel);
-  else fused_step<MAT, HAS_E>(s, src, a, write_vc != 0, sm);
+  else fused_step<MAT, HAS_E>(s, src, a, write_vc != 0, copy_ids != 0, sm);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     // F in layout src ^ 1 is one update behind after the plain G2P; after the
     // fused pass the state of the next step's P2G is in buffer src, current.

@@ -273,7 +273,8 @@ int mode_period(const mpm_sim *sim, int mode) {
 // accumulates into p); fused: the plain G2P is replaced by the G2P2G kernel,
 // which stores v and C when write_vc is set and takes the next step's sort
 // decision from sched (-1: by the policy, on the device).
-int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool write_vc, int sched) {
+int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool write_vc, int sched,
+                  int copy_ids = 1) {
   const int src = (p + 1) & 1;
   const SimDev &d = sim->d;
   switch (k) {
@@ -307,16 +308,16 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
         const int wv = write_vc ? 1 : 0;
         const int g = sim->grid_g2p2g;
         if (d.material == MPM_J_FLUID) {
-          if (d.has_E) k_g2p2g<MPM_J_FLUID, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
-          else k_g2p2g<MPM_J_FLUID, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          if (d.has_E) k_g2p2g<MPM_J_FLUID, true><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
+          else k_g2p2g<MPM_J_FLUID, false><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
         } else if (d.material == MPM_SAND) {
-          if (d.has_E) k_g2p2g<MPM_SAND, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
-          else k_g2p2g<MPM_SAND, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          if (d.has_E) k_g2p2g<MPM_SAND, true><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
+          else k_g2p2g<MPM_SAND, false><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
         } else if (d.material == MPM_SNOW) {
-          k_g2p2g<MPM_SNOW, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          k_g2p2g<MPM_SNOW, true><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
         } else {
-          if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv, sched);
-          else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv, sched);
+          if (d.has_E) k_g2p2g<MPM_FIXED_COROTATED, true><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
+          else k_g2p2g<MPM_FIXED_COROTATED, false><<<g, 64, 0, st>>>(d, src, p, wv, sched, copy_ids);
         }
       } else {
         // (the gather does not depend on the material: sand and snow use the elastic instance)
@@ -329,27 +330,35 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
 }
 
 // Which kernels step n runs in a mode: all five, or (mode 2, a step after a
-// fused pass) the fused kernel alone; and the fused kernel's sched argument.
-// lean_ok = false forces all five (the first step under a new schedule,
-// whose P2G may not have run).
-void step_plan(const mpm_sim *sim, int64_t n, int mode, bool lean_ok, bool run[NUM_KERNELS], int &sched) {
+// fused pass) the fused kernel alone; and the fused kernel's sched and
+// copy_ids arguments.  lean_ok = false forces all five (the first step
+// under a new schedule, whose P2G may not have run).  A lean step's fused
+// pass follows a fused pass (of the full step that sorted, or of the first
+// step under the schedule) that copied the ids and moduli into the other
+// buffer at the same slots, and no sort has moved them since: it leaves
+// them in place.
+void step_plan(const mpm_sim *sim, int64_t n, int mode, bool lean_ok, bool run[NUM_KERNELS], int &sched,
+               int &copy_ids) {
   for (int k = 0; k < NUM_KERNELS; ++k) run[k] = true;
   sched = -1;
+  copy_ids = 1;
   if (mode == 2) {
     const int K = sim->sort_interval, c = (int)(n % K);
     sched = (c == K - 1) ? 1 : 0;
-    if (c != 0 && lean_ok)
+    if (c != 0 && lean_ok) {
       for (int k = 0; k < NUM_KERNELS - 1; ++k) run[k] = false;
+      copy_ids = 0;
+    }
   }
 }
 
 int enqueue_step(mpm_sim *sim, hipStream_t st, int64_t n, int mode, bool lean_ok, bool write_vc) {
   bool run[NUM_KERNELS];
-  int sched;
-  step_plan(sim, n, mode, lean_ok, run, sched);
+  int sched, copy_ids;
+  step_plan(sim, n, mode, lean_ok, run, sched, copy_ids);
   for (int k = 0; k < NUM_KERNELS; ++k) {
     if (!run[k]) continue;
-    const int rc = launch_kernel(sim, k, st, (int)(n % NACC), mode != 0, write_vc, sched);
+    const int rc = launch_kernel(sim, k, st, (int)(n % NACC), mode != 0, write_vc, sched, copy_ids);
     if (rc) return rc;
   }
   return MPM_OK;
@@ -591,11 +600,11 @@ int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel
   for (int32_t s = 0; s < n_steps && rc == MPM_OK; ++s) {
     // the same kernels as the graphs (a kernel a step does not run takes no time)
     bool run[NUM_KERNELS];
-    int sched;
-    step_plan(sim, sim->steps, mode, mode == 2 && sim->sched_ready, run, sched);
+    int sched, copy_ids;
+    step_plan(sim, sim->steps, mode, mode == 2 && sim->sched_ready, run, sched, copy_ids);
     if (hipEventRecord(ev[0], st) != hipSuccess) { rc = MPM_ERR_HIP; break; }
     for (int k = 0; k < NUM_KERNELS && rc == MPM_OK; ++k) {
-      if (run[k]) rc = launch_kernel(sim, k, st, (int)(sim->steps % NACC), mode != 0, true, sched);
+      if (run[k]) rc = launch_kernel(sim, k, st, (int)(sim->steps % NACC), mode != 0, true, sched, copy_ids);
       if (rc == MPM_OK && hipEventRecord(ev[k + 1], st) != hipSuccess) rc = MPM_ERR_HIP;
     }
     if (rc != MPM_OK) break;
