@@ -288,6 +288,47 @@ SCENES = {
 }
 
 
+def clamp_scene(seed: int = 17, n: int = 32, dt: float = 1e-3, per_cluster: int = 300) -> Scene:
+    """Four clusters of particles on a grid without walls and without gravity,
+    each cluster moving at one uniform velocity (so that the grid reproduces
+    it exactly), for tests of the position clamp to [2dx, (n-2)dx].
+
+    Cluster 0 lies against the low x clamp plane (x in [2dx, 2.4dx]) and
+    moves -x by 0.6 dx per step; cluster 1 lies against the high y plane and
+    moves +y by 0.6 dx per step (and +x by 0.1 dx); cluster 2 lies in the
+    corner at low x, low y and high z and moves out through all three planes;
+    cluster 3 is interior and never reaches a plane.  The clusters are more
+    than 3 cells apart, so they share no grid node.  extra["cluster"] holds
+    each particle's cluster and extra["clamped_per_step"] the number of
+    position components that leave the box in each step (clusters 0 and 1:
+    one per particle, cluster 2: three, cluster 3: none).
+    """
+    rng = np.random.default_rng(seed)
+    dx = 1.0 / n
+    lo_p, hi_p = 2 * dx, (n - 2) * dx
+    u = 0.6 * dx / dt
+    boxes = [
+        ((lo_p, 0.35, 0.35), (lo_p + 0.4 * dx, 0.5, 0.5), (-u, 0.0, 0.0)),
+        ((0.55, hi_p - 0.4 * dx, 0.55), (0.7, hi_p, 0.7), (u / 6, u, 0.0)),
+        ((lo_p, lo_p, hi_p - 0.4 * dx), (lo_p + 0.4 * dx, lo_p + 0.4 * dx, hi_p), (-u, -u, u)),
+        ((0.4, 0.4, 0.45), (0.55, 0.55, 0.6), (0.3 * u, -0.2 * u, 0.1 * u)),
+    ]
+    xs, vs, cl = [], [], []
+    for k, (lo, hi, vel) in enumerate(boxes):
+        lo, hi = np.asarray(lo), np.asarray(hi)
+        xs.append(lo + (hi - lo) * rng.random((per_cluster, 3)))
+        vs.append(np.tile(np.asarray(vel, np.float64), (per_cluster, 1)))
+        cl.append(np.full(per_cluster, k, np.int32))
+    x = np.concatenate(xs)
+    v = np.concatenate(vs)
+    return Scene("clamp_faces", "four clusters leaving the clamp box through its faces",
+                 x.astype(np.float32), v.astype(np.float32), None,
+                 n=n, dt=dt, gravity=(0.0, 0.0, 0.0), wall=0,
+                 material=FIXED_COROTATED, E=100.0, nu=0.3, rho=1.0,
+                 p_vol=dx ** 3 / 4, steps=3,
+                 extra={"cluster": np.concatenate(cl), "clamped_per_step": 5 * per_cluster})
+
+
 def random_rotation(rng, m: int) -> np.ndarray:
     """m uniformly random rotations (QR of Gaussian matrices, det fixed to +1)."""
     a = rng.normal(size=(m, 3, 3))

@@ -52,6 +52,12 @@ MUTANTS = [
     ("G2P advects with pre-gravity velocity", "real xa = x[3 * p + a] + dt * vn[a];",
      "real xa = x[3 * p + a] + dt * (vn[a] - dt * (real)P->gravity[a]);"),
     ("G2P velocity of neighbour axis", "vn[a] += wt * vi[a];", "vn[a] += wt * vi[(a + 1) % 3];"),
+    ("G2P without the position clamp", "if (xa < lo) { xa = lo; ++clamped; }\n      if (xa > hi) { xa = hi; ++clamped; }",
+     ""),
+    ("G2P clamp box [dx, (n-1)dx]", "const real lo = 2 * dx, hi = (real)(n - 2) * dx;",
+     "const real lo = dx, hi = (real)(n - 1) * dx;"),
+    ("G2P clamp counts the x component only", "if (xa < lo) { xa = lo; ++clamped; }\n      if (xa > hi) { xa = hi; ++clamped; }",
+     "if (xa < lo) { xa = lo; clamped += a == 0; }\n      if (xa > hi) { xa = hi; clamped += a == 0; }"),
     ("sand tip on compression", "  if (t > 0) {\n    kind = 1;", "  if (t < 0) {\n    kind = 1;"),
     ("sand cone factor doubled", "const real g = nd + (1 + nu) / (1 - 2 * nu) * t * alpha;",
      "const real g = nd + 2 * (1 + nu) / (1 - 2 * nu) * t * alpha;"),
@@ -100,6 +106,7 @@ def _all_pins():
         lambda o: pins.test_free_fall(),
         lambda o: pins.test_step_momentum_conservation(),
         lambda o: pins.test_walls_zero_velocity(),
+        lambda o: pins.test_position_clamp(),
         lambda o: pins.test_stress_force_is_energy_gradient(),
         lambda o: pins.test_fluid_J_matches_det_F(),
         pins.test_sand_alpha_is_the_mohr_coulomb_fit,

@@ -307,6 +307,42 @@ def test_walls_zero_velocity():
     assert np.all(sim.x >= 2.0 / n) and np.all(sim.x <= 1 - 2.0 / n)
 
 
+def test_position_clamp():
+    """Reading S15 (the page is silent): after advection each position
+    component is clamped to [2dx, (n-2)dx], and every clamped component is
+    counted.  Four clusters move at uniform velocities with walls and gravity
+    off, so G2P returns each cluster's velocity exactly (affine reproduction,
+    pinned above) and the new position is x + dt v before the clamp.  Three
+    clusters cross the clamp planes by 0.6 dx per step: their crossing
+    components must land exactly on the plane (not merely inside a wider box
+    such as [dx, (n-1)dx]), the others must be x + dt v, and the returned
+    count must be the number of crossing components, step after step."""
+    sc = scenes.clamp_scene()
+    sim = oracle.OracleSim(sc, "f64")
+    P = sc.params()
+    dt, n = P["dt"], sc.n
+    lo, hi = 2.0 / n, (n - 2.0) / n
+    v0 = sc.v.astype(np.float64)
+    cl = sc.extra["cluster"]
+    total = 0
+    for step in range(1, 4):
+        xp = sim.x.copy()
+        sim.step()
+        assert np.allclose(sim.v, v0, rtol=0, atol=1e-12 * np.abs(v0).max())
+        raw = xp + dt * v0
+        low, high = raw < lo, raw > hi
+        hits = int(low.sum() + high.sum())
+        assert hits == sc.extra["clamped_per_step"]
+        # the crossing components, by cluster: x of 0, y of 1, all three of 2, none of 3
+        assert np.all(low[cl == 0, 0]) and np.all(high[cl == 1, 1]) and np.all(low[cl == 2, :2])
+        assert np.all(high[cl == 2, 2]) and not low[cl == 3].any() and not high[cl == 3].any()
+        assert np.all(sim.x[low] == lo) and np.all(sim.x[high] == hi)
+        inside = ~(low | high)
+        assert np.allclose(sim.x[inside], raw[inside], rtol=0, atol=1e-14)
+        total += hits
+        assert sim.clamped == total
+
+
 def test_stress_force_is_energy_gradient():
     """Work conjugacy of the stress transfer: with v = 0 and C = 0, P2G leaves
     p_i = dt f_i with f_i = -dE/du_i, where E(u) = sum_p V0 Psi(F_p(u)) and
