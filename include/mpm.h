@@ -65,7 +65,7 @@ extern "C" {
 #define MPM_STATUS_INVERTED 0x4u   /* det F <= 0 (or J <= 0) met in the stress evaluation */
 #define MPM_STATUS_BAD_INPUT 0x8u  /* non-finite or out-of-domain input at creation (it was clamped) */
 #define MPM_STATUS_NO_CONVERGE 0x10u /* the polar iteration hit its iteration cap */
-#define MPM_STATUS_WORDS 8         /* [0] flags, [1] clamp count, [2] inverted count,
+#define MPM_STATUS_WORDS 8         /* [0] flags, [1] clamped position components, [2] inverted count,
                                       [3] non-finite count, [4..7] reserved (0) */
 
 typedef struct mpm_sim mpm_sim;
@@ -120,7 +120,11 @@ typedef struct {
 } mpm_params;
 
 /* Bytes of device workspace a simulation of n_particles needs (0 when the
- * parameters are invalid).  Pure host computation. */
+ * parameters are invalid).  Pure host computation.  The page's second
+ * single-GPU principle (reducing memory reallocation once the simulation
+ * starts; its Fig. 3 shows reallocation outlasting the kernels of a small
+ * scene): the whole need is known before the first step, so the caller hands
+ * the memory over once, at creation. */
 size_t mpm_workspace_bytes(const mpm_params *params, int64_t n_particles);
 
 /* Create a simulation and upload its initial state (the particle set of the
@@ -158,7 +162,12 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
 
 /* Advance n_steps >= 0 explicit steps, enqueued asynchronously on `stream`
  * (captured graphs of 8 steps, then single steps: per step key/bucket sort,
- * P2G, grid update, G2P).  No host synchronisation, no allocation. */
+ * P2G, grid update, G2P: the phases of the page's pipeline, with its
+ * principles of few kernels per step and no CPU-GPU synchronisation, Fig. 4).
+ * No host synchronisation, no allocation.  One
+ * exception: the first call after the fused host-scheduled interval changed
+ * (mpm_set_sort_policy with fused steps on) waits on the host for this
+ * handle's earlier work before it replaces the graphs of the old interval. */
 int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream);
 
 /* Sort policy: the free zone of the page's non-essential-phase discussion
@@ -197,7 +206,10 @@ int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget
 int mpm_set_fused_steps(mpm_sim *sim, int32_t enable);
 
 /* Copy the particle state after the last step, in creation order, into
- * caller-owned device arrays: x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)
+ * caller-owned device arrays (the Lagrangian half of the page's problem
+ * statement, its introduction: material points that the explicit steps carry
+ * across the background grid; asynchronous, as its CPU-GPU synchronisation
+ * principle asks, Fig. 4): x (N,3), v (N,3), C (N,3,3), F_or_J (N,3,3)
  * for the elastic material, sand and snow (for sand and snow the elastic part
  * after the step's plasticity projection) or (N) for the fluid.  Any output
  * may be NULL.  Asynchronous on `stream`. */
@@ -211,26 +223,38 @@ int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J
  * alpha or another material.  Asynchronous on `stream`. */
 int mpm_read_plastic_state(mpm_sim *sim, float *alpha, void *stream);
 
-/* Copy the grid state of the last step into caller-owned dense device arrays:
+/* Copy the grid state of the last step into caller-owned dense device arrays
+ * (the Eulerian half of the page's problem statement, its introduction, after
+ * the nodal computations of its multi-GPU reduction discussion: updating
+ * nodal velocities and resolving collisions):
  * mass (n^3) and momentum (n^3 x 3) = m_i * v_i after gravity and walls.
  * Nodes the last step did not touch are 0.  Either output may be NULL.
  * Before any step both are all zero.  Asynchronous on `stream`. */
 int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream);
 
 /* Copy the MPM_STATUS_WORDS uint32 status words (flags, counters since
- * creation) into a caller-owned device array.  Asynchronous on `stream`. */
+ * creation) into a caller-owned device array.  Asynchronous on `stream`.
+ * Anomalies are recorded on the device and read when the caller chooses,
+ * instead of being checked on the host inside a step: the page's CPU-GPU
+ * synchronisation principle (a host check stalls the GPU in a pipeline
+ * bubble, Fig. 4). */
 int mpm_status(mpm_sim *sim, uint32_t *status_device, void *stream);
 
-/* Steps taken since creation (host-side counter, no synchronisation). */
+/* Steps taken since creation: a host-side counter, so the caller learns it
+ * without reading anything back from the device (the page's CPU-GPU
+ * synchronisation principle, Fig. 4). */
 int64_t mpm_steps_taken(const mpm_sim *sim);
 
 /* Number of kernel slots of a step (scan tiles, scan bins, scatter, P2G, G2P;
  * with fused steps the last slot is the G2P2G kernel, and a step between
- * host-scheduled sorts launches that slot alone), and the name of slot k. */
+ * host-scheduled sorts launches that slot alone), and the name of slot k:
+ * the kernels the page's third single-GPU principle counts (minimising the
+ * kernels executed within one time step). */
 int32_t mpm_num_kernels(void);
 const char *mpm_kernel_name(int32_t k);
 
-/* Measurement helper: run n_steps steps eagerly (the same kernels and launch
+/* Measurement helper, for per-kernel time breakdowns like those of the page's
+ * ablation study (§6.2): run n_steps steps eagerly (the same kernels and launch
  * shapes as the graph), bracketing every kernel with HIP events on `stream`,
  * then synchronise `stream` and add each kernel's elapsed milliseconds into
  * kernel_ms[k] (host, mpm_num_kernels() entries, caller-initialised); a
@@ -238,11 +262,18 @@ const char *mpm_kernel_name(int32_t k);
  * stores v and C. */
 int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms);
 
-/* Release the handle and its graphs (not the caller's workspace).  Waits for
- * the handle's pending work on its private stream.  NULL is ignored. */
+/* Release the handle and its graphs (not the caller's workspace): memory is
+ * returned only when the simulation ends, never during it (the page's memory
+ * reallocation principle, Fig. 3).  Blocks the host until every operation
+ * this handle enqueued (steps, policy changes, readbacks, status copies) has
+ * completed on the device, whatever stream it was enqueued on, so the caller
+ * may free the workspace and the output arrays once this returns; the
+ * streams themselves need not exist any more.  NULL is ignored. */
 void mpm_destroy(mpm_sim *sim);
 
-/* Static description of a return code. */
+/* Static description of a return code.  Argument errors are found on the
+ * host before anything is enqueued, so reporting them needs no device round
+ * trip (the page's CPU-GPU synchronisation principle, Fig. 4). */
 const char *mpm_error_string(int code);
 
 #ifdef __cplusplus

@@ -215,7 +215,7 @@ __device__ __forceinline__ uint32_t wave_aggregated_increment(uint32_t *counters
   return slot;
 }
 
-__device__ __forceinline__ void flag_status(const SimDev &s, uint32_t bit, int counter_word) {
+__device__ __forceinline__ void flag_status(const SimDev &s, uint32_t bit, int counter_word, uint32_t amount = 1u) {
   atomicOr(&s.status[0], bit);
-  if (counter_word > 0) atomicAdd(&s.status[counter_word], 1u);
+  if (counter_word > 0) atomicAdd(&s.status[counter_word], amount);
 }

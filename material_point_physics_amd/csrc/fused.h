@@ -94,7 +94,8 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       }
       float v[3], B[9], xn[3], Cn[9];
       gather_particle(s, sm.vel, a, xp, ox0, oy0, oz0, v, B);
-      bool clamped = false, nonfinite = false;
+      uint32_t clamped = 0;
+      bool nonfinite = false;
       advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
       // P2G of step n + 1: F update with the new C, stress, deposit at xn
       update_F<MAT>(Fp, Cn, dt);
@@ -113,7 +114,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
 #pragma unroll
           for (int k = 0; k < 9; ++k) stream_store(Cn[k], at_byte(out.C + k * Np, so));
         }
-        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
+        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1, clamped);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
       if (MAT != MPM_SAND && MAT != MPM_SNOW) st = affine_momentum<MAT>(s, Fp, E, Cn, A);

@@ -170,15 +170,16 @@ __device__ __forceinline__ void gather_particle(const SimDev &s, const float4 *w
     for (int c2 = 0; c2 < 3; ++c2) B[k * 3 + c2] = fmaf(d[c2][0], v[k], B[k * 3 + c2]);  // d[c2][0] = -f_c2
 }
 
-// Advection x + dt v, clamped to the box; status bits for a clamp or a
-// non-finite value (of x, v or C = c_scale B, which the caller stores).
+// Advection x + dt v, clamped to the box; the number of clamped components
+// and whether a value (of x, v or C = c_scale B, which the caller stores) is
+// not finite.
 __device__ __forceinline__ void advect(const SimDev &s, const float xp[3], const float v[3], const float B[9],
-                                       float xn[3], float C[9], bool &clamped, bool &nonfinite) {
+                                       float xn[3], float C[9], uint32_t &clamped, bool &nonfinite) {
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const float xa = fmaf(s.dt, v[k], xp[k]);
     if (!isfinite(xa) || !isfinite(v[k])) nonfinite = true;
-    if (xa < s.lo || xa > s.hi) clamped = true;
+    if (xa < s.lo || xa > s.hi) ++clamped;
     xn[k] = advanced(s, xp[k], v[k]);
   }
 #pragma unroll
@@ -233,7 +234,8 @@ __device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4
       if (valid) {
         float v[3], B[9], xn[3], Cn[9];
         gather_particle(s, win, a, xp, ox0, oy0, oz0, v, B);
-        bool clamped = false, nonfinite = false;
+        uint32_t clamped = 0;
+        bool nonfinite = false;
         advect(s, xp, v, B, xn, Cn, clamped, nonfinite);
         int b[3];
         // (the new position is not stored: the next P2G, or the readback,
@@ -250,7 +252,7 @@ __device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4
         const bool same_bin = (b[0] >> 2) == (ox0 >> 2) && (b[1] >> 2) == (oy0 >> 2) && (b[2] >> 2) == (oz0 >> 2);
         key = (__ballot(!same_bin) == 0ull) ? bin : bin_key(s, b[0], b[1], b[2]);
         at_byte(s.key, so) = key | (cell_in_bin(b[0], b[1], b[2]) << KEY_CELL_SHIFT);
-        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1);
+        if (clamped) flag_status(s, MPM_STATUS_CLAMPED, 1, clamped);
         if (nonfinite) flag_status(s, MPM_STATUS_NONFINITE, 3);
       }
       wave_aggregated_increment(s.bin_count, key, valid);

@@ -239,6 +239,11 @@ struct mpm_sim {
   int sched_K = 0;                // K of the built mode-2 graphs
   bool sched_ready = false;       // the last step left the state the mode-2 schedule expects
   hipStream_t cap = nullptr;
+  // Recorded after every operation the handle enqueues, on the caller's
+  // stream: destroying graphs (or the handle) first waits for it, so no
+  // graph is destroyed while a launch of it is pending, and the caller may
+  // free the workspace once mpm_destroy returns.
+  hipEvent_t done = nullptr;
   hipGraph_t graph[3][2 * MAX_PERIOD] = {};
   hipGraphExec_t exec[3][2 * MAX_PERIOD] = {};
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
@@ -394,8 +399,17 @@ int build_graphs(mpm_sim *sim, int mode) {
   return MPM_OK;
 }
 
+// Record the handle's completion event after the work just enqueued on st.
+int mark(mpm_sim *sim, hipStream_t st) {
+  return hipEventRecord(sim->done, st) == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
 void release(mpm_sim *sim) {
   if (!sim) return;
+  if (sim->done) {
+    (void)hipEventSynchronize(sim->done);  // the last operation enqueued, on whatever stream
+    (void)hipEventDestroy(sim->done);
+  }
   for (int m = 0; m < 3; ++m) destroy_graphs(sim, m);
   if (sim->cap) {
     (void)hipStreamSynchronize(sim->cap);
@@ -488,6 +502,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
     // short dependent loads per chunk, so it wants many chunks in flight
     sim->grid_scatter = cus * 32;
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    if (hipEventCreateWithFlags(&sim->done, hipEventDisableTiming) != hipSuccess) { rc = MPM_ERR_HIP; break; }
 
     // Clear counters, flags, status and the P2G accumulator, then upload.
     k_zero_u32<<<1, WG, 0, st>>>(d.ctr, CTR_WORDS);
@@ -513,6 +528,7 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
       sim->cur = 1;
     }
     if (hipGetLastError() != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    if ((rc = mark(sim, st)) != MPM_OK) break;
     if (d.N > 0) rc = build_graphs(sim, 0);
   } while (0);
   if (rc != MPM_OK) {
@@ -531,6 +547,8 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
   }
   const int mode = step_mode(sim);
   if (mode == 2 && sim->sched_K != sim->sort_interval) {
+    // (a rare host wait: launches of the old graphs may still be pending)
+    if (hipEventSynchronize(sim->done) != hipSuccess) return MPM_ERR_HIP;
     destroy_graphs(sim, 2);
     sim->sched_K = 0;
   }
@@ -564,7 +582,7 @@ int mpm_step(mpm_sim *sim, int32_t n_steps, void *stream) {
     sim->cur ^= 1;
     sim->steps += 1;
   }
-  return MPM_OK;
+  return mark(sim, st);
 }
 
 int mpm_set_fused_steps(mpm_sim *sim, int32_t enable) {
@@ -582,7 +600,7 @@ int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget
   sim->sort_interval = max_interval;
   sim->mover_budget = mover_budget;
   sim->sched_ready = false;
-  return MPM_OK;
+  return mark(sim, static_cast<hipStream_t>(stream));
 }
 
 int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms) {
@@ -619,6 +637,7 @@ int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel
     sim->sched_ready = mode == 2;
   }
   for (int k = 0; k <= NUM_KERNELS; ++k) (void)hipEventDestroy(ev[k]);
+  if (rc == MPM_OK) rc = mark(sim, st);
   return rc;
 }
 
@@ -632,7 +651,7 @@ int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J
   else if (d.material == MPM_SAND) k_read_particles<MPM_SAND><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
   else if (d.material == MPM_SNOW) k_read_particles<MPM_SNOW><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
   else k_read_particles<MPM_FIXED_COROTATED><<<g, 64, 0, st>>>(d, sim->cur, x, v, C, F_or_J, nullptr);
-  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? mark(sim, st) : MPM_ERR_HIP;
 }
 
 int mpm_read_plastic_state(mpm_sim *sim, float *alpha, void *stream) {
@@ -640,7 +659,7 @@ int mpm_read_plastic_state(mpm_sim *sim, float *alpha, void *stream) {
   if (sim->d.N == 0) return MPM_OK;
   k_read_particles<MPM_SNOW><<<sim->grid_g2p, 64, 0, static_cast<hipStream_t>(stream)>>>(
       sim->d, sim->cur, nullptr, nullptr, nullptr, nullptr, alpha);
-  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? mark(sim, static_cast<hipStream_t>(stream)) : MPM_ERR_HIP;
 }
 
 int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream) {
@@ -653,7 +672,7 @@ int mpm_read_grid(mpm_sim *sim, float *mass, float *momentum, void *stream) {
   // the last step accumulated into its phase's accumulator
   if (sim->d.N > 0 && sim->steps > 0)
     k_read_grid<<<sim->grid_blocks, WG, 0, st>>>(sim->d, (int)((sim->steps - 1) % NACC), mass, momentum);
-  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? mark(sim, st) : MPM_ERR_HIP;
 }
 
 int mpm_status(mpm_sim *sim, uint32_t *status_device, void *stream) {
@@ -661,7 +680,7 @@ int mpm_status(mpm_sim *sim, uint32_t *status_device, void *stream) {
   if (hipMemcpyAsync(status_device, sim->d.status, sizeof(uint32_t) * MPM_STATUS_WORDS, hipMemcpyDeviceToDevice,
                      static_cast<hipStream_t>(stream)) != hipSuccess)
     return MPM_ERR_HIP;
-  return MPM_OK;
+  return mark(sim, static_cast<hipStream_t>(stream));
 }
 
 int64_t mpm_steps_taken(const mpm_sim *sim) { return sim ? sim->steps : -1; }

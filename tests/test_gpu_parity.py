@@ -246,3 +246,30 @@ def test_multiple_chunks_per_block():
     gpu = pu.gpu_run(sc, 2)
     orc, env = pu.envelope(sc, 2)
     assert_particle_parity(sc, gpu, orc, env)
+
+
+@pytest.mark.parametrize("mode", ["sorted", "free_zone", "fused_scheduled"])
+def test_position_clamp_matches_oracle(mode):
+    """Reading S15: positions are clamped to [2dx, (n-2)dx] after advection,
+    and status word 1 counts the clamped components.  Three clusters leave
+    the box through its faces (walls and gravity off) and are clamped in
+    every one of 5 steps; the fourth stays inside.  x, v, C, F and the clamp
+    count must match the oracle's, with the clamp taken by G2P (sorting every
+    step or under the free-zone policy) or by the fused G2P2G pass."""
+    sc = scenes.clamp_scene()
+    steps = 5
+    pu.log(f"position clamp, {mode}: N={sc.N} n={sc.n} steps={steps}")
+    policy = {"sorted": None, "free_zone": (4, 1 << 40), "fused_scheduled": (4, 1 << 40)}[mode]
+    gpu = pu.gpu_run(sc, steps, sort_policy=policy, fused=mode == "fused_scheduled")
+    orc, env = pu.envelope(sc, steps)
+    assert orc.clamped == steps * sc.extra["clamped_per_step"]
+    n = sc.n
+    lo, hi = np.float32(2.0 / n), np.float32((n - 2.0) / n)
+    cl = sc.extra["cluster"]
+    # the crossing components sit exactly on their planes
+    assert np.all(gpu["x"][cl == 0, 0] == lo) and np.all(gpu["x"][cl == 1, 1] == hi)
+    assert np.all(gpu["x"][cl == 2, :2] == lo) and np.all(gpu["x"][cl == 2, 2] == hi)
+    assert_particle_parity(sc, gpu, orc, env)
+    pu.log(f"clamp counts: gpu {gpu['status'][1]}, oracle {orc.clamped}")
+    assert gpu["status"][1] == orc.clamped
+    assert gpu["status"][0] == mpm.MPM_STATUS_CLAMPED
