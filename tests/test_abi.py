@@ -23,6 +23,41 @@ def test_header_declares_the_binding_exports():
     assert declared_functions() == sorted(mpm.EXPORTS)
 
 
+def declaration_comments():
+    """Each function declaration of the header with the comment block right
+    before it (a declaration may share the comment of the one before it
+    when they are adjacent, as mpm_num_kernels and mpm_kernel_name do)."""
+    text = open(HEADER).read()
+    out = {}
+    last_comment = ""
+    pos = 0
+    for m in re.finditer(r"/\*.*?\*/|\b(mpm_[a-z_]+)\s*\(", text, flags=re.S):
+        if m.group(0).startswith("/*"):
+            last_comment = m.group(0)
+            pos = m.end()
+            continue
+        name = m.group(1)
+        between = text[pos:m.start()]
+        # the comment belongs to this declaration if only code of the
+        # declarations since it lies in between
+        if ";" in between and not re.search(r"mpm_[a-z_]+\s*\(", between):
+            last_comment = ""
+        out.setdefault(name, last_comment)
+    return out
+
+
+def test_every_declaration_cites_the_page():
+    """Each entry point's comment names the passage of the MPM page it
+    follows (its problem statement, a single-GPU principle, a figure, the
+    free zone, the fused kernel, a scene or a section)."""
+    cites = declaration_comments()
+    assert set(cites) == set(declared_functions())
+    for name, comment in cites.items():
+        assert re.search(r"\bpage'?s?\b", comment), (name, comment[:120])
+        assert re.search(r"principle|problem statement|Fig\.|§|free zone|fused|scene|discussion|study",
+                         comment), (name, comment[:120])
+
+
 def test_library_exports_every_declared_symbol():
     L = mpm.lib()
     for name in declared_functions():

@@ -1,0 +1,139 @@
+"""Element-by-element GPU parity over every particle and every grid node,
+with the stress path active, at the headline sizes and on the chunk path of
+large scenes.
+
+* The 12M-particle slab and the 4M-particle dam break (the workloads the
+  benchmark times; the page's offline 12M-particle scene, introduction and
+  results), sorting every step as the benchmark does, two steps.  The first
+  step starts at rest with C = 0 and F = I (J = 1), so its stress vanishes;
+  the second step deposits the stress of the updated F.
+* A 1.1M-particle scene with random velocities, random C and stretched F
+  at about 16 particles per cell: at this size P2G takes chunks of 256
+  particles (four 64-lane sub-rounds), and most 4^3-cell bins hold four full
+  chunks, so the scatter's dense-bin block transpose runs.  Sorting every
+  step and with fused G2P2G steps.
+
+Tolerances (reading S13 and the fp32 envelope): the grid after each step,
+per field, max|gpu - oracle| / max|oracle| <= max(1e-5, 10x the fp32
+oracle's error on the same scene); every particle field, normalised by its
+scale, within 10x the fp32 oracle's error and never required below 2e-6.
+The fp64 and fp32 oracles run in two threads (the C oracle releases the
+interpreter lock).
+"""
+import threading
+
+import numpy as np
+import pytest
+
+import material_point_physics_amd as mpm
+import oracle
+from material_point_physics_amd import scenes
+import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_two_steps(sc, fused=False):
+    """Read particles and grid after step 1 and after step 2."""
+    sim = mpm.Simulation(sc)
+    out = []
+    try:
+        if fused:
+            sim.set_sort_policy(16, 1 << 40)
+            sim.set_fused_steps(True)
+        for _ in range(2):
+            sim.step(1)
+            x, v, C, F = sim.read_particles()
+            m, p = sim.read_grid()
+            out.append(dict(x=x.cpu().numpy(), v=v.cpu().numpy(), C=C.cpu().numpy(), F=F.cpu().numpy(),
+                            m=m.cpu().numpy(), p=p.cpu().numpy()))
+            del x, v, C, F, m, p
+        out.append(sim.status())
+    finally:
+        sim.close()
+    return out
+
+
+def oracle_two_steps(sc):
+    """fp64 and fp32 oracle snapshots after steps 1 and 2, run concurrently."""
+    res = {}
+
+    def run(prec):
+        o = oracle.OracleSim(sc, prec)
+        snaps = []
+        for _ in range(2):
+            o.step(1)
+            snaps.append(dict(x=o.x.copy(), v=o.v.copy(), C=o.C.copy(),
+                              F=(o.J.copy() if sc.material == scenes.J_FLUID else o.F.copy()),
+                              m=o.grid_mass().copy(), p=o.grid_momentum().copy(), n=o.n))
+        res[prec] = snaps
+
+    ts = [threading.Thread(target=run, args=(p,)) for p in ("f64", "f32")]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return res["f64"], res["f32"]
+
+
+def particle_errs(got, ref, n):
+    vmax = max(np.abs(ref["v"]).max(), 1e-30)
+    cs = 4 * n * vmax + np.abs(ref["C"]).max()
+    return dict(x=float(np.abs(got["x"] - ref["x"]).max()),
+                v=float(np.abs(got["v"] - ref["v"]).max() / vmax),
+                C=float(np.abs(got["C"] - ref["C"]).max() / cs),
+                F=float(np.abs(got["F"] - ref["F"]).max()))
+
+
+def check_two_steps(sc, gpu, o64, o32):
+    for k in range(2):
+        g, r, r32 = gpu[k], o64[k], o32[k]
+        for fld in ("m", "p"):
+            e = pu.field_maxrel(g[fld], r[fld])
+            e32 = pu.field_maxrel(r32[fld], r[fld])
+            pu.log(f"{sc.name} step {k + 1} grid {fld}: {e:.3e} (fp32 oracle {e32:.3e})")
+            assert e <= max(1e-5, 10 * e32), (k, fld, e, e32)
+        err = particle_errs(g, r, sc.n)
+        env = particle_errs(r32, r, sc.n)
+        pu.log(f"{sc.name} step {k + 1} particles: {err} (fp32 oracle {env})")
+        for f in err:
+            assert err[f] <= max(10 * env[f], 2e-6), (k, f, err[f], env[f])
+    status = gpu[2]
+    assert status[0] == 0, status
+
+
+@pytest.mark.parametrize("name", ["slab_12m", "dambreak_4m"])
+def test_headline_full_field_two_steps(name):
+    sc = scenes.SCENES[name]()
+    pu.log(f"full field {name}: N={sc.N} n={sc.n}, two steps sorting every step")
+    gpu = gpu_two_steps(sc)
+    pu.log("oracles (fp64, fp32) on the whole scene")
+    o64, o32 = oracle_two_steps(sc)
+    check_two_steps(sc, gpu, o64, o32)
+
+
+def chunk256_scene():
+    """1.1M particles at about 16 per cell in a 41^3-cell box of a 128^3
+    grid, with random velocities, C and stretched F."""
+    n = 128
+    lo, hi = 44.0 / n, 85.0 / n
+    sc = scenes.random_scene(1_100_000, n, 61, lo=[lo] * 3, hi=[hi] * 3, vscale=1.0, cscale=5.0,
+                             fstretch=0.1, dt=2e-5)
+    return sc
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["sorted", "fused"])
+def test_chunk256_full_field_two_steps(fused):
+    sc = chunk256_scene()
+    # 256-particle chunks: at least as many as the P2G launch has wavefronts
+    # (16 per CU on 256 CUs), and dense bins of four full chunks
+    assert sc.N >> 8 >= 16 * 256
+    b = np.floor(sc.x.astype(np.float64) * sc.n / 4).astype(np.int64)
+    per_bin = np.bincount((b[:, 2] * 32 + b[:, 1]) * 32 + b[:, 0])
+    pu.log(f"chunk path scene: N={sc.N}, bins with >= 4 full chunks: {(per_bin >= 1024).sum()}, "
+           f">= 2: {(per_bin >= 512).sum()} of {(per_bin > 0).sum()}")
+    # both block transposes of the scatter: bins of two or three full chunks and of four
+    assert (per_bin >= 1024).sum() >= 100 and ((per_bin >= 512) & (per_bin < 1024)).sum() >= 100
+    gpu = gpu_two_steps(sc, fused=fused)
+    o64, o32 = oracle_two_steps(sc)
+    check_two_steps(sc, gpu, o64, o32)
