@@ -51,6 +51,13 @@ extern "C" {
 #define MPM_ERR_WORKSPACE (-2)   /* workspace missing, too small or misaligned */
 #define MPM_ERR_HIP (-3)         /* a HIP runtime call failed */
 #define MPM_ERR_STATE (-4)       /* the handle is not usable (e.g. graph missing) */
+#define MPM_ERR_TOO_LARGE (-5)   /* mpm_run_noalloc: the problem needs more than its static scratch */
+
+/* Bytes of the static scratch of mpm_run_noalloc.  The library holds one
+ * array of this size in the memory of every device it runs on, from the
+ * first call there until the process ends: enough for the page's real-time
+ * scenes (55,000 particles on a 64^3 grid need 54 MiB). */
+#define MPM_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* ---- materials ---- */
 #define MPM_FIXED_COROTATED 0 /* elastic solid, state F (3x3) */
@@ -214,6 +221,35 @@ int mpm_set_fused_steps(mpm_sim *sim, int32_t enable);
  * after the step's plasticity projection) or (N) for the fluid.  Any output
  * may be NULL.  Asynchronous on `stream`. */
 int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J, void *stream);
+
+/* For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  One call does what
+ * mpm_create, mpm_step(n_steps), mpm_read_particles and mpm_status do on a
+ * handle, with the same kernels, and allocates nothing: no device memory
+ * (no hipMalloc or hipFree), no host memory, no stream, event or graph.  Its
+ * workspace is the library's static scratch (MPM_NOALLOC_SCRATCH_BYTES on
+ * each device) instead of a caller's: a problem for which
+ * mpm_workspace_bytes(params, n_particles) exceeds it returns
+ * MPM_ERR_TOO_LARGE before anything is enqueued.  The steps are launched one
+ * kernel at a time (no graphs), each sorting, as mpm_step does by default.
+ *   params, n_particles : as for mpm_create; the snow material is refused
+ *                 (MPM_ERR_INVALID_ARG: its plastic state has no output here).
+ *   x, v, C, F_or_J : device, caller-owned, the particle state in creation
+ *                 order, read at the start and overwritten with the state after
+ *                 n_steps steps (layouts of mpm_create and mpm_read_particles).
+ *                 x is required when n_particles > 0; a NULL v, C or F_or_J
+ *                 starts at zero (I, 1) and is not written back.
+ *   E_p         : device, (N) per-particle Young's modulus, or NULL.
+ *   n_steps     : >= 0.
+ *   status      : device, MPM_STATUS_WORDS words of this run's status (as
+ *                 mpm_status), or NULL.
+ *   stream      : everything is enqueued on it, asynchronously.
+ * Every call on one device uses that device's one scratch array and starts by
+ * clearing all of it that the run reads (the array keeps the last call's
+ * contents): calls that overlap on one device, on different streams or from
+ * different threads, race and must be serialised by the caller. */
+int mpm_run_noalloc(const mpm_params *params, int64_t n_particles, float *x, float *v, float *C, float *F_or_J,
+                    const float *E_p, int32_t n_steps, uint32_t *status, void *stream);
 
 /* Snow only: copy each particle's log plastic volume a = ln J_P after the last
  * step (after its plasticity projection, as mpm_read_particles reads F), in

@@ -25,6 +25,8 @@ MPM_ERR_INVALID_ARG = -1
 MPM_ERR_WORKSPACE = -2
 MPM_ERR_HIP = -3
 MPM_ERR_STATE = -4
+MPM_ERR_TOO_LARGE = -5
+MPM_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MPM_FIXED_COROTATED = 0
 MPM_J_FLUID = 1
@@ -40,7 +42,7 @@ MPM_STATUS_WORDS = 8
 
 # Every symbol include/mpm.h declares.
 EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_set_sort_policy", "mpm_set_fused_steps",
-           "mpm_read_particles", "mpm_read_plastic_state",
+           "mpm_read_particles", "mpm_run_noalloc", "mpm_read_plastic_state",
            "mpm_read_grid",
            "mpm_status", "mpm_steps_taken", "mpm_num_kernels", "mpm_kernel_name", "mpm_step_profiled",
            "mpm_destroy", "mpm_error_string")
@@ -100,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.mpm_set_fused_steps.argtypes = [vp, i32]
     L.mpm_set_fused_steps.restype = ctypes.c_int
     L.mpm_read_particles.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.mpm_run_noalloc.argtypes = [pp, i64, vp, vp, vp, vp, vp, i32, vp, vp]
+    L.mpm_run_noalloc.restype = ctypes.c_int
     L.mpm_read_plastic_state.argtypes = [vp, vp, vp]
     L.mpm_read_plastic_state.restype = ctypes.c_int
     L.mpm_read_particles.restype = ctypes.c_int
@@ -180,6 +184,13 @@ def mpm_set_fused_steps(sim: int, enable: int) -> None:
 def mpm_read_particles(sim: int, x=None, v=None, C=None, F_or_J=None, stream=None) -> None:
     _check(lib().mpm_read_particles(sim, _addr(x), _addr(v), _addr(C), _addr(F_or_J), _stream(stream)),
            "mpm_read_particles")
+
+
+def mpm_run_noalloc(params: mpm_params, n_particles: int, x, v=None, C=None, F_or_J=None, E_p=None,
+                    n_steps: int = 1, status=None, stream=None) -> None:
+    _check(lib().mpm_run_noalloc(ctypes.byref(params), int(n_particles), _addr(x), _addr(v), _addr(C),
+                                 _addr(F_or_J), _addr(E_p), int(n_steps), _addr(status), _stream(stream)),
+           "mpm_run_noalloc")
 
 
 def mpm_read_plastic_state(sim: int, alpha, stream=None) -> None:

@@ -58,6 +58,15 @@
 
 #include "../../include/mpm.h"
 
+#include <mutex>
+
+// Static scratch of mpm_run_noalloc: the workspace of a run that allocates
+// nothing.  Every device the library runs on holds its own copy until the
+// process ends.  In host code the name `scratch` is only a stand-in for the
+// array, never a device address: host code uses the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[MPM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 #include "common.h"
@@ -401,6 +410,7 @@ int build_graphs(mpm_sim *sim, int mode) {
 
 // Record the handle's completion event after the work just enqueued on st.
 int mark(mpm_sim *sim, hipStream_t st) {
+  if (!sim->done) return MPM_OK;  // (a handle-free run: no event)
   return hipEventRecord(sim->done, st) == hipSuccess ? MPM_OK : MPM_ERR_HIP;
 }
 
@@ -416,6 +426,111 @@ void release(mpm_sim *sim) {
     (void)hipStreamDestroy(sim->cap);
   }
   delete sim;
+}
+
+// Launch shapes of the simulation's kernels on the current device, and its
+// chunk size (host queries only: nothing is allocated).
+int launch_shapes(mpm_sim *sim) {
+  const SimDev &d = sim->d;
+  if (hipGetDevice(&sim->device) != hipSuccess) return MPM_ERR_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, sim->device) != hipSuccess || cus <= 0)
+    cus = 256;
+  sim->grid_particles = (int)(((d.N + WG - 1) / WG + 7) / 8 * 8);
+  // (occupancy of the instance this material launches)
+  int occ = 0;
+  const void *pk = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true>
+                                          : (const void *)k_p2g<MPM_FIXED_COROTATED, false>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pk, 64, 0) != hipSuccess || occ <= 0) occ = 16;
+  // Measured: 4 waves per SIMD (16 single-wave workgroups per CU) is
+  // P2G's best launch; fewer expose latency and more slowed the kernel.
+  occ = occ < 16 ? occ : 16;
+  sim->grid_p2g = ((cus * occ + NQ - 1) / NQ) * NQ;
+  // Chunk size: KMAX particles when there is enough work for every P2G
+  // wavefront, else smaller (down to 64), so that a small scene's few bins
+  // still spread over many wavefronts: the step time of small scenes is
+  // the latency of one wavefront's chunks.
+  {
+    int shift = KMAX_SHIFT;
+    while (shift > KMIN_SHIFT && ((int64_t)d.N >> shift) < (int64_t)sim->grid_p2g) --shift;
+    sim->d.chunk_shift = shift;
+  }
+  int occ_g = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
+    occ_g = 16;
+  // Measured: 5 waves per SIMD (20 workgroups per CU) is G2P's best launch;
+  // 24 per CU, which 74 VGPRs would allow, was slower.
+  occ_g = occ_g < 20 ? occ_g : 20;
+  sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
+  // The fused kernel holds the G2P velocity window and the P2G windows
+  // (10 KB of LDS, at most 15 workgroups per CU) and, with its loads one
+  // round ahead, 130-150 VGPRs (3 waves per SIMD); P2G's cap of 16 applies.
+  int occ_f = 0;
+  const void *fk = d.material == MPM_J_FLUID
+                       ? (d.has_E ? (const void *)k_g2p2g<MPM_J_FLUID, true> : (const void *)k_g2p2g<MPM_J_FLUID, false>)
+                   : d.material == MPM_SAND
+                       ? (d.has_E ? (const void *)k_g2p2g<MPM_SAND, true> : (const void *)k_g2p2g<MPM_SAND, false>)
+                   : d.material == MPM_SNOW ? (const void *)k_g2p2g<MPM_SNOW, true>
+                       : (d.has_E ? (const void *)k_g2p2g<MPM_FIXED_COROTATED, true>
+                                  : (const void *)k_g2p2g<MPM_FIXED_COROTATED, false>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, fk, 64, 0) != hipSuccess || occ_f <= 0) occ_f = 8;
+  occ_f = occ_f < 16 ? occ_f : 16;
+  sim->grid_g2p2g = ((cus * occ_f + NQ - 1) / NQ) * NQ;
+  sim->grid_blocks = cus * 8;
+  // single-wavefront workgroups, 8 per SIMD: the scatter is a chain of
+  // short dependent loads per chunk, so it wants many chunks in flight
+  sim->grid_scatter = cus * 32;
+  return MPM_OK;
+}
+
+// The initial state: clear the control words, counters, block flags and
+// accumulators, upload the inputs (creation order) and bucket them into
+// bin order in buffer 1.  Fill kernels only: no memset and no allocation.
+int init_state(mpm_sim *sim, const float *x0, const float *v0, const float *C0, const float *F0,
+               const float *E_p, hipStream_t st) {
+  const SimDev &d = sim->d;
+  k_zero_u32<<<1, WG, 0, st>>>(d.ctr, CTR_WORDS);
+  k_zero_u32<<<1, WG, 0, st>>>(d.status, MPM_STATUS_WORDS);
+  const int zb = (int)std::min<int64_t>(((int64_t)d.nbins + WG - 1) / WG, 4096);
+  k_zero_u32<<<zb, WG, 0, st>>>(d.bin_count, (size_t)d.nbins);
+  k_zero_u32<<<zb, WG, 0, st>>>(d.stay_count, (size_t)d.nbins);
+  const int gb = (int)std::min<int64_t>(((int64_t)d.nblk * 512 * 4 + WG - 1) / WG, 16384);
+  for (int k = 0; k < NACC; ++k) {
+    k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[k], (size_t)d.nblk);
+    // G2P may read a stencil node whose weight is exactly zero and that no
+    // particle marked active; it must hold a finite value, so start at zero.
+    k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[k]), (size_t)d.nblk * 512 * 4);
+  }
+  if (d.N > 0) {
+    k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
+    // one bucket pass to bring the initial state into bin order (buffer 1,
+    // whose chunk list the scan writes): the scans of a step that reads
+    // buffer 0 (phase 1)
+    launch_kernel(sim, 0, st, 1, false, false, -1);
+    launch_kernel(sim, 1, st, 1, false, false, -1);
+    k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
+    sim->cur = 1;
+  }
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
+// Device address of `scratch` on device dev, looked up once per device with
+// that device current (each device holds its own copy, at its own address).
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void *noalloc_ptr[NOALLOC_MAX_DEVICES] = {};
+
+int noalloc_scratch(int dev, void **out) {
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return MPM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MPM_ERR_HIP;
+    if ((reinterpret_cast<uintptr_t>(p) & 255u) != 0) return MPM_ERR_WORKSPACE;
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return MPM_OK;
 }
 
 }  // namespace
@@ -453,81 +568,10 @@ int mpm_create(const mpm_params *params, int64_t n_particles, const float *x0, c
 
   int rc = MPM_OK;
   do {
-    if (hipGetDevice(&sim->device) != hipSuccess) { rc = MPM_ERR_HIP; break; }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, sim->device) != hipSuccess || cus <= 0)
-      cus = 256;
-    sim->grid_particles = (int)(((d.N + WG - 1) / WG + 7) / 8 * 8);
-    // (occupancy of the instance this material launches)
-    int occ = 0;
-    const void *pk = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true>
-                                            : (const void *)k_p2g<MPM_FIXED_COROTATED, false>;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pk, 64, 0) != hipSuccess || occ <= 0) occ = 16;
-    // Measured: 4 waves per SIMD (16 single-wave workgroups per CU) is
-    // P2G's best launch; fewer expose latency and more slowed the kernel.
-    occ = occ < 16 ? occ : 16;
-    sim->grid_p2g = ((cus * occ + NQ - 1) / NQ) * NQ;
-    // Chunk size: KMAX particles when there is enough work for every P2G
-    // wavefront, else smaller (down to 64), so that a small scene's few bins
-    // still spread over many wavefronts: the step time of small scenes is
-    // the latency of one wavefront's chunks.
-    {
-      int shift = KMAX_SHIFT;
-      while (shift > KMIN_SHIFT && ((int64_t)d.N >> shift) < (int64_t)sim->grid_p2g) --shift;
-      sim->d.chunk_shift = shift;
-    }
-    int occ_g = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
-      occ_g = 16;
-    // Measured: 5 waves per SIMD (20 workgroups per CU) is G2P's best launch;
-    // 24 per CU, which 74 VGPRs would allow, was slower.
-    occ_g = occ_g < 20 ? occ_g : 20;
-    sim->grid_g2p = ((cus * occ_g + NQ - 1) / NQ) * NQ;
-    // The fused kernel holds the G2P velocity window and the P2G windows
-    // (10 KB of LDS, at most 15 workgroups per CU) and, with its loads one
-    // round ahead, 130-150 VGPRs (3 waves per SIMD); P2G's cap of 16 applies.
-    int occ_f = 0;
-    const void *fk = d.material == MPM_J_FLUID
-                         ? (d.has_E ? (const void *)k_g2p2g<MPM_J_FLUID, true> : (const void *)k_g2p2g<MPM_J_FLUID, false>)
-                     : d.material == MPM_SAND
-                         ? (d.has_E ? (const void *)k_g2p2g<MPM_SAND, true> : (const void *)k_g2p2g<MPM_SAND, false>)
-                     : d.material == MPM_SNOW ? (const void *)k_g2p2g<MPM_SNOW, true>
-                         : (d.has_E ? (const void *)k_g2p2g<MPM_FIXED_COROTATED, true>
-                                    : (const void *)k_g2p2g<MPM_FIXED_COROTATED, false>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, fk, 64, 0) != hipSuccess || occ_f <= 0) occ_f = 8;
-    occ_f = occ_f < 16 ? occ_f : 16;
-    sim->grid_g2p2g = ((cus * occ_f + NQ - 1) / NQ) * NQ;
-    sim->grid_blocks = cus * 8;
-    // single-wavefront workgroups, 8 per SIMD: the scatter is a chain of
-    // short dependent loads per chunk, so it wants many chunks in flight
-    sim->grid_scatter = cus * 32;
+    if ((rc = launch_shapes(sim)) != MPM_OK) break;
     if (hipStreamCreateWithFlags(&sim->cap, hipStreamNonBlocking) != hipSuccess) { rc = MPM_ERR_HIP; break; }
     if (hipEventCreateWithFlags(&sim->done, hipEventDisableTiming) != hipSuccess) { rc = MPM_ERR_HIP; break; }
-
-    // Clear counters, flags, status and the P2G accumulator, then upload.
-    k_zero_u32<<<1, WG, 0, st>>>(d.ctr, CTR_WORDS);
-    k_zero_u32<<<1, WG, 0, st>>>(d.status, MPM_STATUS_WORDS);
-    const int zb = (int)std::min<int64_t>(((int64_t)d.nbins + WG - 1) / WG, 4096);
-    k_zero_u32<<<zb, WG, 0, st>>>(d.bin_count, (size_t)d.nbins);
-    k_zero_u32<<<zb, WG, 0, st>>>(d.stay_count, (size_t)d.nbins);
-    const int gb = (int)std::min<int64_t>(((int64_t)d.nblk * 512 * 4 + WG - 1) / WG, 16384);
-    for (int k = 0; k < NACC; ++k) {
-      k_zero_u32<<<zb, WG, 0, st>>>(d.active_flag[k], (size_t)d.nblk);
-      // G2P may read a stencil node whose weight is exactly zero and that no
-      // particle marked active; it must hold a finite value, so start at zero.
-      k_zero_f32<<<gb, WG, 0, st>>>(reinterpret_cast<float *>(d.gridA[k]), (size_t)d.nblk * 512 * 4);
-    }
-    if (d.N > 0) {
-      k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
-      // one bucket pass to bring the initial state into bin order (buffer 1,
-      // whose chunk list the scan writes): the scans of a step that reads
-      // buffer 0 (phase 1)
-      launch_kernel(sim, 0, st, 1, false, false, -1);
-      launch_kernel(sim, 1, st, 1, false, false, -1);
-      k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
-      sim->cur = 1;
-    }
-    if (hipGetLastError() != hipSuccess) { rc = MPM_ERR_HIP; break; }
+    if ((rc = init_state(sim, x0, v0, C0, F0, E_p, st)) != MPM_OK) break;
     if ((rc = mark(sim, st)) != MPM_OK) break;
     if (d.N > 0) rc = build_graphs(sim, 0);
   } while (0);
@@ -654,6 +698,44 @@ int mpm_read_particles(mpm_sim *sim, float *x, float *v, float *C, float *F_or_J
   return hipGetLastError() == hipSuccess ? mark(sim, st) : MPM_ERR_HIP;
 }
 
+int mpm_run_noalloc(const mpm_params *params, int64_t n_particles, float *x, float *v, float *C, float *F_or_J,
+                    const float *E_p, int32_t n_steps, uint32_t *status, void *stream) {
+  if (!valid_params(params) || n_particles < 0 || n_steps < 0) return MPM_ERR_INVALID_ARG;
+  if (params->material == MPM_SNOW) return MPM_ERR_INVALID_ARG;  // (its plastic state has no output here)
+  if (n_particles > 0 && !x) return MPM_ERR_INVALID_ARG;
+  const size_t need = mpm_workspace_bytes(params, n_particles);
+  if (need == 0) return MPM_ERR_INVALID_ARG;
+  if (need > (size_t)MPM_NOALLOC_SCRATCH_BYTES) return MPM_ERR_TOO_LARGE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MPM_ERR_HIP;
+  void *base = nullptr;
+  int rc = noalloc_scratch(dev, &base);
+  if (rc != MPM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The state of a handle, on the stack: no graphs, no event, no private
+  // stream; the steps are launched eagerly, as the graphs would run them.
+  mpm_sim sim;
+  layout(params, n_particles, E_p != nullptr, static_cast<char *>(base), &sim.d);
+  const SimDev &d = sim.d;
+  if ((rc = launch_shapes(&sim)) != MPM_OK) return rc;
+  // every word the run reads is written first: all of the scratch it uses
+  // starts from the fill kernels of init_state, whatever an earlier call left
+  if ((rc = init_state(&sim, x, v, C, F_or_J, E_p, st)) != MPM_OK) return rc;
+  if (d.N > 0) {
+    for (int32_t k = 0; k < n_steps; ++k) {
+      if ((rc = enqueue_step(&sim, st, sim.steps, 0, true, true)) != MPM_OK) return rc;
+      sim.cur ^= 1;
+      sim.steps += 1;
+    }
+    const int g = sim.grid_g2p;
+    if (d.material == MPM_J_FLUID) k_read_particles<MPM_J_FLUID><<<g, 64, 0, st>>>(d, sim.cur, x, v, C, F_or_J, nullptr);
+    else if (d.material == MPM_SAND) k_read_particles<MPM_SAND><<<g, 64, 0, st>>>(d, sim.cur, x, v, C, F_or_J, nullptr);
+    else k_read_particles<MPM_FIXED_COROTATED><<<g, 64, 0, st>>>(d, sim.cur, x, v, C, F_or_J, nullptr);
+  }
+  if (status) k_copy_u32<<<1, 64, 0, st>>>(status, d.status, MPM_STATUS_WORDS);
+  return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;
+}
+
 int mpm_read_plastic_state(mpm_sim *sim, float *alpha, void *stream) {
   if (!sim || !alpha || sim->d.material != MPM_SNOW) return MPM_ERR_INVALID_ARG;
   if (sim->d.N == 0) return MPM_OK;
@@ -698,6 +780,8 @@ const char *mpm_error_string(int code) {
     case MPM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MPM_ERR_HIP: return "HIP runtime error";
     case MPM_ERR_STATE: return "simulation handle not usable";
+    case MPM_ERR_TOO_LARGE: return "the problem needs more memory than the static scratch of mpm_run_noalloc "
+                                   "(MPM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error";
   }
 }

@@ -51,6 +51,10 @@ __global__ __launch_bounds__(WG) void k_zero_u32(uint32_t *p, size_t n) {
   for (size_t k = (size_t)blockIdx.x * WG + threadIdx.x; k < n; k += (size_t)gridDim.x * WG) p[k] = 0u;
 }
 
+__global__ __launch_bounds__(WG) void k_copy_u32(uint32_t *dst, const uint32_t *src, int n) {
+  for (int k = threadIdx.x; k < n; k += blockDim.x) dst[k] = src[k];
+}
+
 __global__ __launch_bounds__(WG) void k_zero_f32(float *p, size_t n) {
   for (size_t k = (size_t)blockIdx.x * WG + threadIdx.x; k < n; k += (size_t)gridDim.x * WG) p[k] = 0.f;
 }

@@ -53,6 +53,10 @@ def test_every_declaration_cites_the_page():
     cites = declaration_comments()
     assert set(cites) == set(declared_functions())
     for name, comment in cites.items():
+        if name == "mpm_run_noalloc":
+            # not a step of the page's method: its comment names the callers it serves
+            assert "cannot allocate" in comment, comment[:120]
+            continue
         assert re.search(r"\bpage'?s?\b", comment), (name, comment[:120])
         assert re.search(r"principle|problem statement|Fig\.|§|free zone|fused|scene|discussion|study",
                          comment), (name, comment[:120])
@@ -172,3 +176,23 @@ def test_params_struct_matches_header():
         assert ctypes.sizeof(ct) == ctypes.sizeof(want), name
     # uint32 + int32 + float + float[3] + int32 + int32 + 9 floats = 68 bytes
     assert ctypes.sizeof(mpm.mpm_params) == 68
+
+
+def test_run_noalloc_rejects_on_the_host():
+    """mpm_run_noalloc checks its arguments and its size limit before any HIP
+    call (so these run without a GPU): a problem whose workspace exceeds the
+    static scratch, the snow material, negative counts, a missing x."""
+    big = good_params(n=128)
+    assert mpm.mpm_workspace_bytes(big, 100000) > mpm.MPM_NOALLOC_SCRATCH_BYTES
+    L = mpm.lib()
+
+    def run(prm, n, x=1 << 20, steps=1):
+        return L.mpm_run_noalloc(ctypes.byref(prm), n, x, None, None, None, None, steps, None, None)
+
+    assert run(big, 100000) == mpm.MPM_ERR_TOO_LARGE
+    assert run(good_params(material=3), 1000) == mpm.MPM_ERR_INVALID_ARG
+    assert run(good_params(), -1) == mpm.MPM_ERR_INVALID_ARG
+    assert run(good_params(), 1000, steps=-1) == mpm.MPM_ERR_INVALID_ARG
+    assert run(good_params(), 1000, x=None) == mpm.MPM_ERR_INVALID_ARG
+    assert run(good_params(n=4), 1000) == mpm.MPM_ERR_INVALID_ARG
+    assert "scratch" in mpm.mpm_error_string(mpm.MPM_ERR_TOO_LARGE)
