@@ -50,7 +50,7 @@ struct PBuf {
   float *x;      // [3][Np]
   float *v;      // [3][Np]
   float *C;      // [9][Np], row-major components
-  float *F;      // [9][Np] (elastic) or [1][Np] (fluid J), one step behind: see header note
+  float *F;      // [9][Np] F - I (elastic, sand, snow) or [1][Np] J - 1 (fluid), one step behind: see update_F
   float *E;      // [Np] per-particle Young's modulus, or nullptr
   uint32_t *id;  // [Np] creation index
 };
@@ -106,6 +106,23 @@ __device__ __forceinline__ float advanced(const SimDev &s, float x, float v) {
 }
 
 // ------------------------------------------------------------ device utils
+
+// A uniform record (a chunk record) read through the scalar data cache: the
+// address is made wave-uniform and read in the constant address space, so the
+// load is a scalar one.  Chunk records are written by an earlier kernel and
+// only read by the kernels that use this (a wave may write the stayer count
+// of a record it has read; no wave reads a record another one writes).
+// Scalar loads are counted apart from vector memory operations, so waiting
+// for a record does not also wait for the wave's outstanding vector stores
+// and float atomics (which a vector load issued after them would).
+__device__ __forceinline__ uint4 load_record(const uint4 *p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 r = *reinterpret_cast<const __attribute__((address_space(4))) u32x4 *>(((uint64_t)hi << 32) | lo);
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -46,10 +46,10 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
   // (copied here, for a next step that runs no scan).
   if (blockIdx.x == 0 && lane == 0) s.ctr[CTR_NCHUNKS + src] = nch;
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);  // chunk records are loaded one chunk ahead
-  if (qbeg + wq < qend) ch_next = chunks[qbeg + wq];
+  if (qbeg + wq < qend) ch_next = load_record(chunks + qbeg + wq);
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = ch_next;
-    if (c + nwq < qend) ch_next = chunks[c + nwq];
+    if (c + nwq < qend) ch_next = load_record(chunks + c + nwq);
     if (lane == 0) s.chunks[src][c] = ch;
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;

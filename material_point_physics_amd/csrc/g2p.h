@@ -28,39 +28,106 @@ __device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int
 // is loaded once into LDS; each particle then gathers its 27 nodes from LDS.
 
 // Window load in whole cubes (one 128-byte line each): lane = (cube, node in
-// cube), 8 cubes per load instruction, 4 instructions.  This lane's window
-// node of instruction t, packed wx | wy << 8 | wz << 16 (all ones when cube
-// 8t + lane / 8 is past the 27th).
+// cube), 8 cubes per load instruction, 4 instructions.  This lane's word for
+// instruction t (all ones when cube 8t + lane / 8 is past the 27th) packs
+//   bits 0-9   8 cx + 32 cy + 128 cz + j: the node's offset, in node-index
+//              units, from the first node of the window origin's node-block
+//              when each axis' origin is a multiple of 8 (cube (cx, cy, cz)
+//              of the window, node j = jx + 2 jy + 4 jz in the cube);
+//   bits 10-17 its window index (wz PW + wy) PW + wx;
+//   bits 18-20 cx == 2, cy == 2, cz == 2.
+// A window origin is a multiple of 4 per axis.  When it is 4 mod 8 on an
+// axis, that axis' cube coordinates 0 and 1 fall on the origin block's
+// cubes 2 and 3 (offset +16, +64, +128 x 2 node-index units for x, y, z) and
+// coordinate 2 on the next block's cube 0: the offsets below add these as
+// uniform terms.
+constexpr uint32_t WIN_NONE = 0xFFFFFFFFu;
 __device__ __forceinline__ void window_lanes(uint32_t wpack[4]) {
   const int lane = threadIdx.x;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int cb = 8 * t + (lane >> 3), j = lane & 7;
-    const int wx = 2 * (cb % 3) + (j & 1), wy = 2 * ((cb / 3) % 3) + ((j >> 1) & 1), wz = 2 * (cb / 9) + (j >> 2);
-    wpack[t] = cb < 27 ? (uint32_t)(wx | (wy << 8) | (wz << 16)) : 0xFFFFFFFFu;
+    const int cx = cb % 3, cy = (cb / 3) % 3, cz = cb / 9;
+    const int wx = 2 * cx + (j & 1), wy = 2 * cy + ((j >> 1) & 1), wz = 2 * cz + (j >> 2);
+    const uint32_t base = (uint32_t)(8 * cx + 32 * cy + 128 * cz + j);
+    const uint32_t li = (uint32_t)((wz * PW + wy) * PW + wx);
+    const uint32_t c2 = (cx == 2 ? 1u : 0u) | (cy == 2 ? 2u : 0u) | (cz == 2 ? 4u : 0u);
+    wpack[t] = cb < 27 ? (base | li << 10 | c2 << 18) : WIN_NONE;
   }
+}
+__device__ __forceinline__ int wp_li(uint32_t w) { return (int)((w >> 10) & 0xFFu); }
+__device__ __forceinline__ void wp_coords(uint32_t w, int &wx, int &wy, int &wz) {
+  const int li = wp_li(w);
+  wx = li % PW;
+  wy = (li / PW) % PW;
+  wz = li / (PW * PW);
+}
+
+// Whether the window at (ox0, oy0, oz0) lies inside the grid, and whether it
+// also holds no sticky-wall node: uniform per chunk, so most windows take the
+// fast paths below without per-node bounds and wall tests.
+__device__ __forceinline__ bool window_inside(const SimDev &s, int ox0, int oy0, int oz0) {
+  return ox0 + PW <= s.n && oy0 + PW <= s.n && oz0 + PW <= s.n;
+}
+__device__ __forceinline__ bool window_off_walls(const SimDev &s, int ox0, int oy0, int oz0) {
+  const int lo = s.wall, hi = s.n - s.wall;
+  return ox0 >= lo && oy0 >= lo && oz0 >= lo && ox0 + PW <= hi && oy0 + PW <= hi && oz0 + PW <= hi;
 }
 
 // Requests the accumulator values (m, p) of the window at (ox0, oy0, oz0)
 // from accumulator a; nodes outside the grid read as zero.
 __device__ __forceinline__ void fetch_window(const SimDev &s, int a, int ox0, int oy0, int oz0, const uint32_t wpack[4],
                                              float4 acc[4]) {
+  if (window_inside(s, ox0, oy0, oz0)) {
+    const uint32_t nbs = (uint32_t)s.nb;
+    const uint32_t px = (uint32_t)(ox0 >> 2) & 1u, py = (uint32_t)(oy0 >> 2) & 1u, pz = (uint32_t)(oz0 >> 2) & 1u;
+    const uint32_t s0 = 16u * px + 64u * py + 256u * pz;
+    const uint32_t dx2 = px * 480u, dy2 = py * (nbs * 512u - 128u), dz2 = pz * (nbs * nbs * 512u - 512u);
+    float4 *gblk = s.gridA[a] + (((size_t)(oz0 >> 3) * nbs + (size_t)(oy0 >> 3)) * nbs + (size_t)(ox0 >> 3)) * 512u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t w = wpack[t];
+      const uint32_t off = (w & 0x3FFu) + s0 + ((w >> 18) & 1u) * dx2 + ((w >> 19) & 1u) * dy2 + ((w >> 20) & 1u) * dz2;
+      if (t < 3 || w != WIN_NONE) acc[t] = at_byte(gblk, 16u * off);
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int gx = ox0 + (int)(wpack[t] & 0xFFu), gy = oy0 + (int)((wpack[t] >> 8) & 0xFFu),
-              gz = oz0 + (int)((wpack[t] >> 16) & 0xFFu);
-    if (wpack[t] != 0xFFFFFFFFu && gx < s.n && gy < s.n && gz < s.n) acc[t] = s.gridA[a][node_index(s, gx, gy, gz)];
+    int wx, wy, wz;
+    wp_coords(wpack[t], wx, wy, wz);
+    const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
+    if (wpack[t] != WIN_NONE && gx < s.n && gy < s.n && gz < s.n) acc[t] = s.gridA[a][node_index(s, gx, gy, gz)];
   }
 }
 
 // Converts fetched window values to grid velocities (the grid update) in LDS.
 __device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4], const uint32_t wpack[4], int ox0,
                                              int oy0, int oz0, float4 *win) {
+  if (window_inside(s, ox0, oy0, oz0) && window_off_walls(s, ox0, oy0, oz0)) {
+    const float gx = s.dt * s.g[0], gy = s.dt * s.g[1], gz = s.dt * s.g[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t == 3 && wpack[t] == WIN_NONE) continue;
+      const float4 m = acc[t];
+      float4 o = make_float4(0.f, 0.f, 0.f, m.x);
+      if (m.x > 0.f) {
+        const float inv = 1.f / m.x;
+        o.x = m.y * inv + gx;
+        o.y = m.z * inv + gy;
+        o.z = m.w * inv + gz;
+      }
+      win[wp_li(wpack[t])] = o;
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    if (wpack[t] == 0xFFFFFFFFu) continue;
-    const int wx = (int)(wpack[t] & 0xFFu), wy = (int)((wpack[t] >> 8) & 0xFFu), wz = (int)((wpack[t] >> 16) & 0xFFu);
+    if (wpack[t] == WIN_NONE) continue;
+    int wx, wy, wz;
+    wp_coords(wpack[t], wx, wy, wz);
     const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
     win[(wz * PW + wy) * PW + wx] =
         (gx < s.n && gy < s.n && gz < s.n) ? grid_velocity(s, acc[t], gx, gy, gz) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -205,8 +272,11 @@ __device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4
   const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
   uint32_t wpack[4];
   window_lanes(wpack);
+  uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);  // chunk records are loaded one chunk ahead
+  if (qbeg + wq < qend) ch_next = load_record(chunks + qbeg + wq);
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
-    const uint4 ch = chunks[c];
+    const uint4 ch = ch_next;
+    if (c + nwq < qend) ch_next = load_record(chunks + c + nwq);
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
     // The window's accumulator values and the first round's positions are
@@ -282,7 +352,7 @@ __device__ __forceinline__ void g2p_handoff(const SimDev &s, int lay) {
 // G2P of a step that reads buffer src (accumulator a): writes x, v, C in
 // place in layout src ^ 1 and the next step's bin keys and counts.
 template <int MAT>
-__global__ __launch_bounds__(64) void k_g2p(SimDev s, int src, int a) {
+__global__ __launch_bounds__(64, 5) void k_g2p(SimDev s, int src, int a) {
   __shared__ float4 win[PW3];
   g2p_step<MAT>(s, src ^ 1, a, win);
   g2p_handoff(s, src ^ 1);

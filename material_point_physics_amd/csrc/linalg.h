@@ -9,6 +9,25 @@ __device__ __forceinline__ float det3(const float A[9]) {
          A[2] * (A[3] * A[7] - A[4] * A[6]);
 }
 
+// For X = I + Y: the cofactor matrix of X minus I (K, row-major, so that
+// X^{-T} = (I + K) / det X) and det X - 1 (returned), formed without adding
+// and then subtracting I: both keep the relative precision of a small Y (the
+// deformation of an element that has barely strained).
+__device__ __forceinline__ float cofactor_minus_identity(const float Y[9], float K[9]) {
+  const float o0 = 1.f + Y[0], o1 = 1.f + Y[4], o2 = 1.f + Y[8];
+  K[0] = Y[4] + Y[8] + (Y[4] * Y[8] - Y[5] * Y[7]);
+  K[1] = Y[5] * Y[6] - Y[3] * o2;
+  K[2] = Y[3] * Y[7] - o1 * Y[6];
+  K[3] = Y[2] * Y[7] - Y[1] * o2;
+  K[4] = Y[0] + Y[8] + (Y[0] * Y[8] - Y[2] * Y[6]);
+  K[5] = Y[1] * Y[6] - o0 * Y[7];
+  K[6] = Y[1] * Y[5] - Y[2] * o1;
+  K[7] = Y[2] * Y[3] - o0 * Y[5];
+  K[8] = Y[0] + Y[4] + (Y[0] * Y[4] - Y[1] * Y[3]);
+  // first-row expansion: (1 + Y00)(1 + K00) + Y01 K01 + Y02 K02 - 1
+  return Y[0] + K[0] + Y[0] * K[0] + Y[1] * K[1] + Y[2] * K[2];
+}
+
 // Eigenvector of the smallest eigenvalue of a symmetric 3x3 matrix by cyclic
 // Jacobi rotations (Rutishauser's formulation of the symmetric Jacobi method,
 // as in Golub & Van Loan, "Matrix Computations"): accurate to about eps/gap
@@ -132,4 +151,66 @@ __device__ uint32_t rotation_of(const float F[9], float R[9]) {
 #pragma unroll
   for (int k = 0; k < 9; ++k) R[k] = X[k];
   return st;
+}
+
+// The same rotation for F = I + H, returned as Q = R - I with the scaled
+// Newton iteration written for Y = X - I: with the cofactor form above,
+// X' = a X + b (I + K) becomes Y' = a Y + b K + (a + b - 1) I, a = zeta / 2,
+// b = 1 / (2 zeta det X); near a rotation (zeta = 1) a + b - 1 =
+// -d / (2 (1 + d)) with d = det X - 1.  No term subtracts I from a value
+// near I, so F - R = H - Q keeps the relative precision of a small H.  *dF
+// receives det F - 1.  A reflected F (det F < 0) takes the full-matrix path.
+__device__ uint32_t rotation_minus_identity(const float H[9], float Q[9], float *dF) {
+  float K[9];
+  const float d0 = cofactor_minus_identity(H, K);
+  *dF = d0;
+  const float detF = 1.f + d0;
+  if (!(fabsf(detF) > 1e-20f) || !isfinite(detF)) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Q[k] = 0.f;
+    return MPM_STATUS_INVERTED;
+  }
+  if (detF < 0.f) {
+    float F[9], R[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) F[k] = H[k] + ((k % 4 == 0) ? 1.f : 0.f);
+    const uint32_t st = rotation_of(F, R);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Q[k] = R[k] - ((k % 4 == 0) ? 1.f : 0.f);
+    return st;
+  }
+  float Y[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) Y[k] = H[k];
+  bool done = false;
+  float d = d0;
+  for (int it = 0; it < 24 && !done; ++it) {
+    if (it > 0) d = cofactor_minus_identity(Y, K);
+    float a = 0.5f, b, c;
+    if (fabsf(d) > 0.05f) {
+      // determinant scaling for a strongly stretched F
+      const float zeta = exp2f(-0.333333333f * log2f(1.f + d));
+      a = 0.5f * zeta;
+      b = 0.5f * __builtin_amdgcn_rcpf(zeta * (1.f + d));
+      c = a + b - 1.f;
+    } else {
+      // (the iteration corrects the hardware reciprocal's error in b, and c
+      // carries it only relative to d)
+      const float r = __builtin_amdgcn_rcpf(1.f + d);
+      b = 0.5f * r;
+      c = -0.5f * d * r;
+    }
+    float diff = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const float yn = a * Y[k] + b * K[k] + ((k % 4 == 0) ? c : 0.f);
+      const float e = yn - Y[k];
+      diff += e * e;
+      Y[k] = yn;
+    }
+    done = diff < 1e-11f;
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) Q[k] = Y[k];
+  return done ? 0u : (uint32_t)MPM_STATUS_NO_CONVERGE;
 }

@@ -277,15 +277,19 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
   clear_accumulator(s, (acc + 2) & (NACC - 1));
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
   if (qbeg + wq < qend) {
-    ch_next = chunks[qbeg + wq];
+    ch_next = load_record(chunks + qbeg + wq);
     prefetch(ch_next);
   }
+  // (waited for here, as at the end of every chunk below, so that the first
+  // use in the chunk loop needs no wait: see the note before the flush)
+#pragma unroll
+  for (int j = 0; j < KMAX / 64; ++j) __asm__ __volatile__("" ::"v"(pf_src[j]), "v"(pf_cell[j]));
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = ch_next;
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;  // first base node of the bin = window origin
     const bool has_next = c + nwq < qend;
-    if (has_next) ch_next = chunks[c + nwq];
+    if (has_next) ch_next = load_record(chunks + c + nwq);
 
     // Pass A: cell of each particle and its rank within the cell.  Ranks
     // follow the particles' previous storage order (their source index), so
@@ -500,6 +504,12 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
         }
       }
     }
+    // The next chunk's prefetched sources and cells are waited for here,
+    // before the flush: a vector load is complete only once every vector
+    // operation issued before it is, so a wait for them after the flush
+    // would also wait for the flush's atomics.
+#pragma unroll
+    for (int j = 0; j < KMAX / 64; ++j) __asm__ __volatile__("" ::"v"(pf_src[j]), "v"(pf_cell[j]));
     __syncthreads();
     flush_windows(s, sm.win, ox0, oy0, oz0, acc);
     __syncthreads();

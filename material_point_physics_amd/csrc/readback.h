@@ -36,27 +36,24 @@ __global__ __launch_bounds__(64) void k_read_particles(SimDev s, int cur, float 
       if (C)
         for (int k = 0; k < 9; ++k) C[9 * id + k] = Cp[k];
       if (!F && !alpha) continue;
+      // (stored as J - 1 and F - I: see update_F)
       if (MAT == MPM_J_FLUID) {
-        float J = b.F[slot];
-        if (pending) {
-          const float G[9] = {1.f + dt * Cp[0], dt * Cp[1], dt * Cp[2], dt * Cp[3], 1.f + dt * Cp[4],
-                              dt * Cp[5], dt * Cp[6], dt * Cp[7], 1.f + dt * Cp[8]};
-          J = J * det3(G);
-        }
-        F[id] = J;
+        float j = b.F[slot];
+        if (pending) update_F<MPM_J_FLUID>(&j, Cp, dt);
+        F[id] = 1.f + j;
       } else {
-        float Fp[9];
-        for (int k = 0; k < 9; ++k) Fp[k] = b.F[k * Np + slot];
+        float Hp[9];
+        for (int k = 0; k < 9; ++k) Hp[k] = b.F[k * Np + slot];
         float ap = MAT == MPM_SNOW ? b.E[slot] : 0.f;
         if (pending) {
-          update_F<MPM_FIXED_COROTATED>(Fp, Cp, dt);
+          update_F<MPM_FIXED_COROTATED>(Hp, Cp, dt);
           if (MAT == MPM_SAND || MAT == MPM_SNOW) {  // and the plasticity projection that follows the update
             float A[9];
-            (void)plastic_affine<MAT>(s, Fp, s.E, ap, Cp, A, true);
+            (void)plastic_affine<MAT>(s, Hp, s.E, ap, Cp, A, true);
           }
         }
         if (F)
-          for (int k = 0; k < 9; ++k) F[9 * id + k] = Fp[k];
+          for (int k = 0; k < 9; ++k) F[9 * id + k] = Hp[k] + ((k % 4 == 0) ? 1.f : 0.f);
         if (MAT == MPM_SNOW && alpha) alpha[id] = ap;
       }
     }

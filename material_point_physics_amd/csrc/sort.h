@@ -5,6 +5,7 @@
 // --------------------------------------------------------------- kernels
 
 // Creation: AoS inputs -> SoA buffer 0 (creation order), ids, first keys.
+// F (J) is stored as F - I (J - 1).
 __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__ x0, const float *__restrict__ v0,
                                              const float *__restrict__ C0, const float *__restrict__ F0,
                                              const float *__restrict__ E_p) {
@@ -26,10 +27,11 @@ __global__ __launch_bounds__(WG) void k_init(SimDev s, const float *__restrict__
     }
     if (bad) flag_status(s, MPM_STATUS_BAD_INPUT, 0);
     for (int k = 0; k < 9; ++k) b.C[k * Np + i] = C0 ? C0[9 * (size_t)i + k] : 0.f;
+    // the deformation is stored as F - I (J - 1): see update_F
     if (s.material == MPM_J_FLUID) {
-      b.F[i] = F0 ? F0[i] : 1.f;
+      b.F[i] = F0 ? F0[i] - 1.f : 0.f;
     } else {
-      for (int k = 0; k < 9; ++k) b.F[k * Np + i] = F0 ? F0[9 * (size_t)i + k] : ((k % 4 == 0) ? 1.f : 0.f);
+      for (int k = 0; k < 9; ++k) b.F[k * Np + i] = F0 ? F0[9 * (size_t)i + k] - ((k % 4 == 0) ? 1.f : 0.f) : 0.f;
     }
     if (s.has_E) b.E[i] = E_p ? E_p[i] : s.snow_a0;  // snow: the slot holds the log plastic volume
     b.id[i] = i;
@@ -346,16 +348,16 @@ __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
   uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
   uint32_t prev_next = 0xFFFFFFFFu;
   if (blockIdx.x < nch) {
-    ch_next = chunks[blockIdx.x];
-    if (blockIdx.x > 0) prev_next = chunks[blockIdx.x - 1].z;
+    ch_next = load_record(chunks + blockIdx.x);
+    if (blockIdx.x > 0) prev_next = load_record(chunks + blockIdx.x - 1).z;
   }
   for (uint32_t c = blockIdx.x; c < nch; c += gridDim.x) {
     const uint4 ch = ch_next;
     const uint32_t prev_bin = prev_next;
     const uint32_t start = ch.x, count = min(ch.y, (uint32_t)KMAX), bin = ch.z;
     if (c + gridDim.x < nch) {
-      ch_next = chunks[c + gridDim.x];
-      prev_next = chunks[c + gridDim.x - 1].z;
+      ch_next = load_record(chunks + c + gridDim.x);
+      prev_next = load_record(chunks + c + gridDim.x - 1).z;
     }
     // all of the chunk's keys at once (lanes past the count read none)
     uint32_t kc[KMAX / 64];

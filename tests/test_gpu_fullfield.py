@@ -17,6 +17,10 @@ Tolerances (reading S13 and the fp32 envelope): the grid after each step,
 per field, max|gpu - oracle| / max|oracle| <= max(1e-5, 10x the fp32
 oracle's error on the same scene); every particle field, normalised by its
 scale, within 10x the fp32 oracle's error and never required below 2e-6.
+At the headline sizes the kernels must also meet 1e-5 outright on every
+field after both steps: from the second step the slab's stress comes from
+strains near 1e-7, which an fp32 F would round (the fp32 oracle is 4% of
+max |v| off there), and the kernels keep F - I instead.
 The fp64 and fp32 oracles run in two threads (the C oracle releases the
 interpreter lock).
 """
@@ -85,7 +89,10 @@ def particle_errs(got, ref, n):
                 F=float(np.abs(got["F"] - ref["F"]).max()))
 
 
-def check_two_steps(sc, gpu, o64, o32):
+def check_two_steps(sc, gpu, o64, o32, tight=None):
+    """tight: also hold every particle field and the grid to this bound
+    against the fp64 oracle (the kernels keep the deformation as F - I, so a
+    small strain keeps full single precision where an fp32 F would not)."""
     for k in range(2):
         g, r, r32 = gpu[k], o64[k], o32[k]
         for fld in ("m", "p"):
@@ -98,6 +105,11 @@ def check_two_steps(sc, gpu, o64, o32):
         pu.log(f"{sc.name} step {k + 1} particles: {err} (fp32 oracle {env})")
         for f in err:
             assert err[f] <= max(10 * env[f], 2e-6), (k, f, err[f], env[f])
+            if tight is not None:
+                assert err[f] <= tight, (k, f, err[f], tight)
+        if tight is not None:
+            for fld in ("m", "p"):
+                assert pu.field_maxrel(g[fld], r[fld]) <= tight, (k, fld)
     status = gpu[2]
     assert status[0] == 0, status
 
@@ -109,7 +121,7 @@ def test_headline_full_field_two_steps(name):
     gpu = gpu_two_steps(sc)
     pu.log("oracles (fp64, fp32) on the whole scene")
     o64, o32 = oracle_two_steps(sc)
-    check_two_steps(sc, gpu, o64, o32)
+    check_two_steps(sc, gpu, o64, o32, tight=1e-5)
 
 
 def chunk256_scene():
