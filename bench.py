@@ -79,6 +79,23 @@ def kernel_bytes(N: int, active_nodes: int, nbins: int, material: int, has_E: bo
     }
 
 
+def roctx():
+    """ROCTx range push/pop (the profiler SDK's marker library), so that a
+    `rocprofv3 --marker-trace` run can delimit the timed region; None when
+    the library is absent (the markers are then skipped)."""
+    import ctypes
+    for name in ("librocprofiler-sdk-roctx.so.1", "/opt/rocm/lib/librocprofiler-sdk-roctx.so.1"):
+        try:
+            L = ctypes.CDLL(name)
+        except OSError:
+            continue
+        L.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        L.roctxRangePushA.restype = ctypes.c_int
+        L.roctxRangePop.restype = ctypes.c_int
+        return L
+    return None
+
+
 def source_sha1() -> str:
     """sha1 of the kernel code: every file of csrc/ in name order, with
     comments and whitespace removed (a comment edit does not change a kernel)."""
@@ -165,13 +182,19 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: K graph-replayed steps, synchronised on both sides
+    # (a ROCTx range "mpm_timed_steps" marks it for the API-trace audit)
+    rtx = roctx()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
+    if rtx:
+        rtx.roctxRangePushA(b"mpm_timed_steps")
     ev0.record(stream)
     sim.step(args.steps)
     ev1.record(stream)
+    if rtx:
+        rtx.roctxRangePop()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_start
     dev_ms = ev0.elapsed_time(ev1)

@@ -3,6 +3,7 @@
 Usage:
     python -m material_point_physics_amd.profiling <results.db> [--kernels k_] [--title TEXT]
     python -m material_point_physics_amd.profiling <fetch.db> --write-db <write.db>
+    python -m material_point_physics_amd.profiling <trace.db> --api-audit
 
 Prints, per kernel: number of dispatches, average / median / total duration
 (from the kernel trace), and the per-dispatch median of every collected
@@ -84,7 +85,12 @@ def main():
     ap.add_argument("--kernels", default="")
     ap.add_argument("--title", default="")
     ap.add_argument("--write-db", default="", help="with a FETCH_SIZE db: print copy-calibrated traffic")
+    ap.add_argument("--api-audit", action="store_true",
+                    help="with a --hip-trace --marker-trace db: HIP calls inside the timed range")
     a = ap.parse_args()
+    if a.api_audit:
+        print(api_audit_text(a.db, a.title))
+        return
     if a.write_db:
         t = traffic(a.db, a.write_db, a.kernels or "k_")
         print(f"copy calibration: FETCH_SIZE x {t['fetch_factor']:.4f}, WRITE_SIZE x {t['write_factor']:.4f}")
@@ -133,6 +139,54 @@ def traffic(fetch_db: str, write_db: str, kernels: str = "k_"):
         w = wc.get(k, {}).get("WRITE_SIZE", 0.0) * wk * 1024
         out[k] = {"fetch_bytes": f, "write_bytes": w, "total_bytes": f + w}
     return {"fetch_factor": fk, "write_factor": wk, "kernels": out}
+
+
+# ------------------------------------------------------- host-API audit
+
+# HIP calls that would stall the host on the device, copy device data back,
+# or allocate: none may occur between two steps.
+FORBIDDEN_API = ("Synchronize", "hipMemcpy", "hipMalloc", "hipFree", "hipHostMalloc", "hipHostFree",
+                 "hipMemset", "hipStreamQuery", "hipEventQuery", "hipDeviceReset")
+
+
+def api_audit(db: str, marker: str = "mpm_timed_steps"):
+    """HIP runtime calls made on the thread of the ROCTx range `marker`
+    while it was open (a `rocprofv3 --hip-trace --marker-trace` database):
+    returns (calls by name, the range's duration in ns, forbidden names seen)."""
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select category, name, tid, start, end, id from regions").fetchall()
+    # rocprofv3 records a ROCTx range under the API name (roctxThreadRangeA)
+    # with the message among the region's arguments
+    msgs = collections.defaultdict(list)
+    try:
+        for rid, val in cur.execute("select id, value from region_args"):
+            msgs[rid].append(str(val))
+    except sqlite3.OperationalError:
+        pass
+    rng = [r for r in rows if r[1] == marker or ("MARKER" in str(r[0]).upper() and marker in msgs.get(r[5], []))]
+    if not rng:
+        # (the message is not always stored: then the run's only ROCTx range,
+        # which bench.py opens around its timed steps and nowhere else)
+        rng = [r for r in rows if "MARKER" in str(r[0]).upper() and "RANGE" in str(r[0]).upper()]
+    if len(rng) != 1:
+        raise ValueError(f"expected one '{marker}' range in {db}, found {len(rng)}")
+    _, _, tid, t0, t1, _ = rng[0]
+    calls = collections.Counter(r[1] for r in rows
+                                if r[2] == tid and t0 <= r[3] <= t1 and r[1] != marker
+                                and "MARKER" not in str(r[0]).upper())
+    bad = sorted(n for n in calls if any(f in n for f in FORBIDDEN_API))
+    return calls, t1 - t0, bad
+
+
+def api_audit_text(db: str, title: str = "") -> str:
+    calls, dur, bad = api_audit(db)
+    out = [title] if title else []
+    out.append(f"timed range: {dur / 1e6:.3f} ms")
+    out.append(f"{'HIP call inside the timed range':40s} {'count':>8s}")
+    for n, k in sorted(calls.items(), key=lambda kv: (-kv[1], kv[0])):
+        out.append(f"{n:40s} {k:8d}")
+    out.append(f"forbidden calls (synchronisation, copies, allocation): {', '.join(bad) if bad else 'none'}")
+    return "\n".join(out)
 
 
 if __name__ == "__main__":

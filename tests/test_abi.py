@@ -196,3 +196,25 @@ def test_run_noalloc_rejects_on_the_host():
     assert run(good_params(), 1000, x=None) == mpm.MPM_ERR_INVALID_ARG
     assert run(good_params(n=4), 1000) == mpm.MPM_ERR_INVALID_ARG
     assert "scratch" in mpm.mpm_error_string(mpm.MPM_ERR_TOO_LARGE)
+
+
+def test_committed_api_trace_shows_no_sync_or_allocation_between_steps():
+    """The committed HIP API trace of bench.py's timed region (rocprofv3
+    --hip-trace, delimited by a ROCTx range): the steps are graph launches,
+    and no synchronisation, device-to-host copy or allocation occurs between
+    them (the page's CPU-GPU synchronisation and memory-reallocation
+    principles, Figs. 3 and 4)."""
+    path = os.path.join(ROOT, "profiles", "jelly3_55k_timed_steps_hip_api.txt")
+    calls = {}
+    forbidden_line = None
+    for line in open(path):
+        m = re.match(r"^(hip[A-Za-z0-9_]+)\s+(\d+)\s*$", line)
+        if m:
+            calls[m.group(1)] = int(m.group(2))
+        if line.startswith("forbidden calls"):
+            forbidden_line = line
+    assert forbidden_line is not None and forbidden_line.strip().endswith(": none")
+    assert calls.get("hipGraphLaunch", 0) == 50 // 8 + 50 % 8
+    for name in calls:
+        for bad in ("Synchronize", "hipMemcpy", "hipMalloc", "hipFree", "hipMemset", "Query"):
+            assert bad not in name, name
