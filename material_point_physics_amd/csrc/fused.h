@@ -158,7 +158,7 @@ __device__ __forceinline__ void fused_step(const SimDev &s, int src, int a, bool
       }
     }
     __syncthreads();
-    flush_windows(s, sm.win, ox0, oy0, oz0, a1);
+    flush_windows<NWIN>(s, sm.win, ox0, oy0, oz0, a1);
     if (lane == 0 && nmov) atomicAdd(s.ctr + CTR_MOVERS, nmov);  // for the sort decision two steps on
     __syncthreads();  // the windows are cleared for the next chunk
   }

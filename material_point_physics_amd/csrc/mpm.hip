@@ -258,6 +258,7 @@ struct mpm_sim {
   int grid_particles = 0;  // ceil(N / WG), rounded up to a multiple of 8
   int grid_scatter = 0;
   int grid_p2g = 0;
+  bool p2g_wide = false;  // small scene: P2G with NWIN_WIDE windows per wavefront
   int grid_g2p = 0;
   int grid_g2p2g = 0;
   int grid_blocks = 0;   // node-block loops (grid readback)
@@ -283,6 +284,25 @@ int mode_period(const mpm_sim *sim, int mode) {
   return mode == 2 ? std::max(sim->sort_interval, STEP_BATCH) : NACC;
 }
 
+// P2G of the step of phase p with NW accumulation windows per wavefront.
+template <int NW>
+void launch_p2g(const mpm_sim *sim, hipStream_t st, int src, int p) {
+  const SimDev &d = sim->d;
+  const int g = sim->grid_p2g;
+  if (d.material == MPM_J_FLUID) {
+    if (d.has_E) k_p2g<MPM_J_FLUID, true, NW><<<g, 64, 0, st>>>(d, src, p);
+    else k_p2g<MPM_J_FLUID, false, NW><<<g, 64, 0, st>>>(d, src, p);
+  } else if (d.material == MPM_SAND) {
+    if (d.has_E) k_p2g<MPM_SAND, true, NW><<<g, 64, 0, st>>>(d, src, p);
+    else k_p2g<MPM_SAND, false, NW><<<g, 64, 0, st>>>(d, src, p);
+  } else if (d.material == MPM_SNOW) {  // (its scalar slot always carries the log plastic volume)
+    k_p2g<MPM_SNOW, true, NW><<<g, 64, 0, st>>>(d, src, p);
+  } else {
+    if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true, NW><<<g, 64, 0, st>>>(d, src, p);
+    else k_p2g<MPM_FIXED_COROTATED, false, NW><<<g, 64, 0, st>>>(d, src, p);
+  }
+}
+
 // Kernel k of the step of phase p (reads buffer src = (p + 1) mod 2,
 // accumulates into p); fused: the plain G2P is replaced by the G2P2G kernel,
 // which stores v and C when write_vc is set and takes the next step's sort
@@ -304,18 +324,8 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
       k_scatter<<<sim->grid_scatter, 64, 0, st>>>(d, src);
       break;
     case 3:
-      if (d.material == MPM_J_FLUID) {
-        if (d.has_E) k_p2g<MPM_J_FLUID, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-        else k_p2g<MPM_J_FLUID, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-      } else if (d.material == MPM_SAND) {
-        if (d.has_E) k_p2g<MPM_SAND, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-        else k_p2g<MPM_SAND, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-      } else if (d.material == MPM_SNOW) {  // (its scalar slot always carries the log plastic volume)
-        k_p2g<MPM_SNOW, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-      } else {
-        if (d.has_E) k_p2g<MPM_FIXED_COROTATED, true><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-        else k_p2g<MPM_FIXED_COROTATED, false><<<sim->grid_p2g, 64, 0, st>>>(d, src, p);
-      }
+      if (sim->p2g_wide) launch_p2g<NWIN_WIDE>(sim, st, src, p);
+      else launch_p2g<NWIN>(sim, st, src, p);
       break;
     case 4:
       if (fused) {
@@ -439,8 +449,8 @@ int launch_shapes(mpm_sim *sim) {
   sim->grid_particles = (int)(((d.N + WG - 1) / WG + 7) / 8 * 8);
   // (occupancy of the instance this material launches)
   int occ = 0;
-  const void *pk = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true>
-                                          : (const void *)k_p2g<MPM_FIXED_COROTATED, false>;
+  const void *pk = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true, NWIN>
+                                          : (const void *)k_p2g<MPM_FIXED_COROTATED, false, NWIN>;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pk, 64, 0) != hipSuccess || occ <= 0) occ = 16;
   // Measured: 4 waves per SIMD (16 single-wave workgroups per CU) is
   // P2G's best launch; fewer expose latency and more slowed the kernel.
@@ -454,6 +464,20 @@ int launch_shapes(mpm_sim *sim) {
     int shift = KMAX_SHIFT;
     while (shift > KMIN_SHIFT && ((int64_t)d.N >> shift) < (int64_t)sim->grid_p2g) --shift;
     sim->d.chunk_shift = shift;
+  }
+  // A scene whose 64-particle chunks fit in about three quarters of the
+  // launch the eight-window P2G allows (its LDS admits fewer wavefronts per
+  // CU) takes that P2G: every chunk still has a wavefront to itself, and the
+  // dense chunks that set the step time need a quarter of the passes.
+  {
+    int occ_w = 0;
+    const void *pw = d.material == MPM_SNOW ? (const void *)k_p2g<MPM_SNOW, true, NWIN_WIDE>
+                                            : (const void *)k_p2g<MPM_FIXED_COROTATED, false, NWIN_WIDE>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_w, pw, 64, 0) != hipSuccess || occ_w <= 0) occ_w = 1;
+    const int grid_w = ((cus * occ_w) / NQ) * NQ;
+    sim->p2g_wide = sim->d.chunk_shift == KMIN_SHIFT && grid_w >= NQ &&
+                    4 * ((int64_t)d.N >> KMIN_SHIFT) <= 3 * (int64_t)grid_w;
+    if (sim->p2g_wide) sim->grid_p2g = grid_w;
   }
   int occ_g = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)

@@ -7,9 +7,9 @@
 //
 // Accumulation without atomics: on gfx950, LDS float atomics serialise per
 // lane, so the windows are private to the wavefront and updated with plain
-// read-modify-writes.  There are NWIN windows; the particle of rank r in its
-// cell (r-th of that cell in the chunk) accumulates into window r % NWIN and
-// has super-rank r / NWIN.  The chunk's particles are ordered by (super-rank,
+// read-modify-writes.  There are NW windows; the particle of rank r in its
+// cell (r-th of that cell in the chunk) accumulates into window r % NW and
+// has super-rank r / NW.  The chunk's particles are ordered by (super-rank,
 // window, cell): lanes that share a super-rank differ in (window, cell), so
 // for a fixed stencil offset their target addresses are distinct, and one
 // masked ds_read/ds_write pair per offset adds all of them.  A round of 64
@@ -17,21 +17,29 @@
 // executes a wavefront's accesses in issue order; compiler fences keep that
 // order.  The flush adds the windows and issues one native global atomic per
 // node and channel.
-constexpr int NWIN = 2;                  // accumulation windows per wavefront
-constexpr int KSR = KMAX / NWIN;         // super-ranks per chunk, at most
+// NW windows per wavefront: two where many wavefronts share a compute unit
+// (large scenes: 16 per CU, 8 KB of LDS each), eight for small scenes, whose
+// few chunks leave most of the LDS free.  A small scene's P2G lasts as long as
+// its slowest chunk, and a chunk drawn from a dense or partly filled bin may
+// hold 16-32 particles of one cell: with eight windows it needs a quarter of
+// the passes.  The fused G2P2G pass uses two.
+constexpr int NWIN = 2;                  // windows of the large-scene P2G and of the fused pass
+constexpr int NWIN_WIDE = 8;             // windows of the small-scene P2G
 
+template <int NW>
 struct P2GRankTables {                   // lives in the window space while a chunk is ordered
   uint32_t hist[CB3];                    // particles per cell
   uint32_t subcnt[KMAX / 64][CB3];       // particles per cell in each sub-round of 64
-  uint32_t rstart[KSR + 2];              // first position of each super-rank
-  uint64_t rmask[NWIN * KSR];            // per (super-rank, window): cells present (bit = cell)
+  uint32_t rstart[KMAX / NW + 2];        // first position of each super-rank
+  uint64_t rmask[KMAX];                  // per (super-rank, window): cells present (bit = cell)
 };
-static_assert(sizeof(P2GRankTables) <= sizeof(float4) * NWIN * PW3, "rank tables must fit the windows");
 
+template <int NW>
 union P2GShared {
-  float4 win[NWIN * PW3];
-  P2GRankTables rk;
+  float4 win[NW * PW3];
+  P2GRankTables<NW> rk;
 };
+static_assert(sizeof(P2GRankTables<NWIN>) <= sizeof(float4) * NWIN * PW3, "rank tables must fit the windows");
 
 
 // Base node b = floor(x/dx - 1/2), fractional offset f and quadratic
@@ -130,7 +138,7 @@ __device__ __forceinline__ void clear_accumulator(const SimDev &s, int a) {
   }
 }
 
-// Flush: the sum of the NWIN windows (window origin = first base node of
+// Flush: the sum of the NW windows (window origin = first base node of
 // the bin, ox0, oy0, oz0), one native global float atomic per nonzero value
 // (adding zero changes nothing) into accumulator a, in whole cubes: lane =
 // (cube of the pair, node in cube, channel), so each atomic instruction
@@ -144,6 +152,7 @@ __device__ __forceinline__ void clear_accumulator(const SimDev &s, int a) {
 // steps later clears exactly these (and mpm_read_grid reads them).  A marked
 // block whose nodes got no mass is cleared for nothing, which is harmless.
 // Plain stores: every writer stores the same value.
+template <int NW>
 __device__ __forceinline__ void flush_windows(const SimDev &s, const float4 *win, int ox0, int oy0, int oz0, int a) {
   const int lane = threadIdx.x;
   {
@@ -176,7 +185,7 @@ __device__ __forceinline__ void flush_windows(const SimDev &s, const float4 *win
       const int kw = h ? kw1 : kw0;
       float val = 0.f;
 #pragma unroll
-      for (int w = 0; w < NWIN; ++w) val += winl[4 * (kw + w * PW3)];
+      for (int w = 0; w < NW; ++w) val += winl[4 * (kw + w * PW3)];
       bool inb = val != 0.f;
       if (!interior) {
         const int cx = h ? x1 : x0, cy = h ? y1 : y0, cz = h ? z1 : z0;
@@ -230,8 +239,8 @@ __device__ __forceinline__ void deposit_global(const SimDev &s, int a, const int
 // The P2G of one step.  FREE: a step without a sort (free-zone policy), with
 // the paths for particles outside their chunk's bin; the per-step-sort
 // instance has none of that code.
-template <int MAT, bool HAS_E, bool FREE>
-__device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GShared &sm, uint32_t *order,
+template <int MAT, bool HAS_E, bool FREE, int NW>
+__device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GShared<NW> &sm, uint32_t *order,
                                          uint8_t *ordtag) {
   const PBuf in = s.buf[src], out = s.buf[src ^ 1];
   const int lane = threadIdx.x;
@@ -300,7 +309,7 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
     // are ranked in the order of their smallest source.  Lanes with the same
     // cell are matched bit by bit with ballots; the lowest lane of each group
     // records the group's size (leaders have distinct cells: no atomics).
-    P2GRankTables &rk = sm.rk;
+    P2GRankTables<NW> &rk = sm.rk;
     const uint64_t below = (1ull << lane) - 1ull;
     // (source index and cell come in sorted order: the scatter carried the
     // cell that G2P computed with the key, so no position gather is needed)
@@ -363,20 +372,20 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       rk.hist[lane] = total;
     }
     __syncthreads();
-    // Rank tables: rmask[NWIN sr + w] = cells holding a particle of rank
-    // NWIN sr + w (lane = cell), rstart[sr] = position of the first particle
+    // Rank tables: rmask[NW sr + w] = cells holding a particle of rank
+    // NW sr + w (lane = cell), rstart[sr] = position of the first particle
     // of super-rank sr.
     {
       const uint32_t cnt = rk.hist[lane];
       uint32_t mx = cnt;
       for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
       uint32_t run = 0;
-      for (uint32_t sr = 0; NWIN * sr < mx; ++sr) {
+      for (uint32_t sr = 0; NW * sr < mx; ++sr) {
         uint32_t here = 0;
 #pragma unroll
-        for (int w = 0; w < NWIN; ++w) {
-          const uint64_t m = __ballot(cnt > NWIN * sr + w);
-          if (lane == 0) rk.rmask[NWIN * sr + w] = m;
+        for (int w = 0; w < NW; ++w) {
+          const uint64_t m = __ballot(cnt > NW * sr + w);
+          if (lane == 0) rk.rmask[NW * sr + w] = m;
           here += (uint32_t)__popcll(m);
         }
         if (lane == 0) rk.rstart[sr] = run;
@@ -395,19 +404,19 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
           order[pos] = srcs[j];
           ordtag[pos] = MOVER_TAG;
         } else {
-          const uint32_t cell = cells[j], sr = rank[j] / NWIN, w = rank[j] % NWIN;
-          uint32_t pos = rk.rstart[sr] + (uint32_t)__popcll(rk.rmask[NWIN * sr + w] & ((1ull << cell) - 1ull));
-          for (uint32_t w2 = 0; w2 < w; ++w2) pos += (uint32_t)__popcll(rk.rmask[NWIN * sr + w2]);
+          const uint32_t cell = cells[j], sr = rank[j] / NW, w = rank[j] % NW;
+          uint32_t pos = rk.rstart[sr] + (uint32_t)__popcll(rk.rmask[NW * sr + w] & ((1ull << cell) - 1ull));
+          for (uint32_t w2 = 0; w2 < w; ++w2) pos += (uint32_t)__popcll(rk.rmask[NW * sr + w2]);
           pos = min(pos, (uint32_t)KMAX - 1u);
           order[pos] = srcs[j];
-          ordtag[pos] = (uint8_t)(sr * NWIN + w);
+          ordtag[pos] = (uint8_t)(sr * NW + w);
         }
       }
       mbefore += (uint32_t)__popcll(mmask);
     }
     __syncthreads();
     // the tables are dead: clear the windows
-    for (int k = lane; k < NWIN * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = lane; k < NW * PW3; k += 64) sm.win[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
 
     if (has_next) prefetch(ch_next);
@@ -470,7 +479,7 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       momentum_terms(mass, dx, vp, A, f, q0, Ad);
       const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
                 lz = min(max(b[2] - oz0, 0), CB - 1);
-      const int li0 = (int)(tag % NWIN) * PW3 + (lz * PW + ly) * PW + lx;
+      const int li0 = (int)(tag % NW) * PW3 + (lz * PW + ly) * PW + lx;
 
       // Passes: lanes conflict only when they share (window, cell).  The
       // lane's pass is its occurrence index among the earlier lanes of the
@@ -482,10 +491,12 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       const bool inwin = valid && !mov;
       uint32_t pass_id;
       {
-        const uint32_t wc = (tag % NWIN) * (uint32_t)CB3 + (uint32_t)((lz * CB + ly) * CB + lx);
+        const uint32_t wc = (tag % NW) * (uint32_t)CB3 + (uint32_t)((lz * CB + ly) * CB + lx);
         uint64_t peers = __ballot(inwin);
+        constexpr int WC_BITS = NW == 2 ? 7 : (NW == 4 ? 8 : 9);  // 6 cell bits + log2(NW)
+        static_assert(NW == 2 || NW == 4 || NW == 8, "window counts with a bit width here");
 #pragma unroll
-        for (int k = 0; k < 7; ++k) {
+        for (int k = 0; k < WC_BITS; ++k) {
           const uint64_t bk = __ballot((wc >> k) & 1u);
           peers &= ((wc >> k) & 1u) ? bk : ~bk;
         }
@@ -511,19 +522,19 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
 #pragma unroll
     for (int j = 0; j < KMAX / 64; ++j) __asm__ __volatile__("" ::"v"(pf_src[j]), "v"(pf_cell[j]));
     __syncthreads();
-    flush_windows(s, sm.win, ox0, oy0, oz0, acc);
+    flush_windows<NW>(s, sm.win, ox0, oy0, oz0, acc);
     __syncthreads();
   }
 }
 
-template <int MAT, bool HAS_E>
+template <int MAT, bool HAS_E, int NW>
 // (snow: at least 4 waves per SIMD, which holds it at 128 VGPRs with no spill;
 // measured 13% faster than its unconstrained 130 VGPRs at 3 waves)
-__global__ __launch_bounds__(64, (MAT == MPM_SNOW) ? 4 : 1) void k_p2g(SimDev s, int src, int acc) {
-  __shared__ P2GShared sm;
+__global__ __launch_bounds__(64, (MAT == MPM_SNOW && NW == NWIN) ? 4 : 1) void k_p2g(SimDev s, int src, int acc) {
+  __shared__ P2GShared<NW> sm;
   __shared__ uint32_t order[KMAX];  // source index of each processing position
-  __shared__ uint8_t ordtag[KMAX];  // super-rank * NWIN + window of each position (or MOVER_TAG)
+  __shared__ uint8_t ordtag[KMAX];  // super-rank * NW + window of each position (or MOVER_TAG)
   if (s.ctr[CTR_LOOK + src] != 0u) return;  // done by the fused kernel of the step before
-  if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false>(s, src, acc, sm, order, ordtag);
-  else p2g_step<MAT, HAS_E, true>(s, src, acc, sm, order, ordtag);
+  if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false, NW>(s, src, acc, sm, order, ordtag);
+  else p2g_step<MAT, HAS_E, true, NW>(s, src, acc, sm, order, ordtag);
 }
