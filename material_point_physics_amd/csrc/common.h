@@ -73,6 +73,7 @@ struct SimDev {
   float lo, hi;               // position clamp
   uint32_t max_chunks;
   int32_t chunk_shift;        // chunks hold up to 2^chunk_shift (64..KMAX) particles of one bin
+  int32_t sort_small;         // 1: k_sort_small sorts (the step's P2G then keeps the control words)
   PBuf buf[2];
   uint32_t *perm, *key;         // key = bin | cell << KEY_CELL_SHIFT (cell of the base node in its bin)
   uint8_t *cellp;              // cell of the base node in its bin, in perm (sorted) order
@@ -210,6 +211,21 @@ __device__ __forceinline__ void bspline_weights(float f, float w[3]) {
   w[0] = 0.5f * a * a;
   w[1] = 0.75f - b * b;
   w[2] = 0.5f * c * c;
+}
+
+// Inclusive prefix sum over the wavefront's 64 lanes (Hillis-Steele with DPP
+// row shifts by 1, 2, 4 and 8 lanes within each row of 16, then the
+// broadcasts of lane 15 into rows 1 and 3 and of lane 31 into rows 2 and 3).
+// Lanes a shift reaches past the row's start, and rows a broadcast skips,
+// add the 0 they receive.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
 // Wave-aggregated atomic add of 1 per valid lane into counters[key]: one

@@ -259,6 +259,7 @@ struct mpm_sim {
   int grid_scatter = 0;
   int grid_p2g = 0;
   bool p2g_wide = false;  // small scene: P2G with NWIN_WIDE windows per wavefront
+  int grid_sort_small = 0;  // k_sort_small's launch (d.sort_small)
   int grid_g2p = 0;
   int grid_g2p2g = 0;
   int grid_blocks = 0;   // node-block loops (grid readback)
@@ -303,6 +304,21 @@ void launch_p2g(const mpm_sim *sim, hipStream_t st, int src, int p) {
   }
 }
 
+// Phase 0 (tile totals) or 1 (bins) of the scan of a step that reads
+// buffer src.  (A small grid's bins are scanned by one workgroup, without
+// tile totals.)
+void launch_scan(const mpm_sim *sim, hipStream_t st, int src, int phase) {
+  const SimDev &d = sim->d;
+  const bool tiles = d.nbins > SCAN_SMALL_NT * SCAN_PER;
+  if (phase == 0) {
+    if (tiles) k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d, src);
+  } else if (tiles) {
+    k_scan_bins<WG><<<d.ntiles, WG, 0, st>>>(d, src ^ 1);
+  } else {
+    k_scan_bins<SCAN_SMALL_NT><<<1, SCAN_SMALL_NT, 0, st>>>(d, src ^ 1);
+  }
+}
+
 // Kernel k of the step of phase p (reads buffer src = (p + 1) mod 2,
 // accumulates into p); fused: the plain G2P is replaced by the G2P2G kernel,
 // which stores v and C when write_vc is set and takes the next step's sort
@@ -313,15 +329,19 @@ int launch_kernel(mpm_sim *sim, int k, hipStream_t st, int p, bool fused, bool w
   const SimDev &d = sim->d;
   switch (k) {
     case 0:
-      // (a small grid's bins are scanned by one workgroup, without tile totals)
-      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_tiles<<<d.ntiles, WG, 0, st>>>(d, src);
+      if (!d.sort_small) launch_scan(sim, st, src, 0);
       break;
     case 1:
-      if (d.nbins > SCAN_SMALL_NT * SCAN_PER) k_scan_bins<WG><<<d.ntiles, WG, 0, st>>>(d, src ^ 1);
-      else k_scan_bins<SCAN_SMALL_NT><<<1, SCAN_SMALL_NT, 0, st>>>(d, src ^ 1);
+      if (d.sort_small) {
+        // (nbins = 8^k: 8, 64, 512 or 4096 bins, in 1, 1, 2 or 16 rounds of 256)
+        if (d.nbins <= 256) k_sort_small<1><<<sim->grid_sort_small, 64, 0, st>>>(d, src);
+        else if (d.nbins <= 512) k_sort_small<2><<<sim->grid_sort_small, 64, 0, st>>>(d, src);
+        else k_sort_small<SMALL_SORT_BINS / 256><<<sim->grid_sort_small, 64, 0, st>>>(d, src);
+      }
+      else launch_scan(sim, st, src, 1);
       break;
     case 2:
-      k_scatter<<<sim->grid_scatter, 64, 0, st>>>(d, src);
+      if (!d.sort_small) k_scatter<<<sim->grid_scatter, 64, 0, st>>>(d, src);
       break;
     case 3:
       if (sim->p2g_wide) launch_p2g<NWIN_WIDE>(sim, st, src, p);
@@ -479,6 +499,16 @@ int launch_shapes(mpm_sim *sim) {
                     4 * ((int64_t)d.N >> KMIN_SHIFT) <= 3 * (int64_t)grid_w;
     if (sim->p2g_wide) sim->grid_p2g = grid_w;
   }
+  // A small scene whose bins fit k_sort_small's tables (and whose chunk
+  // indexes fit their 16 bits) sorts with it: scan and scatter in one kernel.
+  {
+    int occ_s = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_s, k_sort_small<SMALL_SORT_BINS / 256>, 64, 0) != hipSuccess ||
+        occ_s <= 0)
+      occ_s = 1;
+    sim->d.sort_small = sim->p2g_wide && d.nbins <= SMALL_SORT_BINS && d.max_chunks < 65536u ? 1 : 0;
+    sim->grid_sort_small = cus * occ_s;
+  }
   int occ_g = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_g, k_g2p<MPM_FIXED_COROTATED>, 64, 0) != hipSuccess || occ_g <= 0)
     occ_g = 16;
@@ -528,11 +558,13 @@ int init_state(mpm_sim *sim, const float *x0, const float *v0, const float *C0, 
   if (d.N > 0) {
     k_init<<<(d.N + WG - 1) / WG, WG, 0, st>>>(d, x0, v0, C0, F0, E_p);
     // one bucket pass to bring the initial state into bin order (buffer 1,
-    // whose chunk list the scan writes): the scans of a step that reads
-    // buffer 0 (phase 1)
-    launch_kernel(sim, 0, st, 1, false, false, -1);
-    launch_kernel(sim, 1, st, 1, false, false, -1);
+    // whose chunk list the scan writes): the scan of a step that reads
+    // buffer 0, and the bin cursors it sets
+    launch_scan(sim, st, 0, 0);
+    launch_scan(sim, st, 0, 1);
     k_scatter_init<<<sim->grid_particles, WG, 0, st>>>(d);
+    // (k_sort_small counts the movers into a bin from zero)
+    if (d.sort_small) k_zero_u32<<<zb, WG, 0, st>>>(d.bin_cursor, (size_t)d.nbins);
     sim->cur = 1;
   }
   return hipGetLastError() == hipSuccess ? MPM_OK : MPM_ERR_HIP;

@@ -41,6 +41,26 @@ union P2GShared {
 };
 static_assert(sizeof(P2GRankTables<NWIN>) <= sizeof(float4) * NWIN * PW3, "rank tables must fit the windows");
 
+// LDS of the small-chunk P2G: the windows and a per-cell count.
+struct P2GSmallShared {
+  float4 win[NWIN_WIDE * PW3];
+  uint32_t cnt[CB3];  // particles per cell of the chunk being ranked
+};
+
+// Zero NW windows: whole rows of 64 lanes, unrolled (a loop whose trip count
+// depends on the lane runs as a divergent loop, several times slower for a
+// single wavefront), then the partial row.  (The many-wavefront paths keep
+// the loop: unrolled, it raised their register count past an occupancy
+// step.)
+template <int NW>
+__device__ __forceinline__ void clear_windows(float4 *win) {
+  constexpr int N = NW * PW3;
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < N / 64; ++k) win[64 * k + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (N % 64 != 0 && lane < N % 64) win[64 * (N / 64) + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 
 // Base node b = floor(x/dx - 1/2), fractional offset f and quadratic
 // B-spline weights w[axis][o] of a position.
@@ -236,6 +256,107 @@ __device__ __forceinline__ void deposit_global(const SimDev &s, int a, const int
   }
 }
 
+// One round of up to 64 particles, one per lane: load the particle at
+// source slot i, store x, id, F (and the per-particle scalar) at slot dst,
+// apply the deferred deformation update, evaluate the stress, form the APIC
+// momentum and deposit it into the windows (tag: window and pass, or
+// MOVER_TAG).  Lanes with valid = false load a valid particle and store
+// nothing.  P2G writes x and id at dst; G2P reads x from the same slot,
+// without an index indirection, and leaves it: the position it advects to
+// is formed again here from x and its v.
+template <int MAT, bool HAS_E, bool FREE, int NW, bool RANK_PASS>
+__device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &in, const PBuf &out, bool pending, int acc,
+                                             int ox0, int oy0, int oz0, bool valid, uint32_t i, uint32_t tag,
+                                             uint32_t dst, float4 *win) {
+  const int lane = threadIdx.x;
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
+  const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
+  const uint32_t io = 4u * i, od = 4u * dst;  // byte offsets of the source and destination slots
+  float xp[3], vp[3], Cp[9];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    xp[a] = at_byte(in.x + a * Np, io);
+    vp[a] = at_byte(in.v + a * Np, io);
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) Cp[k] = stream_load(at_byte(in.C + k * Np, io));
+  // the pending advection of the G2P before (the same bits as its keys)
+  if (pending)
+#pragma unroll
+    for (int a = 0; a < 3; ++a) xp[a] = advanced(s, xp[a], vp[a]);
+  if (valid) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) at_byte(out.x + a * Np, od) = xp[a];
+    stream_store(at_byte(in.id, io), at_byte(out.id, od));
+  }
+
+  // Deferred deformation-gradient update, stress, APIC momentum.
+  float Fp[MAT == MPM_J_FLUID ? 1 : 9];
+#pragma unroll
+  for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
+  if (pending) update_F<MAT>(Fp, Cp, dt);
+  // the per-particle scalar: Young's modulus, or snow's log plastic volume
+  const float Es = HAS_E ? at_byte(in.E, io) : s.E;
+  const float E = MAT == MPM_SNOW ? s.E : Es;
+  float ap = Es;
+  float A[9];
+  uint32_t st = 0;
+  // sand, snow: the plasticity projection of the updated F, with the stress
+  if (MAT == MPM_SAND || MAT == MPM_SNOW) st = plastic_affine<MAT>(s, Fp, E, ap, Cp, A, pending);
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
+    if (HAS_E) stream_store(MAT == MPM_SNOW ? ap : E, at_byte(out.E, od));
+  }
+  if (MAT != MPM_SAND && MAT != MPM_SNOW) st = affine_momentum<MAT>(s, Fp, E, Cp, A);
+  if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
+  int b[3];
+  float f[3], w[3][3], q0[3], Ad[9];
+  particle_weights(xp, fn, b, f, w);
+  momentum_terms(mass, dx, vp, A, f, q0, Ad);
+  const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
+            lz = min(max(b[2] - oz0, 0), CB - 1);
+  const int li0 = (int)(tag % NW) * PW3 + (lz * PW + ly) * PW + lx;
+
+  // Passes: lanes conflict only when they share (window, cell).  With
+  // RANK_PASS the tag is the particle's rank r in its cell, which is its
+  // occurrence index in window r % NW: its pass is r / NW.  Otherwise the
+  // lane's pass is its occurrence index among the earlier lanes of the
+  // round with the same (window, cell) (ballot-matched), which gives the
+  // fewest conflict-free passes; lanes of one super-rank never share
+  // (window, cell), so this is at most one pass per super-rank.
+  // (a mover's stencil is outside the window: it takes no pass)
+  const bool mov = FREE && tag == MOVER_TAG;
+  const bool inwin = valid && !mov;
+  uint32_t pass_id;
+  if (RANK_PASS) {
+    pass_id = tag / NW;
+  } else {
+    const uint32_t wc = (tag % NW) * (uint32_t)CB3 + (uint32_t)((lz * CB + ly) * CB + lx);
+    uint64_t peers = __ballot(inwin);
+    constexpr int WC_BITS = NW == 2 ? 7 : (NW == 4 ? 8 : 9);  // 6 cell bits + log2(NW)
+    static_assert(NW == 2 || NW == 4 || NW == 8, "window counts with a bit width here");
+#pragma unroll
+    for (int k = 0; k < WC_BITS; ++k) {
+      const uint64_t bk = __ballot((wc >> k) & 1u);
+      peers &= ((wc >> k) & 1u) ? bk : ~bk;
+    }
+    pass_id = (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
+  }
+  // A mover (only in a step without a sort; rare) deposits directly.
+  if (FREE && valid && mov) deposit_global(s, acc, b, w, q0, Ad);
+  bool todo = inwin;
+  for (uint32_t pnow = 0;; ++pnow) {
+    // (occurrence indices of a key are 0, 1, ..., so no lane waits for a
+    // pass after an empty one)
+    if (__ballot(todo && pass_id == pnow) == 0ull) break;
+    if (todo && pass_id == pnow) {
+      deposit_window(win, li0, w, q0, Ad, mass);
+      todo = false;
+    }
+  }
+}
+
 // The P2G of one step.  FREE: a step without a sort (free-zone policy), with
 // the paths for particles outside their chunk's bin; the per-step-sort
 // instance has none of that code.
@@ -258,7 +379,6 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
   // and a particle whose key names another bin is outside the chunk's window
   // (a mover: deposited with direct global atomics).
   constexpr bool sorted = !FREE;
-  const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
 
   // A chunk's sorted source indices and cells are loaded one chunk ahead,
   // during the previous chunk's pass B, so pass A starts with them in
@@ -430,90 +550,9 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       const uint32_t tag = ordtag[at];
       // The new state is stored in this processing order, (bin, super-rank,
       // window, cell): the next step's gathers then run over nearly
-      // consecutive addresses.  P2G writes x and id there; G2P reads x from
-      // the same slot, without an index indirection, and leaves it: the
-      // position it advects to is formed again here from x and its v.
-      const uint32_t dst = start + at;
-      const uint32_t io = 4u * i, od = 4u * dst;  // byte offsets of the source and destination slots
-      float xp[3], vp[3], Cp[9];
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        xp[a] = at_byte(in.x + a * Np, io);
-        vp[a] = at_byte(in.v + a * Np, io);
-      }
-#pragma unroll
-      for (int k = 0; k < 9; ++k) Cp[k] = stream_load(at_byte(in.C + k * Np, io));
-      // the pending advection of the G2P before (the same bits as its keys)
-      if (pending)
-#pragma unroll
-        for (int a = 0; a < 3; ++a) xp[a] = advanced(s, xp[a], vp[a]);
-      if (valid) {
-#pragma unroll
-        for (int a = 0; a < 3; ++a) at_byte(out.x + a * Np, od) = xp[a];
-        stream_store(at_byte(in.id, io), at_byte(out.id, od));
-      }
-
-      // Deferred deformation-gradient update, stress, APIC momentum.
-      float Fp[MAT == MPM_J_FLUID ? 1 : 9];
-#pragma unroll
-      for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
-      if (pending) update_F<MAT>(Fp, Cp, dt);
-      // the per-particle scalar: Young's modulus, or snow's log plastic volume
-      const float Es = HAS_E ? at_byte(in.E, io) : s.E;
-      const float E = MAT == MPM_SNOW ? s.E : Es;
-      float ap = Es;
-      float A[9];
-      uint32_t st = 0;
-      // sand, snow: the plasticity projection of the updated F, with the stress
-      if (MAT == MPM_SAND || MAT == MPM_SNOW) st = plastic_affine<MAT>(s, Fp, E, ap, Cp, A, pending);
-      if (valid) {
-#pragma unroll
-        for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) stream_store(Fp[k], at_byte(out.F + k * Np, od));
-        if (HAS_E) stream_store(MAT == MPM_SNOW ? ap : E, at_byte(out.E, od));
-      }
-      if (MAT != MPM_SAND && MAT != MPM_SNOW) st = affine_momentum<MAT>(s, Fp, E, Cp, A);
-      if (st && valid) flag_status(s, st, (st & MPM_STATUS_INVERTED) ? 2 : 0);
-      int b[3];
-      float f[3], w[3][3], q0[3], Ad[9];
-      particle_weights(xp, fn, b, f, w);
-      momentum_terms(mass, dx, vp, A, f, q0, Ad);
-      const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
-                lz = min(max(b[2] - oz0, 0), CB - 1);
-      const int li0 = (int)(tag % NW) * PW3 + (lz * PW + ly) * PW + lx;
-
-      // Passes: lanes conflict only when they share (window, cell).  The
-      // lane's pass is its occurrence index among the earlier lanes of the
-      // round with the same (window, cell) (ballot-matched, 7 bits), which
-      // gives the fewest conflict-free passes; lanes of one super-rank never
-      // share (window, cell), so this is at most one pass per super-rank.
-      // (a mover's stencil is outside the window: it takes no pass)
-      const bool mov = FREE && tag == MOVER_TAG;
-      const bool inwin = valid && !mov;
-      uint32_t pass_id;
-      {
-        const uint32_t wc = (tag % NW) * (uint32_t)CB3 + (uint32_t)((lz * CB + ly) * CB + lx);
-        uint64_t peers = __ballot(inwin);
-        constexpr int WC_BITS = NW == 2 ? 7 : (NW == 4 ? 8 : 9);  // 6 cell bits + log2(NW)
-        static_assert(NW == 2 || NW == 4 || NW == 8, "window counts with a bit width here");
-#pragma unroll
-        for (int k = 0; k < WC_BITS; ++k) {
-          const uint64_t bk = __ballot((wc >> k) & 1u);
-          peers &= ((wc >> k) & 1u) ? bk : ~bk;
-        }
-        pass_id = (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
-      }
-      // A mover (only in a step without a sort; rare) deposits directly.
-      if (FREE && valid && mov) deposit_global(s, acc, b, w, q0, Ad);
-      bool todo = inwin;
-      for (uint32_t pnow = 0;; ++pnow) {
-        // (occurrence indices of a key are 0, 1, ..., so no lane waits for a
-        // pass after an empty one)
-        if (__ballot(todo && pass_id == pnow) == 0ull) break;
-        if (todo && pass_id == pnow) {
-          deposit_window(sm.win, li0, w, q0, Ad, mass);
-          todo = false;
-        }
-      }
+      // consecutive addresses.
+      p2g_particle<MAT, HAS_E, FREE, NW, false>(s, in, out, pending, acc, ox0, oy0, oz0, valid, i, tag, start + at,
+                                                sm.win);
     }
     // The next chunk's prefetched sources and cells are waited for here,
     // before the flush: a vector load is complete only once every vector
@@ -527,14 +566,142 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
   }
 }
 
+// The P2G of one step for chunks of at most 64 particles (small scenes,
+// NWIN_WIDE windows): one round per chunk, so the ordering needs no tables
+// in LDS.  Each lane keeps its particle; its rank r in its cell gives its
+// window (r % NW), its pass (r / NW) and its storage slot, the position of
+// (r, cell) in (rank, cell) order -- the (super-rank, window, cell) order of
+// the general path.  A single wavefront's step time is its chain of
+// dependent operations: the windows are cleared while the first chunk's
+// loads are in flight, and again after a flush only if another chunk
+// follows.  Requires chunks of at most 64 particles (the scan makes them so
+// when the scene takes this path).
+template <int MAT, bool HAS_E, bool FREE>
+__device__ __forceinline__ void p2g_step_small(const SimDev &s, int src, int acc, P2GSmallShared &sm) {
+  constexpr int NW = NWIN_WIDE;
+  const PBuf in = s.buf[src], out = s.buf[src ^ 1];
+  const int lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t Np = (uint32_t)s.Np;
+  const uint32_t q = blockIdx.x & (NQ - 1), wq = blockIdx.x / NQ, nwq = gridDim.x / NQ;
+  const uint32_t nch = s.ctr[CTR_NCHUNKS + (src ^ 1)];
+  const uint4 *chunks = s.chunks[src ^ 1];
+  const uint32_t qbeg = (uint32_t)(((uint64_t)nch * q) / NQ), qend = (uint32_t)(((uint64_t)nch * (q + 1)) / NQ);
+  const bool pending = s.ctr[CTR_PENDING] != 0u;
+  constexpr bool sorted = !FREE;
+  // a chunk's source index and cell (or, without a sort, whole key) per
+  // lane, loaded one chunk ahead
+  uint32_t pf_src = 0xFFFFFFFFu, pf_cell = 0u;
+  auto prefetch = [&](const uint4 &chrec) {
+    const uint32_t pstart = chrec.x, pcount = min(chrec.y, 64u);
+    pf_src = 0xFFFFFFFFu;
+    pf_cell = 0u;
+    if ((uint32_t)lane < pcount) {
+      pf_src = sorted ? s.perm[pstart + lane] : pstart + (uint32_t)lane;
+      pf_cell = sorted ? (uint32_t)s.cellp[pstart + lane] : s.key[pstart + lane];
+    }
+  };
+  clear_accumulator(s, (acc + 2) & (NACC - 1));
+  // (k_sort_small) the bins' counts, stayer counts and mover counters, which
+  // every workgroup of this step's sort read, cleared for this step's G2P
+  if (!FREE && s.sort_small)
+    for (uint32_t b = blockIdx.x * 64u + (uint32_t)lane; b < (uint32_t)s.nbins; b += gridDim.x * 64u) {
+      s.bin_count[b] = 0u;
+      s.stay_count[b] = 0u;
+      s.bin_cursor[b] = 0u;
+    }
+  uint4 ch_next = make_uint4(0u, 0u, 0u, 0u);
+  if (qbeg + wq < qend) {
+    ch_next = load_record(chunks + qbeg + wq);
+    prefetch(ch_next);
+  }
+  clear_windows<NW>(sm.win);
+  for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
+    const uint4 ch = ch_next;
+    const uint32_t start = ch.x, count = min(ch.y, 64u), bin = ch.z;
+    const int ox0 = (int)compact3(bin) * CB, oy0 = (int)compact3(bin >> 1) * CB, oz0 = (int)compact3(bin >> 2) * CB;
+    const bool has_next = c + nwq < qend;
+    if (has_next) ch_next = load_record(chunks + c + nwq);
+    const bool in_chunk = (uint32_t)lane < count;
+    const uint32_t kc = pf_cell;
+    const bool mov = FREE && in_chunk && (kc & ((1u << KEY_CELL_SHIFT) - 1u)) != bin;
+    const uint32_t cell = (sorted ? kc : (kc >> KEY_CELL_SHIFT)) & (uint32_t)(CB3 - 1);
+    const bool ranked = in_chunk && !mov;
+    // (lanes past the count load the chunk's first particle and store nothing)
+    const uint32_t i = in_chunk ? min(pf_src, Np - 1u) : __builtin_amdgcn_readfirstlane(min(pf_src, Np - 1u));
+    // Rank within the cell: lanes with the same cell matched bit by bit.
+    uint64_t peers = __ballot(ranked);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const uint64_t bk = __ballot((cell >> k) & 1u);
+      peers &= ((cell >> k) & 1u) ? bk : ~bk;
+    }
+    const uint32_t r = (uint32_t)__popcll(peers & below);
+    // Particles per cell, lane = cell: each group's lowest lane writes its
+    // size (the wavefront's LDS accesses execute in issue order).
+    sm.cnt[lane] = 0u;
+    __asm__ __volatile__("" ::: "memory");
+    if (ranked && r == 0u) sm.cnt[cell] = (uint32_t)__popcll(peers);
+    __asm__ __volatile__("" ::: "memory");
+    const uint32_t cnt = sm.cnt[lane];
+    // Lane k of (mlo, mhi) = the cells holding a particle of rank k; lane k
+    // of pre = the position of the first of them.
+    uint32_t mlo = 0u, mhi = 0u, pre = 0u, run = 0u;
+    for (uint32_t k = 0; k < 64u; ++k) {
+      const uint64_t m = __ballot(cnt > k);
+      if (m == 0ull) break;
+      if ((uint32_t)lane == k) {
+        mlo = (uint32_t)m;
+        mhi = (uint32_t)(m >> 32);
+        pre = run;
+      }
+      run += (uint32_t)__popcll(m);
+    }
+    const int rq = ranked ? (int)r : 0;
+    const uint64_t gm = ((uint64_t)(uint32_t)__shfl((int)mhi, rq) << 32) | (uint32_t)__shfl((int)mlo, rq);
+    uint32_t pos = (uint32_t)__shfl((int)pre, rq) + (uint32_t)__popcll(gm & ((1ull << cell) - 1ull));
+    if (FREE) {
+      // movers go after the ranked particles
+      const uint64_t mm = __ballot(mov);
+      if (mov) pos = run + (uint32_t)__popcll(mm & below);
+    }
+    if (has_next) prefetch(ch_next);
+    p2g_particle<MAT, HAS_E, FREE, NW, true>(s, in, out, pending, acc, ox0, oy0, oz0, in_chunk, i,
+                                             mov ? (uint32_t)MOVER_TAG : r, start + pos, sm.win);
+    // (the next chunk's loads are waited for before the flush: a vector load
+    // is complete only once every vector operation issued before it is)
+    __asm__ __volatile__("" ::"v"(pf_src), "v"(pf_cell));
+    flush_windows<NW>(s, sm.win, ox0, oy0, oz0, acc);
+    if (has_next) {
+      __asm__ __volatile__("" ::: "memory");
+      clear_windows<NW>(sm.win);
+    }
+  }
+}
+
 template <int MAT, bool HAS_E, int NW>
 // (snow: at least 4 waves per SIMD, which holds it at 128 VGPRs with no spill;
 // measured 13% faster than its unconstrained 130 VGPRs at 3 waves)
 __global__ __launch_bounds__(64, (MAT == MPM_SNOW && NW == NWIN) ? 4 : 1) void k_p2g(SimDev s, int src, int acc) {
-  __shared__ P2GShared<NW> sm;
-  __shared__ uint32_t order[KMAX];  // source index of each processing position
-  __shared__ uint8_t ordtag[KMAX];  // super-rank * NW + window of each position (or MOVER_TAG)
+  if constexpr (NW == NWIN_WIDE) {
+    // (k_sort_small, which only small scenes use, leaves these to the P2G:
+    // all its workgroups read them)
+    if (s.sort_small && blockIdx.x == 0 && threadIdx.x == 0) {
+      s.ctr[CTR_MOVSNAP] = s.ctr[CTR_MOVERS];
+      s.ctr[CTR_MOVERS] = 0u;
+      s.ctr[CTR_SINCE] = s.ctr[CTR_SORT + src] != 0u ? 0u : s.ctr[CTR_SINCE] + 1u;
+    }
+  }
   if (s.ctr[CTR_LOOK + src] != 0u) return;  // done by the fused kernel of the step before
-  if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false, NW>(s, src, acc, sm, order, ordtag);
-  else p2g_step<MAT, HAS_E, true, NW>(s, src, acc, sm, order, ordtag);
+  if constexpr (NW == NWIN_WIDE) {
+    __shared__ P2GSmallShared sm;
+    if (s.ctr[CTR_SORT + src] != 0u) p2g_step_small<MAT, HAS_E, false>(s, src, acc, sm);
+    else p2g_step_small<MAT, HAS_E, true>(s, src, acc, sm);
+  } else {
+    __shared__ P2GShared<NW> sm;
+    __shared__ uint32_t order[KMAX];  // source index of each processing position
+    __shared__ uint8_t ordtag[KMAX];  // super-rank * NW + window of each position (or MOVER_TAG)
+    if (s.ctr[CTR_SORT + src] != 0u) p2g_step<MAT, HAS_E, false, NW>(s, src, acc, sm, order, ordtag);
+    else p2g_step<MAT, HAS_E, true, NW>(s, src, acc, sm, order, ordtag);
+  }
 }

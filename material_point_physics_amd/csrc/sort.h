@@ -321,15 +321,18 @@ __global__ __launch_bounds__(WG) void k_scatter_init(SimDev s) {
 // Position of the bin's stayer number j (in their previous order) in the
 // bin's new slot range.  A dense bin's stayers fill several chunks of K =
 // 2^kshift; each chunk was stored in P2G's (super-rank, window, cell) order,
-// so its rounds of 64 hold about one particle per cell, while its cells as a
-// whole may be far from balanced (particles created cell by cell stay
-// together).  For Cp = 2 or 4 full chunks (the most with blocks of at least
-// one round), the blocks are transposed -- new chunk q takes block q of every
-// old chunk -- so each new chunk draws evenly from all of them and needs
-// fewer read-modify-write passes.  Other stayers keep their order.
+// so a run of consecutive slots holds about one particle per cell, while a
+// chunk's cells as a whole may be far from balanced (particles created cell
+// by cell stay together).  For Cp = 2, 4 or 8 full chunks, the blocks are
+// transposed -- new chunk q takes block q of every old chunk -- so each new
+// chunk draws evenly from all of them and needs fewer read-modify-write
+// passes.  Blocks hold at least one round of 64 particles when a chunk has
+// several rounds, and at least 8 particles in one-round chunks.  Other
+// stayers keep their order.
 __device__ __forceinline__ uint32_t stayer_slot(uint32_t j, uint32_t stay, uint32_t kshift) {
-  const uint32_t full = stay >> kshift, cap = 1u << (kshift - KMIN_SHIFT);  // blocks >= 64 particles
-  const uint32_t cp = min(full, cap) >= 4u ? 4u : (min(full, cap) >= 2u ? 2u : 1u);
+  const uint32_t full = stay >> kshift, cap = kshift == (uint32_t)KMIN_SHIFT ? 8u : 1u << (kshift - KMIN_SHIFT);
+  const uint32_t f = min(full, cap);
+  const uint32_t cp = f >= 8u ? 8u : (f >= 4u ? 4u : (f >= 2u ? 2u : 1u));
   if (cp == 1u || j >= (cp << kshift)) return j;
   const uint32_t K = 1u << kshift, B = K / cp;
   const uint32_t m = j >> kshift, r = j & (K - 1u), q = r / B, i = r % B;
@@ -401,6 +404,141 @@ __global__ __launch_bounds__(64) void k_scatter(SimDev s, int src) {
         s.perm[slot] = start + r;
         s.cellp[slot] = (uint8_t)(kc[j] >> KEY_CELL_SHIFT);
       }
+    }
+  }
+}
+
+// ----------------------------------------------------- small-scene sort
+// For a grid of at most SMALL_SORT_BINS bins (and chunks of 64), the scan
+// and the scatter are one kernel.  Every workgroup forms the whole slot and
+// chunk prefix of the bins itself -- a few KB of counts, and a few
+// wavefront scans -- into LDS tables, so that no kernel boundary separates
+// the counts from the placement: a small scene's step time is a chain of
+// latencies, and a boundary costs about a microsecond.  Workgroup g writes
+// the new chunk records of every G-th row of 64 bins and places the
+// particles of every G-th old chunk, as k_scatter does (stayers in their
+// previous order, transposed by stayer_slot; movers after the stayers of
+// their bin, through a per-bin counter that starts at zero).  The counts,
+// stayer counts and mover counters are read by every workgroup, so the
+// step's P2G clears them (and updates the control words the one-workgroup
+// scan updates); without a sort this kernel clears the counts itself.
+constexpr int SMALL_SORT_BINS = 4096;
+
+// ROUNDS = ceil(nbins / 256): the rounds of the prefix, unrolled (the bin
+// counts stay in registers).
+template <int ROUNDS>
+__global__ __launch_bounds__(64) void k_sort_small(SimDev s, int src) {
+  __shared__ uint4 tstart4[SMALL_SORT_BINS / 4];  // first slot of each bin in the new layout
+  __shared__ uint2 tchunk4[SMALL_SORT_BINS / 4];  // first chunk of each bin (16 bits each)
+  const int lay = src ^ 1;
+  const int lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t nbins = (uint32_t)s.nbins, kshift = (uint32_t)s.chunk_shift, K = 1u << kshift;
+  const uint32_t G = gridDim.x, g = blockIdx.x;
+  const uint32_t nch_old = s.ctr[CTR_NCHUNKS + src];
+  const uint4 *old = s.chunks[src];
+  const bool sort = decide_sort(s, src);
+  // (a preset decision is already in the word, which other workgroups read)
+  if (g == 0 && lane == 0 && s.ctr[CTR_PRESET + src] == 0u) s.ctr[CTR_SORT + src] = sort ? 1u : 0u;
+  if (!sort) {
+    // Layout lay repeats layout src: its chunk list is copied, and the
+    // counts are cleared for this step's G2P.
+    for (uint32_t c = g * 64u + (uint32_t)lane; c < nch_old; c += G * 64u) s.chunks[lay][c] = old[c];
+    for (uint32_t b = g * 64u + (uint32_t)lane; b < nbins; b += G * 64u) {
+      s.bin_count[b] = 0u;
+      s.stay_count[b] = 0u;
+    }
+    if (g == 0 && lane == 0) s.ctr[CTR_NCHUNKS + lay] = nch_old;
+    return;
+  }
+  // (a workgroup with no old chunk and no row of bins has nothing to do)
+  if (g >= nch_old && 64u * g >= nbins) return;
+  // This workgroup's first old chunk and its keys, and the count of the
+  // bin whose records it writes first, are requested before the tables.
+  uint4 rec = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t key = 0u, prev_bin = 0xFFFFFFFFu;
+  if (g < nch_old) {
+    rec = load_record(old + g);
+    if (g > 0u) prev_bin = load_record(old + g - 1u).z;
+    if ((uint32_t)lane < min(rec.y, 64u)) key = s.key[rec.x + (uint32_t)lane];
+  }
+  const uint32_t brow = 64u * g + (uint32_t)lane;
+  const uint32_t crow = brow < nbins ? s.bin_count[brow] : 0u;
+  // Slot and chunk prefix: rounds of 256 bins, four consecutive bins per lane.
+  static_assert(ROUNDS * 256 <= SMALL_SORT_BINS, "tables hold SMALL_SORT_BINS bins");
+  // (nbins = 8^k >= 8 is a multiple of 4; the loads are unconditional, from
+  // bin 0 past the end, so that they are all in flight together)
+  uint4 c4[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const uint32_t b = 256u * (uint32_t)r + 4u * (uint32_t)lane;
+    c4[r] = *reinterpret_cast<const uint4 *>(s.bin_count + (b < nbins ? b : 0u));
+  }
+  uint32_t sbase = 0u, cbase = 0u;  // slots and chunks of the bins of the earlier rounds
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const bool in = 256u * (uint32_t)r + 4u * (uint32_t)lane < nbins;
+    const uint4 c = make_uint4(in ? c4[r].x : 0u, in ? c4[r].y : 0u, in ? c4[r].z : 0u, in ? c4[r].w : 0u);
+    const uint32_t p0 = padded(c.x), p1 = padded(c.y), p2 = padded(c.z), p3 = padded(c.w);
+    const uint32_t k0 = (c.x + K - 1u) >> kshift, k1 = (c.y + K - 1u) >> kshift, k2 = (c.z + K - 1u) >> kshift,
+                   k3 = (c.w + K - 1u) >> kshift;
+    const uint32_t ps = p0 + p1 + p2 + p3, ks = k0 + k1 + k2 + k3;
+    const uint32_t pi = wave_incl_scan(ps), ki = wave_incl_scan(ks);
+    const uint32_t pe = sbase + pi - ps, ke = cbase + ki - ks;
+    tstart4[64 * r + lane] = make_uint4(pe, pe + p0, pe + p0 + p1, pe + p0 + p1 + p2);
+    tchunk4[64 * r + lane] = make_uint2(ke | ((ke + k0) << 16), (ke + k0 + k1) | ((ke + k0 + k1 + k2) << 16));
+    sbase += (uint32_t)__builtin_amdgcn_readlane((int)pi, 63);
+    cbase += (uint32_t)__builtin_amdgcn_readlane((int)ki, 63);
+  }
+  __syncthreads();
+  const uint32_t *tstart = reinterpret_cast<const uint32_t *>(tstart4);
+  const uint16_t *tchunk = reinterpret_cast<const uint16_t *>(tchunk4);
+  // New chunk records of rows g, g + G, ... of 64 bins.
+  for (uint32_t b = brow; b - (uint32_t)lane < nbins; b += 64u * G) {
+    const uint32_t cnt = b == brow ? crow : (b < nbins ? s.bin_count[b] : 0u);
+    if (b < nbins && cnt > 0u) {
+      const uint32_t p0 = tstart[b], k0 = tchunk[b];
+      for (uint32_t j = 0, off = 0; off < cnt; ++j, off += K)
+        s.chunks[lay][k0 + j] = make_uint4(p0 + off, min(K, cnt - off), b, min(K, cnt - off));
+    }
+  }
+  if (g == 0 && lane == 0) s.ctr[CTR_NCHUNKS + lay] = cbase;
+  // Placement of the particles of old chunks g, g + G, ...
+  for (uint32_t c = g; c < nch_old; c += G) {
+    if (c != g) {
+      rec = load_record(old + c);
+      prev_bin = load_record(old + c - 1u).z;
+      key = (uint32_t)lane < min(rec.y, 64u) ? s.key[rec.x + (uint32_t)lane] : 0u;
+    }
+    const uint32_t start = rec.x, count = min(rec.y, 64u), bin = rec.z;
+    const uint32_t bstay = min(s.stay_count[bin], s.bin_count[bin]);
+    // stayers of the bin's earlier chunks (a bin's chunks are consecutive;
+    // nearly always none, or a few records)
+    uint32_t base = 0u;
+    for (uint32_t c0 = c; prev_bin == bin && c0 > 0u;) {
+      const uint32_t lo = c0 > 64u ? c0 - 64u : 0u;
+      const uint32_t cj = lo + (uint32_t)lane;
+      uint4 r = make_uint4(0u, 0u, 0xFFFFFFFFu, 0u);
+      if (cj < c0) r = old[cj];
+      const bool same = cj < c0 && r.z == bin;
+      uint32_t add = same ? r.w : 0u;
+      for (int d = 32; d >= 1; d >>= 1) add += (uint32_t)__shfl_xor((int)add, d);
+      base += add;
+      if (__ballot(same) != ~0ull || lo == 0u) break;
+      c0 = lo;
+    }
+    const bool valid = (uint32_t)lane < count;
+    const uint32_t kb = min(key & ((1u << KEY_CELL_SHIFT) - 1u), nbins - 1u);
+    const bool stay = valid && kb == bin;
+    const uint64_t sm = __ballot(stay);
+    uint32_t slot = tstart[bin] + stayer_slot(base + (uint32_t)__popcll(sm & below), bstay, kshift);
+    if (__ballot(valid && !stay) != 0ull) {
+      const uint32_t off = wave_aggregated_increment(s.bin_cursor, kb, valid && !stay);
+      if (valid && !stay) slot = tstart[kb] + min(s.stay_count[kb], s.bin_count[kb]) + off;
+    }
+    if (valid && slot < (uint32_t)s.Np) {
+      s.perm[slot] = start + (uint32_t)lane;
+      s.cellp[slot] = (uint8_t)(key >> KEY_CELL_SHIFT);
     }
   }
 }
