@@ -349,8 +349,9 @@ __device__ __forceinline__ void g2p_handoff(const SimDev &s, int lay) {
   }
 }
 
-// G2P of a step that reads buffer src (accumulator a): writes x, v, C in
-// place in layout src ^ 1 and the next step's bin keys and counts.
+// G2P of a step that reads buffer src (accumulator a): writes v and C in
+// place in layout src ^ 1 (x stays; the next P2G advances it) and the next
+// step's bin keys and counts.
 template <int MAT>
 __global__ __launch_bounds__(64, 5) void k_g2p(SimDev s, int src, int a) {
   __shared__ float4 win[PW3];

@@ -3,6 +3,7 @@
 Usage:
     python -m material_point_physics_amd.profiling <results.db> [--kernels k_] [--title TEXT]
     python -m material_point_physics_amd.profiling <fetch.db> --write-db <write.db>
+    python -m material_point_physics_amd.profiling <rdreq.db> --request-write-db <wrreq.db>
     python -m material_point_physics_amd.profiling <trace.db> --api-audit
 
 Prints, per kernel: number of dispatches, average / median / total duration
@@ -85,11 +86,19 @@ def main():
     ap.add_argument("--kernels", default="")
     ap.add_argument("--title", default="")
     ap.add_argument("--write-db", default="", help="with a FETCH_SIZE db: print copy-calibrated traffic")
+    ap.add_argument("--request-write-db", default="",
+                    help="with a TCC_EA0_RDREQ/RDREQ_32B/BUBBLE db: print the request-size traffic range, "
+                         "the writes from this TCC_EA0_WRREQ/WRREQ_64B db")
     ap.add_argument("--api-audit", action="store_true",
                     help="with a --hip-trace --marker-trace db: HIP calls inside the timed range")
     a = ap.parse_args()
     if a.api_audit:
         print(api_audit_text(a.db, a.title))
+        return
+    if a.request_write_db:
+        for k, v in request_traffic(a.db, a.request_write_db, a.kernels or "k_").items():
+            print(f"requests {k} read_bytes=[{v['read_lo']:.6g}, {v['read_hi']:.6g}] write_bytes={v['write']:.6g} "
+                  f"total_bytes=[{v['total_lo']:.6g}, {v['total_hi']:.6g}] ea_atomics={v['atomics']:.6g}")
         return
     if a.write_db:
         t = traffic(a.db, a.write_db, a.kernels or "k_")
@@ -139,6 +148,37 @@ def traffic(fetch_db: str, write_db: str, kernels: str = "k_"):
         w = wc.get(k, {}).get("WRITE_SIZE", 0.0) * wk * 1024
         out[k] = {"fetch_bytes": f, "write_bytes": w, "total_bytes": f + w}
     return {"fetch_factor": fk, "write_factor": wk, "kernels": out}
+
+
+def request_traffic(read_db: str, write_db: str, kernels: str = "k_"):
+    """Per-kernel HBM bytes per dispatch (median) from the request counters
+    of the L2-to-fabric interface, without a calibration factor:
+      reads: TCC_EA0_RDREQ_sum requests, of which TCC_EA0_RDREQ_32B_sum carry
+             32 B and TCC_BUBBLE_sum 128 B; the rest carry 64 or 128 B (no
+             counter tells them apart), so the read bytes lie in
+             [32 R32 + 64 (R - R32 - B128) + 128 B128,  32 R32 + 128 (R - R32)]
+             -- the lower end is rocprofv3's FETCH_SIZE;
+      writes: TCC_EA0_WRREQ_sum transactions of 32 or 64 B, of which
+             TCC_EA0_WRREQ_64B_sum carry 64 B (WRITE_SIZE), atomics included.
+    A streaming copy's reads sit at the upper end (one request per 128-byte
+    line), which is why a FETCH_SIZE calibrated on the copy is this range's
+    upper end."""
+    rc = kernel_counters(read_db)
+    wc = kernel_counters(write_db)
+    out = {}
+    for k in sorted(set(rc) | set(wc)):
+        if kernels and kernels not in k:
+            continue
+        r = rc.get(k, {})
+        R, R32, B = r.get("TCC_EA0_RDREQ_sum", 0.0), r.get("TCC_EA0_RDREQ_32B_sum", 0.0), r.get("TCC_BUBBLE_sum", 0.0)
+        w = wc.get(k, {})
+        W, W64 = w.get("TCC_EA0_WRREQ_sum", 0.0), w.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+        lo = 32 * R32 + 64 * (R - R32 - B) + 128 * B
+        hi = 32 * R32 + 128 * (R - R32)
+        wb = 32 * (W - W64) + 64 * W64
+        out[k] = {"read_lo": lo, "read_hi": hi, "write": wb, "total_lo": lo + wb, "total_hi": hi + wb,
+                  "atomics": w.get("TCC_EA0_ATOMIC_sum", 0.0)}
+    return out
 
 
 # ------------------------------------------------------- host-API audit
