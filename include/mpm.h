@@ -289,6 +289,16 @@ int64_t mpm_steps_taken(const mpm_sim *sim);
 int32_t mpm_num_kernels(void);
 const char *mpm_kernel_name(int32_t k);
 
+/* The launch configuration chosen at creation for the scene's size (the
+ * page's kernel-count principle and its mapping of particles to thread
+ * blocks): out[0] = particles per chunk (64, 128 or 256), out[1] = P2G
+ * accumulation windows per wavefront (2, or 8 for a small scene), out[2] =
+ * kernels of the step's sort (1: the small-scene sort that scans and scatters
+ * in one kernel; 2: a one-workgroup scan and the scatter; 3: tile totals,
+ * scan and scatter).  Host-only, caller-owned out (3 entries).
+ * MPM_ERR_INVALID_ARG for a NULL argument. */
+int mpm_launch_config(const mpm_sim *sim, int32_t *out);
+
 /* Measurement helper, for per-kernel time breakdowns like those of the page's
  * ablation study (§6.2): run n_steps steps eagerly (the same kernels and launch
  * shapes as the graph), bracketing every kernel with HIP events on `stream`,

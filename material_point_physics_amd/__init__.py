@@ -44,7 +44,8 @@ MPM_STATUS_WORDS = 8
 EXPORTS = ("mpm_workspace_bytes", "mpm_create", "mpm_step", "mpm_set_sort_policy", "mpm_set_fused_steps",
            "mpm_read_particles", "mpm_run_noalloc", "mpm_read_plastic_state",
            "mpm_read_grid",
-           "mpm_status", "mpm_steps_taken", "mpm_num_kernels", "mpm_kernel_name", "mpm_step_profiled",
+           "mpm_status", "mpm_steps_taken", "mpm_num_kernels", "mpm_kernel_name", "mpm_launch_config",
+           "mpm_step_profiled",
            "mpm_destroy", "mpm_error_string")
 
 
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
     L.mpm_num_kernels.restype = i32
     L.mpm_kernel_name.argtypes = [i32]
     L.mpm_kernel_name.restype = ctypes.c_char_p
+    L.mpm_launch_config.argtypes = [vp, ctypes.POINTER(i32)]
+    L.mpm_launch_config.restype = ctypes.c_int
     L.mpm_step_profiled.argtypes = [vp, i32, vp, ctypes.POINTER(ctypes.c_float)]
     L.mpm_step_profiled.restype = ctypes.c_int
     L.mpm_destroy.argtypes = [vp]
@@ -218,6 +221,14 @@ def mpm_kernel_name(k: int) -> str:
     return r.decode() if r else None
 
 
+def mpm_launch_config(sim: int) -> dict:
+    """The launch configuration chosen at creation: particles per chunk, P2G
+    windows per wavefront, kernels of the step's sort."""
+    buf = (ctypes.c_int32 * 3)()
+    _check(lib().mpm_launch_config(sim, buf), "mpm_launch_config")
+    return {"chunk": int(buf[0]), "p2g_windows": int(buf[1]), "sort_kernels": int(buf[2])}
+
+
 def mpm_step_profiled(sim: int, n_steps: int, stream=None):
     """Returns the per-kernel elapsed milliseconds summed over n_steps."""
     nk = mpm_num_kernels()
@@ -274,6 +285,9 @@ class Simulation:
                                      self.stream)
         self.stream.synchronize()  # inputs may be released after this
         del x0, v0, C0, F0, E0
+
+    def launch_config(self) -> dict:
+        return mpm_launch_config(self.handle)
 
     def step(self, k: int = 1):
         mpm_step(self.handle, k, self.stream)

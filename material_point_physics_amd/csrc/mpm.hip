@@ -703,6 +703,14 @@ int mpm_set_sort_policy(mpm_sim *sim, int32_t max_interval, int64_t mover_budget
   return mark(sim, static_cast<hipStream_t>(stream));
 }
 
+int mpm_launch_config(const mpm_sim *sim, int32_t *out) {
+  if (!sim || !out) return MPM_ERR_INVALID_ARG;
+  out[0] = 1 << sim->d.chunk_shift;
+  out[1] = sim->p2g_wide ? NWIN_WIDE : NWIN;
+  out[2] = sim->d.sort_small ? 1 : (sim->d.nbins > SCAN_SMALL_NT * SCAN_PER ? 3 : 2);
+  return MPM_OK;
+}
+
 int mpm_step_profiled(mpm_sim *sim, int32_t n_steps, void *stream, float *kernel_ms) {
   if (!sim || n_steps < 0 || !kernel_ms) return MPM_ERR_INVALID_ARG;
   if (sim->d.N == 0) {
