@@ -264,22 +264,48 @@ __device__ __forceinline__ void deposit_global(const SimDev &s, int a, const int
 // nothing.  P2G writes x and id at dst; G2P reads x from the same slot,
 // without an index indirection, and leaves it: the position it advects to
 // is formed again here from x and its v.
-template <int MAT, bool HAS_E, bool FREE, int NW, bool RANK_PASS>
-__device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &in, const PBuf &out, bool pending, int acc,
-                                             int ox0, int oy0, int oz0, bool valid, uint32_t i, uint32_t tag,
-                                             uint32_t dst, float4 *win) {
+// The state P2G reads of one particle: x, v, C, F (or J), the per-particle
+// scalar and the id, loaded at source byte offset io.
+template <int MAT>
+struct P2GIn {
+  float x[3], v[3], C[9], F[MAT == MPM_J_FLUID ? 1 : 9], E;
+  uint32_t id;
+};
+template <int MAT, bool HAS_E>
+__device__ __forceinline__ void load_p2g(const SimDev &s, const PBuf &in, uint32_t io, P2GIn<MAT> &p) {
+  const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    p.x[a] = at_byte(in.x + a * Np, io);
+    p.v[a] = at_byte(in.v + a * Np, io);
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) p.C[k] = stream_load(at_byte(in.C + k * Np, io));
+#pragma unroll
+  for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) p.F[k] = stream_load(at_byte(in.F + k * Np, io));
+  p.E = HAS_E ? at_byte(in.E, io) : s.E;
+  p.id = stream_load(at_byte(in.id, io));
+}
+
+// (mid, called once the particle's loaded state is used up and before the
+// deposit: the caller requests its next round there, so that the loads
+// overlap the deposit's LDS passes)
+template <int MAT, bool HAS_E, bool FREE, int NW, bool RANK_PASS, typename Mid>
+__device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &out, bool pending, int acc, int ox0,
+                                             int oy0, int oz0, bool valid, const P2GIn<MAT> &pin, uint32_t tag,
+                                             uint32_t dst, float4 *win, Mid mid) {
   const int lane = threadIdx.x;
   const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
   const float dt = s.dt, mass = s.mass, fn = s.fn, dx = s.dx;
-  const uint32_t io = 4u * i, od = 4u * dst;  // byte offsets of the source and destination slots
+  const uint32_t od = 4u * dst;  // byte offset of the destination slot
   float xp[3], vp[3], Cp[9];
 #pragma unroll
   for (int a = 0; a < 3; ++a) {
-    xp[a] = at_byte(in.x + a * Np, io);
-    vp[a] = at_byte(in.v + a * Np, io);
+    xp[a] = pin.x[a];
+    vp[a] = pin.v[a];
   }
 #pragma unroll
-  for (int k = 0; k < 9; ++k) Cp[k] = stream_load(at_byte(in.C + k * Np, io));
+  for (int k = 0; k < 9; ++k) Cp[k] = pin.C[k];
   // the pending advection of the G2P before (the same bits as its keys)
   if (pending)
 #pragma unroll
@@ -287,16 +313,16 @@ __device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &in, co
   if (valid) {
 #pragma unroll
     for (int a = 0; a < 3; ++a) at_byte(out.x + a * Np, od) = xp[a];
-    stream_store(at_byte(in.id, io), at_byte(out.id, od));
+    stream_store(pin.id, at_byte(out.id, od));
   }
 
   // Deferred deformation-gradient update, stress, APIC momentum.
   float Fp[MAT == MPM_J_FLUID ? 1 : 9];
 #pragma unroll
-  for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = stream_load(at_byte(in.F + k * Np, io));
+  for (int k = 0; k < (MAT == MPM_J_FLUID ? 1 : 9); ++k) Fp[k] = pin.F[k];
   if (pending) update_F<MAT>(Fp, Cp, dt);
   // the per-particle scalar: Young's modulus, or snow's log plastic volume
-  const float Es = HAS_E ? at_byte(in.E, io) : s.E;
+  const float Es = pin.E;
   const float E = MAT == MPM_SNOW ? s.E : Es;
   float ap = Es;
   float A[9];
@@ -343,6 +369,7 @@ __device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &in, co
     }
     pass_id = (uint32_t)__popcll(peers & ((1ull << lane) - 1ull));
   }
+  mid();
   // A mover (only in a step without a sort; rare) deposits directly.
   if (FREE && valid && mov) deposit_global(s, acc, b, w, q0, Ad);
   bool todo = inwin;
@@ -542,17 +569,24 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
     if (has_next) prefetch(ch_next);
 
     // Pass B: rounds of 64 particles in (super-rank, window, cell) order.
+    // (lanes past the count load the chunk's last particle and store nothing;
+    // a round's loads are issued before the deposit of the round before)
+    P2GIn<MAT> pin;
+    load_p2g<MAT, HAS_E>(s, in, 4u * order[min((uint32_t)lane, count - 1u)], pin);
     for (uint32_t r0 = 0; r0 < count; r0 += 64) {
       const uint32_t pos = r0 + (uint32_t)lane;
       const bool valid = pos < count;
       const uint32_t at = min(pos, count - 1u);
-      const uint32_t i = order[at];
       const uint32_t tag = ordtag[at];
       // The new state is stored in this processing order, (bin, super-rank,
       // window, cell): the next step's gathers then run over nearly
       // consecutive addresses.
-      p2g_particle<MAT, HAS_E, FREE, NW, false>(s, in, out, pending, acc, ox0, oy0, oz0, valid, i, tag, start + at,
-                                                sm.win);
+      p2g_particle<MAT, HAS_E, FREE, NW, false>(s, out, pending, acc, ox0, oy0, oz0, valid, pin, tag, start + at,
+                                                sm.win, [&]() {
+                                                  if (r0 + 64u < count)
+                                                    load_p2g<MAT, HAS_E>(
+                                                        s, in, 4u * order[min(pos + 64u, count - 1u)], pin);
+                                                });
     }
     // The next chunk's prefetched sources and cells are waited for here,
     // before the flush: a vector load is complete only once every vector
@@ -666,8 +700,10 @@ __device__ __forceinline__ void p2g_step_small(const SimDev &s, int src, int acc
       if (mov) pos = run + (uint32_t)__popcll(mm & below);
     }
     if (has_next) prefetch(ch_next);
-    p2g_particle<MAT, HAS_E, FREE, NW, true>(s, in, out, pending, acc, ox0, oy0, oz0, in_chunk, i,
-                                             mov ? (uint32_t)MOVER_TAG : r, start + pos, sm.win);
+    P2GIn<MAT> pin;
+    load_p2g<MAT, HAS_E>(s, in, 4u * i, pin);
+    p2g_particle<MAT, HAS_E, FREE, NW, true>(s, out, pending, acc, ox0, oy0, oz0, in_chunk, pin,
+                                             mov ? (uint32_t)MOVER_TAG : r, start + pos, sm.win, []() {});
     // (the next chunk's loads are waited for before the flush: a vector load
     // is complete only once every vector operation issued before it is)
     __asm__ __volatile__("" ::"v"(pf_src), "v"(pf_cell));
@@ -682,7 +718,7 @@ __device__ __forceinline__ void p2g_step_small(const SimDev &s, int src, int acc
 template <int MAT, bool HAS_E, int NW>
 // (snow: at least 4 waves per SIMD, which holds it at 128 VGPRs with no spill;
 // measured 13% faster than its unconstrained 130 VGPRs at 3 waves)
-__global__ __launch_bounds__(64, (MAT == MPM_SNOW && NW == NWIN) ? 4 : 1) void k_p2g(SimDev s, int src, int acc) {
+__global__ __launch_bounds__(64, NW == NWIN ? 4 : 1) void k_p2g(SimDev s, int src, int acc) {
   if constexpr (NW == NWIN_WIDE) {
     // (k_sort_small, which only small scenes use, leaves these to the P2G:
     // all its workgroups read them)

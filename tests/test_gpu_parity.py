@@ -212,7 +212,11 @@ def test_profiled_steps_match_graph_steps():
 
 def test_batched_graphs_match_single_steps():
     """mpm_step(17) (two 8-step graphs and one single step) against 17 calls of
-    mpm_step(1): the same steps, and the same step count."""
+    mpm_step(1): the same steps, and the same step count.  Two runs differ by
+    the order of their float atomics (and of the atomic mover slots), as any
+    two runs do, so each field's difference is held to the run-to-run bar of
+    test_gpu_lifecycle: the fp32 oracle's own distance from fp64, with the
+    parity normalisation (C by 4 n max|v| + max|C|)."""
     sc = scenes.random_scene(20000, 32, 66, cscale=10.0, fstretch=0.2, vscale=1.0)
     pu.log("batched vs single-step graphs")
     a = mpm.Simulation(sc)
@@ -222,16 +226,22 @@ def test_batched_graphs_match_single_steps():
         for _ in range(17):
             b.step(1)
         assert mpm.mpm_steps_taken(a.handle) == mpm.mpm_steps_taken(b.handle) == 17
-        ra, rb = a.read_particles(), b.read_particles()
-        for u, w in zip(ra, rb):
-            assert float((u - w).abs().max() / w.abs().max()) < 1e-5
+        ra = [t.cpu().numpy() for t in a.read_particles()]
+        rb = [t.cpu().numpy() for t in b.read_particles()]
         ma, pa = a.read_grid()
         mb, pb = b.read_grid()
-        assert float((ma - mb).abs().max() / mb.abs().max()) < 1e-5
-        assert float((pa - pb).abs().max() / pb.abs().max()) < 1e-5
     finally:
         a.close()
         b.close()
+    orc, env = pu.envelope(sc, 17)
+    vmax = max(np.abs(orc.v).max(), 1e-30)
+    scale = dict(x=1.0, v=vmax, C=4 * sc.n * vmax + np.abs(orc.C).max(), F=1.0)
+    for k, u, w in zip(("x", "v", "C", "F"), ra, rb):
+        d = float(np.abs(u - w).max() / scale[k])
+        pu.log(f"batched vs single {k}: {d:.3e} (fp32 envelope {env[k]:.3e})")
+        assert d <= max(env[k], 2e-6), (k, d, env[k])
+    assert pu.field_maxrel(ma.cpu().numpy(), mb.cpu().numpy()) <= 1e-5
+    assert pu.field_maxrel(pa.cpu().numpy(), pb.cpu().numpy()) <= 1e-5
 
 
 def test_resume_from_read_state():
