@@ -41,9 +41,13 @@ union P2GShared {
 };
 static_assert(sizeof(P2GRankTables<NWIN>) <= sizeof(float4) * NWIN * PW3, "rank tables must fit the windows");
 
-// LDS of the small-chunk P2G: the windows and a per-cell count.
+// LDS of the small-chunk P2G: the windows and a per-cell count.  Its
+// windows are PW3_PAD nodes apart, a multiple of 256 bytes, so that the
+// flush reads one node's value in two windows with one instruction.
+constexpr int PW3_PAD = 224;
+static_assert(PW3_PAD >= PW3 && (PW3_PAD * 16) % 256 == 0, "padded window stride");
 struct P2GSmallShared {
-  float4 win[NWIN_WIDE * PW3];
+  float4 win[NWIN_WIDE * PW3_PAD];
   uint32_t cnt[CB3];  // particles per cell of the chunk being ranked
 };
 
@@ -52,9 +56,9 @@ struct P2GSmallShared {
 // single wavefront), then the partial row.  (The many-wavefront paths keep
 // the loop: unrolled, it raised their register count past an occupancy
 // step.)
-template <int NW>
+template <int NW, int WS = PW3>
 __device__ __forceinline__ void clear_windows(float4 *win) {
-  constexpr int N = NW * PW3;
+  constexpr int N = NW * WS;
   const int lane = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < N / 64; ++k) win[64 * k + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -172,7 +176,7 @@ __device__ __forceinline__ void clear_accumulator(const SimDev &s, int a) {
 // steps later clears exactly these (and mpm_read_grid reads them).  A marked
 // block whose nodes got no mass is cleared for nothing, which is harmless.
 // Plain stores: every writer stores the same value.
-template <int NW>
+template <int NW, int WS = PW3>
 __device__ __forceinline__ void flush_windows(const SimDev &s, const float4 *win, int ox0, int oy0, int oz0, int a) {
   const int lane = threadIdx.x;
   {
@@ -205,7 +209,7 @@ __device__ __forceinline__ void flush_windows(const SimDev &s, const float4 *win
       const int kw = h ? kw1 : kw0;
       float val = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) val += winl[4 * (kw + w * PW3)];
+      for (int w = 0; w < NW; ++w) val += winl[4 * (kw + w * WS)];
       bool inb = val != 0.f;
       if (!interior) {
         const int cx = h ? x1 : x0, cy = h ? y1 : y0, cz = h ? z1 : z0;
@@ -290,7 +294,7 @@ __device__ __forceinline__ void load_p2g(const SimDev &s, const PBuf &in, uint32
 // (mid, called once the particle's loaded state is used up and before the
 // deposit: the caller requests its next round there, so that the loads
 // overlap the deposit's LDS passes)
-template <int MAT, bool HAS_E, bool FREE, int NW, bool RANK_PASS, typename Mid>
+template <int MAT, bool HAS_E, bool FREE, int NW, bool RANK_PASS, int WS, typename Mid>
 __device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &out, bool pending, int acc, int ox0,
                                              int oy0, int oz0, bool valid, const P2GIn<MAT> &pin, uint32_t tag,
                                              uint32_t dst, float4 *win, Mid mid) {
@@ -342,7 +346,7 @@ __device__ __forceinline__ void p2g_particle(const SimDev &s, const PBuf &out, b
   momentum_terms(mass, dx, vp, A, f, q0, Ad);
   const int lx = min(max(b[0] - ox0, 0), CB - 1), ly = min(max(b[1] - oy0, 0), CB - 1),
             lz = min(max(b[2] - oz0, 0), CB - 1);
-  const int li0 = (int)(tag % NW) * PW3 + (lz * PW + ly) * PW + lx;
+  const int li0 = (int)(tag % NW) * WS + (lz * PW + ly) * PW + lx;
 
   // Passes: lanes conflict only when they share (window, cell).  With
   // RANK_PASS the tag is the particle's rank r in its cell, which is its
@@ -581,7 +585,7 @@ __device__ __forceinline__ void p2g_step(const SimDev &s, int src, int acc, P2GS
       // The new state is stored in this processing order, (bin, super-rank,
       // window, cell): the next step's gathers then run over nearly
       // consecutive addresses.
-      p2g_particle<MAT, HAS_E, FREE, NW, false>(s, out, pending, acc, ox0, oy0, oz0, valid, pin, tag, start + at,
+      p2g_particle<MAT, HAS_E, FREE, NW, false, PW3>(s, out, pending, acc, ox0, oy0, oz0, valid, pin, tag, start + at,
                                                 sm.win, [&]() {
                                                   if (r0 + 64u < count)
                                                     load_p2g<MAT, HAS_E>(
@@ -649,7 +653,7 @@ __device__ __forceinline__ void p2g_step_small(const SimDev &s, int src, int acc
     ch_next = load_record(chunks + qbeg + wq);
     prefetch(ch_next);
   }
-  clear_windows<NW>(sm.win);
+  clear_windows<NW, PW3_PAD>(sm.win);
   for (uint32_t c = qbeg + wq; c < qend; c += nwq) {
     const uint4 ch = ch_next;
     const uint32_t start = ch.x, count = min(ch.y, 64u), bin = ch.z;
@@ -702,15 +706,15 @@ __device__ __forceinline__ void p2g_step_small(const SimDev &s, int src, int acc
     if (has_next) prefetch(ch_next);
     P2GIn<MAT> pin;
     load_p2g<MAT, HAS_E>(s, in, 4u * i, pin);
-    p2g_particle<MAT, HAS_E, FREE, NW, true>(s, out, pending, acc, ox0, oy0, oz0, in_chunk, pin,
+    p2g_particle<MAT, HAS_E, FREE, NW, true, PW3_PAD>(s, out, pending, acc, ox0, oy0, oz0, in_chunk, pin,
                                              mov ? (uint32_t)MOVER_TAG : r, start + pos, sm.win, []() {});
     // (the next chunk's loads are waited for before the flush: a vector load
     // is complete only once every vector operation issued before it is)
     __asm__ __volatile__("" ::"v"(pf_src), "v"(pf_cell));
-    flush_windows<NW>(s, sm.win, ox0, oy0, oz0, acc);
+    flush_windows<NW, PW3_PAD>(s, sm.win, ox0, oy0, oz0, acc);
     if (has_next) {
       __asm__ __volatile__("" ::: "memory");
-      clear_windows<NW>(sm.win);
+      clear_windows<NW, PW3_PAD>(sm.win);
     }
   }
 }
