@@ -12,7 +12,7 @@
 // decision is taken here, on the movers the previous step counted); before
 // a sort it runs the plain G2P, which writes the keys the sort needs.
 struct FusedShared {
-  float4 vel[PW3];          // the step's grid velocities around the bin
+  float3 vel[PW3];          // the step's grid velocities around the bin
   float4 win[NWIN * PW3];   // the next step's accumulation windows
 };
 

@@ -103,9 +103,12 @@ __device__ __forceinline__ void fetch_window(const SimDev &s, int a, int ox0, in
   }
 }
 
-// Converts fetched window values to grid velocities (the grid update) in LDS.
+// Converts fetched window values to grid velocities (the grid update) in LDS,
+// three floats per node: packed, the gather's reads of a round hit fewer
+// banks together than at a 16-byte stride (measured: G2P 0.070 -> 0.063 ms
+// on the 4M dam break, 0.059 -> 0.054 on the 3.1M sand column).
 __device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4], const uint32_t wpack[4], int ox0,
-                                             int oy0, int oz0, float4 *win) {
+                                             int oy0, int oz0, float3 *win) {
   if (window_inside(s, ox0, oy0, oz0) && window_off_walls(s, ox0, oy0, oz0)) {
     const float gx = s.dt * s.g[0], gy = s.dt * s.g[1], gz = s.dt * s.g[2];
 #pragma unroll
@@ -119,7 +122,7 @@ __device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4
         o.y = m.z * inv + gy;
         o.z = m.w * inv + gz;
       }
-      win[wp_li(wpack[t])] = o;
+      win[wp_li(wpack[t])] = make_float3(o.x, o.y, o.z);
     }
     return;
   }
@@ -129,8 +132,9 @@ __device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4
     int wx, wy, wz;
     wp_coords(wpack[t], wx, wy, wz);
     const int gx = ox0 + wx, gy = oy0 + wy, gz = oz0 + wz;
-    win[(wz * PW + wy) * PW + wx] =
+    const float4 o =
         (gx < s.n && gy < s.n && gz < s.n) ? grid_velocity(s, acc[t], gx, gy, gz) : make_float4(0.f, 0.f, 0.f, 0.f);
+    win[(wz * PW + wy) * PW + wx] = make_float3(o.x, o.y, o.z);
   }
 }
 
@@ -139,7 +143,7 @@ __device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4
 // bin at (ox0, oy0, oz0), or from accumulator a with the grid update for a
 // particle whose stencil is outside the window (it left the chunk's bin
 // since the last sort: only in steps without a sort; rare).
-__device__ __forceinline__ void gather_particle(const SimDev &s, const float4 *win, int a, const float xp[3], int ox0,
+__device__ __forceinline__ void gather_particle(const SimDev &s, const float3 *win, int a, const float xp[3], int ox0,
                                                 int oy0, int oz0, float v[3], float B[9]) {
   int b[3];
   float w[3][3], d[3][3];
@@ -202,9 +206,9 @@ __device__ __forceinline__ void gather_particle(const SimDev &s, const float4 *w
 #pragma unroll
       for (int oy = 0; oy < 3; ++oy) {
         float S[3], U[3];
-        const float4 g0 = win[li0 + (oz * PW + oy) * PW + 0];
-        const float4 g1 = win[li0 + (oz * PW + oy) * PW + 1];
-        const float4 g2 = win[li0 + (oz * PW + oy) * PW + 2];
+        const float3 g0 = win[li0 + (oz * PW + oy) * PW + 0];
+        const float3 g1 = win[li0 + (oz * PW + oy) * PW + 1];
+        const float3 g2 = win[li0 + (oz * PW + oy) * PW + 2];
         S[0] = w[0][0] * g0.x;
         S[1] = w[0][0] * g0.y;
         S[2] = w[0][0] * g0.z;
@@ -261,7 +265,7 @@ __device__ __forceinline__ void advect(const SimDev &s, const float xp[3], const
 // it with that v), and the next step's bin keys and
 // counts.
 template <int MAT>
-__device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float4 *win) {
+__device__ __forceinline__ void g2p_step(const SimDev &s, int lay, int a, float3 *win) {
   const PBuf out = s.buf[lay];
   const int lane = threadIdx.x;
   const uint32_t Np = (uint32_t)s.Np;  // Np < 2^29: component offsets k Np (k < 9) are exact in 32 bits
@@ -354,7 +358,7 @@ __device__ __forceinline__ void g2p_handoff(const SimDev &s, int lay) {
 // step's bin keys and counts.
 template <int MAT>
 __global__ __launch_bounds__(64, 5) void k_g2p(SimDev s, int src, int a) {
-  __shared__ float4 win[PW3];
+  __shared__ float3 win[PW3];
   g2p_step<MAT>(s, src ^ 1, a, win);
   g2p_handoff(s, src ^ 1);
 }
