@@ -2,6 +2,14 @@
 // Part of mpm.hip: included there, inside its anonymous namespace, after the
 // parts before it; not a standalone header.
 
+// 1/m as the hardware reciprocal (within 1 ulp) refined by one Newton step,
+// r + r (1 - m r): one division per node (G2P evaluates each node once per
+// window that covers it), and p (1/m) is within an ulp of p/m.
+__device__ __forceinline__ float inv_mass(float m) {
+  const float r0 = __builtin_amdgcn_rcpf(m);
+  return fmaf(r0, fmaf(-m, r0, 1.f), r0);
+}
+
 // The grid update -- v = p/m + dt g where m > 0, sticky walls -- is
 // evaluated by G2P on its window nodes as it loads them (grid_velocity), and
 // the accumulator is cleared by the P2G two steps later, so the step needs
@@ -11,9 +19,7 @@ __device__ __forceinline__ float4 grid_velocity(const SimDev &s, float4 acc, int
   float4 o = make_float4(0.f, 0.f, 0.f, acc.x);
   const bool in_wall = gx < wall || gy < wall || gz < wall || gx >= n - wall || gy >= n - wall || gz >= n - wall;
   if (acc.x > 0.f && !in_wall) {
-    // one division per node (G2P evaluates each node once per window that
-    // covers it): p (1/m) is within an ulp of p/m
-    const float inv = 1.f / acc.x;
+    const float inv = inv_mass(acc.x);
     o.x = acc.y * inv + s.dt * s.g[0];
     o.y = acc.z * inv + s.dt * s.g[1];
     o.z = acc.w * inv + s.dt * s.g[2];
@@ -117,7 +123,7 @@ __device__ __forceinline__ void store_window(const SimDev &s, const float4 acc[4
       const float4 m = acc[t];
       float4 o = make_float4(0.f, 0.f, 0.f, m.x);
       if (m.x > 0.f) {
-        const float inv = 1.f / m.x;
+        const float inv = inv_mass(m.x);
         o.x = m.y * inv + gx;
         o.y = m.z * inv + gy;
         o.z = m.w * inv + gz;
@@ -163,10 +169,7 @@ __device__ __forceinline__ void gather_particle(const SimDev &s, const float3 *w
             lz = min(max(b[2] - oz0, 0), CB - 1);
   const int li0 = (lz * PW + ly) * PW + lx;
   // The quadratic B-spline's first moment sum_o w_o (o - f) = 0 gives the
-  // columns of B as B_a = sum w o_a v_i - f_a v.  Reduced along x first for
-  // each (y, z) row: S = sum_x w_x v_i and U = sum_x w_x ox v_i; offsets
-  // equal to zero add nothing, so rows with oy = 0 (oz = 0) skip the y (z)
-  // column.
+  // columns of B as B_a = sum w o_a v_i - f_a v.
   const float w2x = 2.f * w[0][2];
 #pragma unroll
   for (int k = 0; k < 3; ++k) v[k] = 0.f;
@@ -201,39 +204,46 @@ __device__ __forceinline__ void gather_particle(const SimDev &s, const float3 *w
       }
     }
   } else {
+    // Reduced one axis at a time: along x for each (y, z) row, then along y
+    // in each z plane, then along z.  With t = w_1 a_1 formed once, a sum
+    // w_0 a_0 + w_1 a_1 + w_2 a_2 and its first moment w_1 a_1 + 2 w_2 a_2
+    // share that product.  Per plane: P = sum_y w_y S, PU = sum_y w_y U,
+    // PY = sum_y w_y oy S; then v = sum_z w_z P, B_x = sum_z w_z PU,
+    // B_y = sum_z w_z PY, B_z = sum_z w_z oz P.
+    const float w2y = 2.f * w[1][2], w2z = 2.f * w[2][2];
+    float P[3][3], PU[3][3], PY[3][3];
 #pragma unroll
-    for (int oz = 0; oz < 3; ++oz)
+    for (int oz = 0; oz < 3; ++oz) {
+      float S[3][3], U[3][3];
 #pragma unroll
       for (int oy = 0; oy < 3; ++oy) {
-        float S[3], U[3];
         const float3 g0 = win[li0 + (oz * PW + oy) * PW + 0];
         const float3 g1 = win[li0 + (oz * PW + oy) * PW + 1];
         const float3 g2 = win[li0 + (oz * PW + oy) * PW + 2];
-        S[0] = w[0][0] * g0.x;
-        S[1] = w[0][0] * g0.y;
-        S[2] = w[0][0] * g0.z;
-        U[0] = w[0][1] * g1.x;
-        U[1] = w[0][1] * g1.y;
-        U[2] = w[0][1] * g1.z;
-        S[0] = fmaf(w[0][1], g1.x, S[0]);
-        S[1] = fmaf(w[0][1], g1.y, S[1]);
-        S[2] = fmaf(w[0][1], g1.z, S[2]);
-        S[0] = fmaf(w[0][2], g2.x, S[0]);
-        S[1] = fmaf(w[0][2], g2.y, S[1]);
-        S[2] = fmaf(w[0][2], g2.z, S[2]);
-        U[0] = fmaf(w2x, g2.x, U[0]);
-        U[1] = fmaf(w2x, g2.y, U[1]);
-        U[2] = fmaf(w2x, g2.z, U[2]);
-        const float wyz = w[1][oy] * w[2][oz];
-        const float wyz2 = wyz + wyz;
+        const float a0[3] = {g0.x, g0.y, g0.z}, a1[3] = {g1.x, g1.y, g1.z}, a2[3] = {g2.x, g2.y, g2.z};
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-          v[k] = fmaf(wyz, S[k], v[k]);
-          B[k * 3 + 0] = fmaf(wyz, U[k], B[k * 3 + 0]);
-          if (oy > 0) B[k * 3 + 1] = fmaf(oy == 1 ? wyz : wyz2, S[k], B[k * 3 + 1]);
-          if (oz > 0) B[k * 3 + 2] = fmaf(oz == 1 ? wyz : wyz2, S[k], B[k * 3 + 2]);
+          const float t = w[0][1] * a1[k];
+          S[oy][k] = fmaf(w[0][2], a2[k], fmaf(w[0][0], a0[k], t));
+          U[oy][k] = fmaf(w2x, a2[k], t);
         }
       }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float t = w[1][1] * S[1][k];
+        P[oz][k] = fmaf(w[1][2], S[2][k], fmaf(w[1][0], S[0][k], t));
+        PY[oz][k] = fmaf(w2y, S[2][k], t);
+        PU[oz][k] = fmaf(w[1][2], U[2][k], fmaf(w[1][1], U[1][k], w[1][0] * U[0][k]));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const float t = w[2][1] * P[1][k];
+      v[k] = fmaf(w[2][2], P[2][k], fmaf(w[2][0], P[0][k], t));
+      B[k * 3 + 2] = fmaf(w2z, P[2][k], t);
+      B[k * 3 + 0] = fmaf(w[2][2], PU[2][k], fmaf(w[2][1], PU[1][k], w[2][0] * PU[0][k]));
+      B[k * 3 + 1] = fmaf(w[2][2], PY[2][k], fmaf(w[2][1], PY[1][k], w[2][0] * PY[0][k]));
+    }
   }
 #pragma unroll
   for (int k = 0; k < 3; ++k)
