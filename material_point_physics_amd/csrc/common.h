@@ -198,11 +198,15 @@ __device__ __forceinline__ uint32_t bin_key(const SimDev &, int bx, int by, int 
   return spread3((uint32_t)bx >> 2) | (spread3((uint32_t)by >> 2) << 1) | (spread3((uint32_t)bz >> 2) << 2);
 }
 
-// Cell of a base node within its 4^3-cell bin (x fastest), and the key word
-// that carries it above the bin index.  grid_n <= 1024 keeps bins below 2^24.
+// Cell of a base node within its 4^3-cell bin, and the key word that
+// carries it above the bin index.  grid_n <= 1024 keeps bins below 2^24.
+// The number only orders a chunk's particles (the deposit passes take lanes
+// in cell order): x fastest, then z, then y, so that 16 consecutive cells
+// form an (x, z) plane, whose window nodes (strides 1 and 36, which is 4 mod
+// 16) fall in 16 distinct 16-byte LDS bank groups for every stencil offset.
 constexpr int KEY_CELL_SHIFT = 24;
 __device__ __forceinline__ uint32_t cell_in_bin(int bx, int by, int bz) {
-  return ((uint32_t)(bz & 3) << 4) | ((uint32_t)(by & 3) << 2) | (uint32_t)(bx & 3);
+  return ((uint32_t)(by & 3) << 4) | ((uint32_t)(bz & 3) << 2) | (uint32_t)(bx & 3);
 }
 
 // Quadratic B-spline weights of nodes base+0,1,2 at fractional offset f in [0.5,1.5).
